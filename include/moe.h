@@ -1,0 +1,192 @@
+/*
+ * libmoe: the Gemma-4 26B-A4B mixture-of-experts feed-forward block on one
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The layer these calls implement is described on the page "Porting a
+ * 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section "The
+ * architecture: a dual-path FFN nobody warned me about": a router (its own
+ * RMSNorm, a scale, an H -> E projection, softmax in fp32, top-K,
+ * renormalisation, x per_expert_scale), E gated experts stored as a fused
+ * gate_up_proj [E, 2I, H] and a down_proj [E, H, I] evaluated as a sparse
+ * gather / compute / weighted scatter-add, and beside them a dense gated MLP,
+ * with pre- and post-norms on each branch, a final norm, the residual and a
+ * layer_scalar.  The experts' activation is the tanh form of GELU ("Porting
+ * Gemma-4 (2B / 4B / 12B) to AWS Inferentia2", section 4.5).
+ *
+ * The calls split along the page's seams: moe_router is Gemma4TextRouter
+ * (whose output weights already carry the renormalisation and the
+ * per-expert scale); moe_dispatch + moe_expert_ffn + moe_combine are
+ * Gemma4TextExperts' gather, compute and scatter-add; gemma4_ffn_block is the
+ * whole dual-path layer; moe_forward chains the four experts-only calls.
+ *
+ * Conventions (all calls):
+ *   - Every array argument is a DEVICE pointer owned by the caller; nothing is
+ *     retained after the call returns.  Inputs must stay alive and unmodified
+ *     until the stream has executed the enqueued work.
+ *   - Each call validates its arguments on the host first.  On a validation
+ *     failure it returns a negative moe_status, launches nothing and makes no
+ *     HIP call; moe_last_error() then names the problem.  Otherwise it enqueues
+ *     kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ *     returns MOE_OK without synchronising.  A launch failure returns
+ *     MOE_ERR_HIP.
+ *   - T = 0 is a valid no-op.
+ *   - No call allocates device memory.  Calls that need scratch take a
+ *     workspace `ws` of at least moe_workspace_size() bytes, 256-byte aligned.
+ *     Two calls in flight must not share a workspace.
+ *   - Pointers must be 16-byte aligned.
+ *   - Preconditions that are not checked: inputs are finite; topk_idx given to
+ *     moe_dispatch lies in [0, E) with K distinct experts per token; the
+ *     offsets / sorted_slots given to moe_expert_ffn are moe_dispatch's output
+ *     for the same topk_idx.
+ *   - Results are deterministic: no floating-point atomics; the same inputs
+ *     give the same bits on every run.
+ *
+ * Layouts (row-major, innermost index last):
+ *   x, residual, out          [T, H]        act dtype
+ *   router_w                  [E, H]        fp32
+ *   router_scale, gains       [H]           fp32
+ *   per_expert_scale          [E]           fp32
+ *   w_gate_up                 [E, 2I, H]    act dtype; rows [0,I) gate, [I,2I) up
+ *   w_down                    [E, H, I]     act dtype
+ *   dense_gate, dense_up      [D, H]        act dtype
+ *   dense_down                [H, D]        act dtype
+ *   topk_idx                  [T, K]        int32; slot k is the k-th largest logit
+ *   topk_w                    [T, K]        fp32
+ *   y_slots                   [T, K, H]     slot dtype; y_slots[t,k] = w[t,k] * expert(x_t)
+ *   expert_counts             [E]           int32
+ *   expert_offsets            [E + 1]       int32 exclusive prefix sum of counts
+ *   sorted_slots              [T * K]       int32 slot ids t*K+k grouped by expert,
+ *                                           ascending within each expert
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* NULL pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2,  /* dimensions outside the supported range */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4           /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,   /* fp32 storage and fp32 arithmetic (debug path) */
+  MOE_BF16 = 1   /* bf16 storage, fp32 accumulation (fast path) */
+} moe_dtype;
+
+/* Layer dimensions.  Supported: hidden % 64 == 0 and 64 <= hidden <= 8192;
+ * 1 <= num_experts <= 256; 1 <= top_k <= min(num_experts, 32);
+ * expert_inter % 32 == 0, 32 <= expert_inter <= 8192; dense_inter == 0 or
+ * dense_inter % 32 == 0, <= 16384; eps > 0.  act_dtype MOE_F32 requires
+ * slot_dtype MOE_F32.  Token counts up to 65536 with T * top_k <= 2^20. */
+typedef struct moe_dims {
+  int32_t hidden;        /* H (2816 for 26B-A4B) */
+  int32_t num_experts;   /* E (128) */
+  int32_t top_k;         /* K (8) */
+  int32_t expert_inter;  /* I (704) */
+  int32_t dense_inter;   /* D (2112); 0 = no dense branch */
+  float eps;             /* RMSNorm epsilon (1e-6), inside the square root */
+  int32_t act_dtype;     /* moe_dtype of activations and expert / dense weights */
+  int32_t slot_dtype;    /* moe_dtype of y_slots and of the dense branch output */
+} moe_dims;
+
+/* Weights of one dual-path layer (all device pointers). */
+typedef struct gemma4_ffn_weights {
+  const float* g_pre;      /* [H] pre_feedforward_layernorm gain (effective multiplier) */
+  const float* g_pre2;     /* [H] pre_feedforward_layernorm_2 */
+  const float* g_post1;    /* [H] post_feedforward_layernorm_1 (dense branch) */
+  const float* g_post2;    /* [H] post_feedforward_layernorm_2 (MoE branch) */
+  const float* g_post;     /* [H] post_feedforward_layernorm */
+  const void* dense_gate;  /* [D, H] act dtype */
+  const void* dense_up;    /* [D, H] act dtype */
+  const void* dense_down;  /* [H, D] act dtype */
+  const float* router_w;   /* [E, H] */
+  const float* router_scale;      /* [H] */
+  const float* per_expert_scale;  /* [E] */
+  const void* w_gate_up;   /* [E, 2I, H] act dtype */
+  const void* w_down;      /* [E, H, I] act dtype */
+  float layer_scalar;      /* multiplies (FFN + residual) */
+} gemma4_ffn_weights;
+
+/* Bytes of workspace sufficient for every call below with T <= max_tokens.
+ * Returns 0 if the dimensions are unsupported (moe_last_error() says why). */
+size_t moe_workspace_size(const moe_dims* dims, int32_t max_tokens);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Router (Gemma4TextRouter): for each token, v = x (or, when pre_norm_gain is
+ * not NULL, v = RMSNorm(x) * pre_norm_gain, i.e. pre_feedforward_layernorm_2);
+ * vhat = v / sqrt(mean(v^2) + eps) * router_scale; logits = router_w . vhat
+ * (fp32); p = softmax(logits) in fp32; the K experts with the largest logits
+ * (ties to the lower index) in descending order; w_k = p_k / sum_j p_j *
+ * per_expert_scale[e_k].  All router arithmetic is fp32; every reduction over
+ * H runs in 64-element chunks, each a fused multiply-add chain in ascending
+ * index from +0, the chunk results added in ascending chunk order, and the
+ * square root and divisions are correctly rounded, so that the logits are
+ * reproducible bit for bit on any IEEE fp32 machine.
+ * x: [T,H] act dtype.  Outputs topk_idx [T,K], topk_w [T,K]. */
+int moe_router(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+               const float* router_scale, const float* per_expert_scale,
+               const float* pre_norm_gain, int32_t* topk_idx, float* topk_w,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Groups the T*K token-slots by expert (the gather side of the experts'
+ * sparse loop): expert_counts[e] = #slots with topk_idx == e, expert_offsets
+ * their exclusive prefix sum (expert_offsets[E] = T*K), sorted_slots the slot
+ * ids of expert 0, then expert 1, ..., ascending within each expert.
+ * Integer-only and exact. */
+int moe_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* The experts (Gemma4TextExperts' compute): for every slot s = t*K+k routed
+ * to expert e, y_slots[t,k,:] = topk_w[t,k] * down[e] (gelu_tanh(gate[e] x_t)
+ * * (up[e] x_t)).  x: [T,H] expert input (act dtype).  bf16 path: bf16 MFMA
+ * with fp32 accumulation, the GELU product rounded to bf16 before the down
+ * projection.  fp32 path: fp32 arithmetic throughout. */
+int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,
+                   const void* w_down, const float* topk_w, const int32_t* expert_offsets,
+                   const int32_t* sorted_slots, void* y_slots, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* The experts' scatter-add: out[t] = sum_{k=0..K-1} y_slots[t,k] (fp32, k
+ * ascending, no atomics) + addend[t] (if addend is not NULL).
+ * y_slots slot dtype; addend and out act dtype. */
+int moe_combine(const moe_dims* dims, int32_t T, const void* y_slots, const void* addend,
+                void* out, void* stream);
+
+/* Experts-only path in one call: moe_router (no pre-norm), moe_dispatch,
+ * moe_expert_ffn, moe_combine (no addend).  If topk_idx / topk_w are not NULL
+ * the routing is also written there. */
+int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                const float* router_scale, const float* per_expert_scale,
+                const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
+                float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* One dual-path feed-forward layer (the page's diagram):
+ *   xd = RMSNorm_pre(x); xm = RMSNorm_pre2(x)
+ *   moe = experts(xm) routed on pre_feedforward_layernorm_2(x) (moe_router)
+ *   dn  = dense_down (gelu_tanh(dense_gate xd) * (dense_up xd))
+ *   o   = RMSNorm_post(RMSNorm_post1(dn) + RMSNorm_post2(moe))
+ *   out = (o + x) * layer_scalar
+ * residual x and out: [T,H] act dtype.  ffn_out (optional, [T,H] fp32) receives
+ * o, the layer's output before the residual; topk_idx / topk_w (optional)
+ * receive the routing.  Requires dims->dense_inter > 0. */
+int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
+                     const gemma4_ffn_weights* weights, void* out, float* ffn_out,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// Round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// tanh form of GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float inner = c * (z + 0.044715f * z * z * z);
+  return 0.5f * z * (1.0f + tanhf(inner));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Row tiles of a grouped GEMM.  Expert e owns rows [offsets[e], offsets[e+1])
+// of the expert-sorted slot order; it is cut into ceil(count / bm) tiles of
+// bm rows.  Tile number `tile` (counting experts in ascending order) is mapped
+// to its expert and row range by one wave: each lane takes a run of
+// consecutive experts, the lanes' tile totals are scanned, and the owner is
+// found.  Returns false if `tile` is past the last tile.  Every lane of the
+// calling wave gets the same answer.  Requires E <= 4 * 64.
+__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E,
+                                              int bm, int tile, int& e_out, int& row0,
+                                              int& row1) {
+  const int lane = lane_id();
+  const int per = (E + kWave - 1) / kWave;  // experts per lane (<= 4)
+  int base = lane * per;
+  int cnt[4];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = base + j;
+    int c = 0;
+    if (j < per && e < E) c = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    cnt[j] = c;
+    local += c;
+  }
+  // inclusive scan of the lane totals
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  int excl = incl - local;
+  int total = __shfl(incl, kWave - 1, kWave);
+  if (tile >= total) return false;
+  // the lane whose range holds `tile`
+  unsigned long long hit = __ballot(tile >= excl && tile < incl);
+  int owner = __ffsll((long long)hit) - 1;
+  int e_found = 0, t_in = 0;
+  if (lane == owner) {
+    int rem = tile - excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (rem >= 0 && rem < cnt[j]) { e_found = base + j; t_in = rem; }
+      rem -= cnt[j];
+    }
+  }
+  e_out = __shfl(e_found, owner, kWave);
+  t_in = __shfl(t_in, owner, kWave);
+  row0 = offsets[e_out] + t_in * bm;
+  row1 = min(row0 + bm, offsets[e_out + 1]);
+  return true;
+}
+
+}  // namespace moe

@@ -1,0 +1,115 @@
+// Host-side launchers of the libmoe kernels.  Each returns the HIP error of
+// its launches (hipSuccess when all were enqueued).  Arguments are validated
+// by the C ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  int T, H, E, K;
+  float eps;
+  bool x_bf16;
+  const void* x;                 // [T,H]
+  const float* pre_gain;         // [H] or nullptr
+  const float* router_w;         // [E,H]
+  const float* router_scale;     // [H]
+  const float* per_expert_scale; // [E]
+  int32_t* topk_idx;             // [T,K]
+  float* topk_w;                 // [T,K]
+  float* ws_r0;                  // [T]   inverse RMS of x (pre-norm), if pre_gain
+  float* ws_r;                   // [T]   inverse RMS of the router input
+  float* ws_logits;              // [T,E]
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+  int T, E, K;
+  const int32_t* topk_idx;   // [T*K]
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E+1]
+  int32_t* sorted_slots;     // [T*K]
+  int32_t* ws_blk_counts;    // [nblk*E]
+  int32_t* ws_local_rank;    // [T*K]
+};
+int dispatch_num_blocks(int S);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// Grouped gated-MLP over row groups.  Group e owns rows [offsets[e],
+// offsets[e+1]) of the sorted order; row r reads input row
+// sorted_slots[r] / K (or r itself when ident).  w_gate / w_up point at the
+// first group's [N,H] gate and up rows; group e's are at + e * w_stride.
+struct GateUpArgs {
+  int T, H, N, E, K;   // N = intermediate width (I or D)
+  int rows;            // total rows S (or T when ident)
+  bool ident;          // rows are the tokens themselves (dense branch)
+  bool bf16;
+  const void* x;               // [T,H]
+  const void* w_gate;
+  const void* w_up;
+  long long w_stride;          // elements between consecutive groups' weights
+  const int32_t* offsets;      // [E+1] (unused when ident)
+  const int32_t* sorted_slots; // [rows] (unused when ident)
+  void* h;                     // [rows, N] act dtype, sorted order
+};
+hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s);
+
+// Down projection of the gated rows; row r of group e goes to output row
+// sorted_slots[r] (or r when ident), scaled by topk_w of that slot (1 when
+// ident).
+struct DownArgs {
+  int T, H, N, E, K;   // N = intermediate width (contraction length)
+  int rows;
+  bool ident;
+  bool bf16;           // act dtype (h and w_down)
+  bool y_bf16;         // output dtype
+  const void* h;               // [rows, N]
+  const void* w_down;          // group 0's [H, N]
+  long long w_stride;
+  const int32_t* offsets;
+  const int32_t* sorted_slots;
+  const float* topk_w;         // [T*K] (unused when ident)
+  void* y;                     // [T*K, H] slot-major (or [T,H] when ident)
+};
+hipError_t launch_down(const DownArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  int T, H, K;
+  bool y_bf16, act_bf16;
+  const void* y;       // [T,K,H]
+  const void* addend;  // [T,H] act or nullptr
+  void* out;           // [T,H] act
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+struct PreNormArgs {
+  int T, H;
+  float eps;
+  bool bf16;
+  const void* x;
+  const float* g_pre;
+  const float* g_pre2;
+  void* xd;
+  void* xm;
+};
+hipError_t launch_prenorm(const PreNormArgs& a, hipStream_t s);
+
+struct EpilogueArgs {
+  int T, H, K;
+  float eps;
+  float layer_scalar;
+  bool y_bf16, act_bf16;
+  const void* y;       // [T,K,H] slot dtype
+  const void* dn;      // [T,H] slot dtype (dense branch output)
+  const void* x;       // [T,H] act (residual)
+  const float* g_post1;
+  const float* g_post2;
+  const float* g_post;
+  void* out;           // [T,H] act
+  float* ffn_out;      // [T,H] fp32 or nullptr
+};
+hipError_t launch_block_epilogue(const EpilogueArgs& a, hipStream_t s);
+
+}  // namespace moe

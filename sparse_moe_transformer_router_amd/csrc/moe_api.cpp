@@ -1,0 +1,369 @@
+// C ABI of libmoe (declared in include/moe.h): host-side argument checks,
+// workspace layout, and the kernel sequence of each call on the caller's
+// stream.  No call synchronises or allocates.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t dtype_size(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_ERR_ARG, "dims is NULL");
+  if (d->hidden < 64 || d->hidden > 8192 || d->hidden % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: need a multiple of 64 in [64, 8192]", d->hidden);
+  if (d->num_experts < 1 || d->num_experts > 256)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts=%d: need 1..256", d->num_experts);
+  if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > 32)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d: need 1..min(num_experts, 32)", d->top_k);
+  if (d->expert_inter < 32 || d->expert_inter > 8192 || d->expert_inter % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "expert_inter=%d: need a multiple of 32 in [32, 8192]",
+                d->expert_inter);
+  if (d->dense_inter < 0 || d->dense_inter > 16384 || d->dense_inter % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "dense_inter=%d: need 0 or a multiple of 32 up to 16384",
+                d->dense_inter);
+  if (!(d->eps > 0.0f)) return fail(MOE_ERR_ARG, "eps must be > 0");
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_ARG, "act_dtype=%d unknown", d->act_dtype);
+  if (d->slot_dtype != MOE_F32 && d->slot_dtype != MOE_BF16)
+    return fail(MOE_ERR_ARG, "slot_dtype=%d unknown", d->slot_dtype);
+  if (d->act_dtype == MOE_F32 && d->slot_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "act_dtype F32 requires slot_dtype F32");
+  return MOE_OK;
+}
+
+int check_tokens(const moe_dims* d, int32_t T) {
+  if (T < 0 || T > 65536) return fail(MOE_ERR_ARG, "T=%d: need 0..65536", T);
+  if ((long long)T * d->top_k > (1 << 20))
+    return fail(MOE_ERR_UNSUPPORTED, "T*top_k=%lld exceeds 2^20", (long long)T * d->top_k);
+  return MOE_OK;
+}
+
+#define REQUIRE_PTR(p)                                                                   \
+  do {                                                                                   \
+    if (!(p)) return fail(MOE_ERR_ARG, "%s is NULL", #p);                                \
+    if (!aligned16(p)) return fail(MOE_ERR_ARG, "%s is not 16-byte aligned", #p);        \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                                  \
+  do {                                                                                   \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// Workspace regions (byte offsets), all 256-byte aligned, monotone in T so
+// that a workspace sized for max_tokens serves every T <= max_tokens.
+struct Layout {
+  size_t r0, r, logits;             // router
+  size_t blk_counts, local_rank;    // dispatch
+  size_t h;                         // expert gate_up output
+  size_t idx, w, counts, offsets, sorted, y;  // experts-only path / layer
+  size_t xd, xm, hd, dn;            // layer only
+  size_t total;
+};
+
+Layout layout(const moe_dims* d, long long T) {
+  Layout L{};
+  const long long S = T * d->top_k;
+  const long long nblk = (S + 1023) / 1024;
+  const size_t act = dtype_size(d->act_dtype), slot = dtype_size(d->slot_dtype);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.r0 = take(4 * T);
+  L.r = take(4 * T);
+  L.logits = take(4 * T * d->num_experts);
+  L.blk_counts = take(4 * nblk * d->num_experts);
+  L.local_rank = take(4 * S);
+  L.h = take(act * S * d->expert_inter);
+  L.idx = take(4 * S);
+  L.w = take(4 * S);
+  L.counts = take(4 * (size_t)d->num_experts);
+  L.offsets = take(4 * (size_t)(d->num_experts + 1));
+  L.sorted = take(4 * S);
+  L.y = take(slot * S * d->hidden);
+  L.xd = take(act * T * d->hidden);
+  L.xm = take(act * T * d->hidden);
+  L.hd = take(act * T * d->dense_inter);
+  L.dn = take(slot * T * d->hidden);
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_dims* d, int32_t T, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(d, T).total;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T=%d", ws_bytes, need,
+                T);
+  return MOE_OK;
+}
+
+// ---- launch sequences (arguments already checked) -------------------------
+
+int run_router(const moe_dims* d, int32_t T, const void* x, const float* router_w,
+               const float* router_scale, const float* pes, const float* pre_gain,
+               int32_t* idx, float* w, void* ws, hipStream_t s) {
+  const Layout L = layout(d, T);
+  moe::RouterArgs a{};
+  a.T = T; a.H = d->hidden; a.E = d->num_experts; a.K = d->top_k; a.eps = d->eps;
+  a.x_bf16 = d->act_dtype == MOE_BF16;
+  a.x = x; a.pre_gain = pre_gain; a.router_w = router_w; a.router_scale = router_scale;
+  a.per_expert_scale = pes; a.topk_idx = idx; a.topk_w = w;
+  a.ws_r0 = at<float>(ws, L.r0); a.ws_r = at<float>(ws, L.r);
+  a.ws_logits = at<float>(ws, L.logits);
+  hipError_t e = moe::launch_router(a, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router");
+}
+
+int run_dispatch(const moe_dims* d, int32_t T, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
+  const Layout L = layout(d, T);
+  moe::DispatchArgs a{};
+  a.T = T; a.E = d->num_experts; a.K = d->top_k;
+  a.topk_idx = idx; a.counts = counts; a.offsets = offsets; a.sorted_slots = sorted;
+  a.ws_blk_counts = at<int32_t>(ws, L.blk_counts);
+  a.ws_local_rank = at<int32_t>(ws, L.local_rank);
+  hipError_t e = moe::launch_dispatch(a, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dispatch");
+}
+
+int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_gate_up,
+                   const void* w_down, const float* topk_w, const int32_t* offsets,
+                   const int32_t* sorted, void* y, void* ws, hipStream_t s) {
+  const Layout L = layout(d, T);
+  const size_t act = dtype_size(d->act_dtype);
+  const long long H = d->hidden, I = d->expert_inter;
+  moe::GateUpArgs g{};
+  g.T = T; g.H = d->hidden; g.N = d->expert_inter; g.E = d->num_experts; g.K = d->top_k;
+  g.rows = T * d->top_k; g.ident = false; g.bf16 = d->act_dtype == MOE_BF16;
+  g.x = x;
+  g.w_gate = w_gate_up;
+  g.w_up = static_cast<const char*>(w_gate_up) + act * I * H;
+  g.w_stride = 2 * I * H;
+  g.offsets = offsets; g.sorted_slots = sorted;
+  g.h = at<void>(ws, L.h);
+  hipError_t e = moe::launch_gate_up(g, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn (gate_up)");
+  moe::DownArgs dn{};
+  dn.T = T; dn.H = d->hidden; dn.N = d->expert_inter; dn.E = d->num_experts; dn.K = d->top_k;
+  dn.rows = g.rows; dn.ident = false; dn.bf16 = g.bf16; dn.y_bf16 = d->slot_dtype == MOE_BF16;
+  dn.h = g.h; dn.w_down = w_down; dn.w_stride = H * I;
+  dn.offsets = offsets; dn.sorted_slots = sorted; dn.topk_w = topk_w; dn.y = y;
+  e = moe::launch_down(dn, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn (down)");
+}
+
+int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend, void* out,
+                hipStream_t s) {
+  moe::CombineArgs a{};
+  a.T = T; a.H = d->hidden; a.K = d->top_k;
+  a.y_bf16 = d->slot_dtype == MOE_BF16; a.act_bf16 = d->act_dtype == MOE_BF16;
+  a.y = y; a.addend = addend; a.out = out;
+  hipError_t e = moe::launch_combine(a, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  if (check_tokens(dims, max_tokens) != MOE_OK) return 0;
+  return layout(dims, max_tokens).total;
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_router(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+               const float* router_scale, const float* per_expert_scale,
+               const float* pre_norm_gain, int32_t* topk_idx, float* topk_w, void* ws,
+               size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(router_w); REQUIRE_PTR(router_scale);
+  REQUIRE_PTR(per_expert_scale); OPTIONAL_PTR(pre_norm_gain);
+  REQUIRE_PTR(topk_idx); REQUIRE_PTR(topk_w);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_router(dims, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain,
+                    topk_idx, topk_w, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(topk_idx); REQUIRE_PTR(expert_counts); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_dispatch(dims, T, topk_idx, expert_counts, expert_offsets, sorted_slots, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,
+                   const void* w_down, const float* topk_w, const int32_t* expert_offsets,
+                   const int32_t* sorted_slots, void* y_slots, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(expert_offsets); REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_expert_ffn(dims, T, x, w_gate_up, w_down, topk_w, expert_offsets, sorted_slots,
+                        y_slots, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_dims* dims, int32_t T, const void* y_slots, const void* addend,
+                void* out, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(y_slots); OPTIONAL_PTR(addend); REQUIRE_PTR(out);
+  return run_combine(dims, T, y_slots, addend, out, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                const float* router_scale, const float* per_expert_scale,
+                const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
+                float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(router_w); REQUIRE_PTR(router_scale);
+  REQUIRE_PTR(per_expert_scale); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(out);
+  OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(dims, T);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  void* y = at<void>(ws, L.y);
+  if ((rc = run_router(dims, T, x, router_w, router_scale, per_expert_scale, nullptr, idx, w, ws,
+                       s)))
+    return rc;
+  if ((rc = run_dispatch(dims, T, idx, counts, offsets, sorted, ws, s))) return rc;
+  if ((rc = run_expert_ffn(dims, T, x, w_gate_up, w_down, w, offsets, sorted, y, ws, s)))
+    return rc;
+  return run_combine(dims, T, y, nullptr, out, s);
+}
+
+int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
+                     const gemma4_ffn_weights* wt, void* out, float* ffn_out,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if (dims->dense_inter <= 0)
+    return fail(MOE_ERR_UNSUPPORTED, "gemma4_ffn_block needs dense_inter > 0");
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  if (!wt) return fail(MOE_ERR_ARG, "weights is NULL");
+  REQUIRE_PTR(residual); REQUIRE_PTR(out); OPTIONAL_PTR(ffn_out);
+  OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
+  REQUIRE_PTR(wt->g_pre); REQUIRE_PTR(wt->g_pre2); REQUIRE_PTR(wt->g_post1);
+  REQUIRE_PTR(wt->g_post2); REQUIRE_PTR(wt->g_post);
+  REQUIRE_PTR(wt->dense_gate); REQUIRE_PTR(wt->dense_up); REQUIRE_PTR(wt->dense_down);
+  REQUIRE_PTR(wt->router_w); REQUIRE_PTR(wt->router_scale); REQUIRE_PTR(wt->per_expert_scale);
+  REQUIRE_PTR(wt->w_gate_up); REQUIRE_PTR(wt->w_down);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(dims, T);
+  const bool bf = dims->act_dtype == MOE_BF16;
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  void* y = at<void>(ws, L.y);
+  void* xd = at<void>(ws, L.xd);
+  void* xm = at<void>(ws, L.xm);
+  void* hd = at<void>(ws, L.hd);
+  void* dn = at<void>(ws, L.dn);
+
+  moe::PreNormArgs pn{};
+  pn.T = T; pn.H = dims->hidden; pn.eps = dims->eps; pn.bf16 = bf;
+  pn.x = residual; pn.g_pre = wt->g_pre; pn.g_pre2 = wt->g_pre2; pn.xd = xd; pn.xm = xm;
+  hipError_t e = moe::launch_prenorm(pn, s);
+  if (e != hipSuccess) return hip_fail(e, "gemma4_ffn_block (prenorm)");
+
+  if ((rc = run_router(dims, T, residual, wt->router_w, wt->router_scale, wt->per_expert_scale,
+                       wt->g_pre2, idx, w, ws, s)))
+    return rc;
+  if ((rc = run_dispatch(dims, T, idx, counts, offsets, sorted, ws, s))) return rc;
+  if ((rc = run_expert_ffn(dims, T, xm, wt->w_gate_up, wt->w_down, w, offsets, sorted, y, ws, s)))
+    return rc;
+
+  moe::GateUpArgs g{};
+  g.T = T; g.H = dims->hidden; g.N = dims->dense_inter; g.E = 1; g.K = 1; g.rows = T;
+  g.ident = true; g.bf16 = bf; g.x = xd; g.w_gate = wt->dense_gate; g.w_up = wt->dense_up;
+  g.w_stride = 0; g.offsets = nullptr; g.sorted_slots = nullptr; g.h = hd;
+  if ((e = moe::launch_gate_up(g, s)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (dense gate_up)");
+  moe::DownArgs dd{};
+  dd.T = T; dd.H = dims->hidden; dd.N = dims->dense_inter; dd.E = 1; dd.K = 1; dd.rows = T;
+  dd.ident = true; dd.bf16 = bf; dd.y_bf16 = dims->slot_dtype == MOE_BF16; dd.h = hd;
+  dd.w_down = wt->dense_down; dd.w_stride = 0; dd.offsets = nullptr; dd.sorted_slots = nullptr;
+  dd.topk_w = nullptr; dd.y = dn;
+  if ((e = moe::launch_down(dd, s)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (dense down)");
+
+  moe::EpilogueArgs ep{};
+  ep.T = T; ep.H = dims->hidden; ep.K = dims->top_k; ep.eps = dims->eps;
+  ep.layer_scalar = wt->layer_scalar; ep.y_bf16 = dims->slot_dtype == MOE_BF16; ep.act_bf16 = bf;
+  ep.y = y; ep.dn = dn; ep.x = residual; ep.g_post1 = wt->g_post1; ep.g_post2 = wt->g_post2;
+  ep.g_post = wt->g_post; ep.out = out; ep.ffn_out = ffn_out;
+  if ((e = moe::launch_block_epilogue(ep, s)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (epilogue)");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+"""Python binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function takes torch tensors that live on the GPU and passes their
+device pointers and sizes to the C ABI; all arithmetic runs in the library's
+HIP kernels.  torch supplies the memory and the stream (the current stream
+unless one is given).  If libmoe.so has not been built, importing this module
+raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("expert_inter", ctypes.c_int32),
+                ("dense_inter", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("slot_dtype", ctypes.c_int32)]
+
+
+class Gemma4FfnWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "g_pre", "g_pre2", "g_post1", "g_post2", "g_post", "dense_gate", "dense_up",
+        "dense_down", "router_w", "router_scale", "per_expert_scale", "w_gate_up", "w_down")] + \
+        [("layer_scalar", ctypes.c_float)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmoe error {code}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_moe_transformer_router_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(MoeDims)
+    L.moe_workspace_size.argtypes = [D, I32]
+    L.moe_workspace_size.restype = SZ
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_router.argtypes = [D, I32] + [P] * 8 + [SZ, P]
+    L.moe_dispatch.argtypes = [D, I32] + [P] * 5 + [SZ, P]
+    L.moe_expert_ffn.argtypes = [D, I32] + [P] * 8 + [SZ, P]
+    L.moe_combine.argtypes = [D, I32, P, P, P, P]
+    L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
+    L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
+        [SZ, P]
+    for f in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "gemma4_ffn_block"):
+        getattr(L, f).restype = ctypes.c_int
+    return L
+
+
+_lib = _load()
+
+
+def raw():
+    """The ctypes library object (for tests of the exported symbols)."""
+    return _lib
+
+
+def dims(hidden, num_experts, top_k, expert_inter, dense_inter=0, eps=1e-6, act=MOE_BF16,
+         slot=MOE_F32) -> MoeDims:
+    """Layer dimensions.  The per-slot expert outputs default to fp32: rounding
+    them to bf16 adds a third rounding stage to the bf16 path."""
+    return MoeDims(hidden, num_experts, top_k, expert_inter, dense_inter, eps, act, slot)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, _lib.moe_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def workspace_size(d: MoeDims, max_tokens: int) -> int:
+    n = _lib.moe_workspace_size(ctypes.byref(d), max_tokens)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, last_error())
+    return n
+
+
+def workspace(d: MoeDims, max_tokens: int, device="cuda") -> torch.Tensor:
+    """A uint8 device buffer of moe_workspace_size bytes (256-byte aligned)."""
+    return torch.empty(workspace_size(d, max_tokens), dtype=torch.uint8, device=device)
+
+
+def moe_router(d, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain, topk_idx,
+               topk_w, ws, stream=None):
+    _check(_lib.moe_router(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(router_scale),
+                           _ptr(per_expert_scale), _ptr(pre_norm_gain), _ptr(topk_idx),
+                           _ptr(topk_w), _ptr(ws), ws.numel() if ws is not None else 0,
+                           _stream(stream)))
+
+
+def moe_dispatch(d, T, topk_idx, counts, offsets, sorted_slots, ws, stream=None):
+    _check(_lib.moe_dispatch(ctypes.byref(d), T, _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                             _ptr(sorted_slots), _ptr(ws), ws.numel() if ws is not None else 0,
+                             _stream(stream)))
+
+
+def moe_expert_ffn(d, T, x, w_gate_up, w_down, topk_w, offsets, sorted_slots, y_slots, ws,
+                   stream=None):
+    _check(_lib.moe_expert_ffn(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
+                               _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots), _ptr(y_slots),
+                               _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_combine(d, T, y_slots, addend, out, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(d), T, _ptr(y_slots), _ptr(addend), _ptr(out),
+                            _stream(stream)))
+
+
+def moe_forward(d, T, x, router_w, router_scale, per_expert_scale, w_gate_up, w_down, out,
+                topk_idx, topk_w, ws, stream=None):
+    _check(_lib.moe_forward(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(router_scale),
+                            _ptr(per_expert_scale), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+                            _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                            ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def ffn_weights(g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, dense_down,
+                router_w, router_scale, per_expert_scale, w_gate_up, w_down,
+                layer_scalar) -> Gemma4FfnWeights:
+    ts = (g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, dense_down, router_w,
+          router_scale, per_expert_scale, w_gate_up, w_down)
+    return Gemma4FfnWeights(*[_ptr(t) for t in ts], float(layer_scalar))
+
+
+def gemma4_ffn_block(d, T, residual, weights: Gemma4FfnWeights, out, ffn_out, topk_idx, topk_w,
+                     ws, stream=None):
+    _check(_lib.gemma4_ffn_block(ctypes.byref(d), T, _ptr(residual), ctypes.byref(weights),
+                                 _ptr(out), _ptr(ffn_out), _ptr(topk_idx), _ptr(topk_w),
+                                 _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)))

@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (so these tests need no GPU).  No test here launches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+lib_mod = pytest.importorskip("sparse_moe_transformer_router_amd.lib",
+                              reason="libmoe.so not built")
+L = lib_mod.raw()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_calls():
+    fns = declared_functions()
+    for name in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                 "gemma4_ffn_block", "moe_forward", "moe_workspace_size", "moe_last_error"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def D(**kw):
+    base = dict(hidden=2816, num_experts=128, top_k=8, expert_inter=704, dense_inter=2112,
+                eps=1e-6, act=lib_mod.MOE_BF16)
+    base.update(kw)
+    return lib_mod.dims(**base)
+
+
+def router(d, T, x=FAKE, ws=FAKE, ws_bytes=1 << 40, pre=None, idx=FAKE):
+    return L.moe_router(ctypes.byref(d), T, x, FAKE, FAKE, FAKE, pre, idx, FAKE, ws, ws_bytes,
+                        None)
+
+
+def test_workspace_size_is_monotone_and_rejects_bad_dims():
+    d = D()
+    sizes = [L.moe_workspace_size(ctypes.byref(d), t) for t in (1, 8, 64, 4096)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    assert L.moe_workspace_size(ctypes.byref(D(hidden=100)), 8) == 0
+    assert "hidden" in lib_mod.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=0), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=0), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=300), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=0), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=129), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=4, top_k=5), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(expert_inter=700), lib_mod.MOE_ERR_UNSUPPORTED),
+    (dict(eps=0.0), lib_mod.MOE_ERR_ARG),
+    (dict(act=7), lib_mod.MOE_ERR_ARG),
+    (dict(act=lib_mod.MOE_F32, slot=lib_mod.MOE_BF16), lib_mod.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_dims_are_rejected(kw, code):
+    assert router(D(**kw), 4) == code
+    assert lib_mod.last_error()
+
+
+def test_bad_tokens_pointers_and_workspace():
+    d = D()
+    assert router(d, -1) == lib_mod.MOE_ERR_ARG
+    assert router(d, 70000) == lib_mod.MOE_ERR_ARG
+    assert router(d, 4, x=None) == lib_mod.MOE_ERR_ARG and "x" in lib_mod.last_error()
+    assert router(d, 4, x=MISALIGNED) == lib_mod.MOE_ERR_ARG
+    assert router(d, 4, pre=MISALIGNED) == lib_mod.MOE_ERR_ARG
+    assert router(d, 4, idx=None) == lib_mod.MOE_ERR_ARG
+    assert router(d, 4, ws=None) == lib_mod.MOE_ERR_WORKSPACE
+    assert router(d, 4, ws=ctypes.c_void_p(0x10010)) == lib_mod.MOE_ERR_WORKSPACE
+    need = L.moe_workspace_size(ctypes.byref(d), 4)
+    assert router(d, 4, ws_bytes=need - 1) == lib_mod.MOE_ERR_WORKSPACE
+    assert str(need) in lib_mod.last_error()
+
+
+def test_zero_tokens_is_a_no_op_everywhere():
+    d = D()
+    dp = ctypes.byref(d)
+    assert router(d, 0, x=None, ws=None, ws_bytes=0) == lib_mod.MOE_OK
+    assert L.moe_dispatch(dp, 0, None, None, None, None, None, 0, None) == lib_mod.MOE_OK
+    assert L.moe_expert_ffn(dp, 0, *([None] * 8), 0, None) == lib_mod.MOE_OK
+    assert L.moe_combine(dp, 0, None, None, None, None) == lib_mod.MOE_OK
+    assert L.moe_forward(dp, 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
+    assert L.gemma4_ffn_block(dp, 0, None, None, None, None, None, None, None, 0,
+                              None) == lib_mod.MOE_OK
+
+
+def test_block_requires_dense_branch_and_weights():
+    d = D(dense_inter=0)
+    assert L.gemma4_ffn_block(ctypes.byref(d), 4, FAKE, None, FAKE, None, None, None, FAKE,
+                              1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    d = D()
+    assert L.gemma4_ffn_block(ctypes.byref(d), 4, FAKE, None, FAKE, None, None, None, FAKE,
+                              1 << 40, None) == lib_mod.MOE_ERR_ARG
+    w = lib_mod.Gemma4FfnWeights()
+    for f, _ in w._fields_[:-1]:
+        setattr(w, f, 0x10000)
+    w.dense_up = None
+    assert L.gemma4_ffn_block(ctypes.byref(d), 4, FAKE, ctypes.byref(w), FAKE, None, None, None,
+                              FAKE, 1 << 40, None) == lib_mod.MOE_ERR_ARG
+    assert "dense_up" in lib_mod.last_error()
+
+
+def test_other_calls_validate():
+    d = D()
+    dp = ctypes.byref(d)
+    assert L.moe_dispatch(dp, 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
+                          None) == lib_mod.MOE_ERR_ARG
+    assert L.moe_expert_ffn(dp, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                            None) == lib_mod.MOE_ERR_WORKSPACE
+    assert L.moe_combine(dp, 4, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert L.moe_forward(dp, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE,
+                         1 << 40, None) == lib_mod.MOE_ERR_ARG
