@@ -157,6 +157,18 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w
                    const int32_t* sorted_slots, void* y_slots, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately.  moe_expert_gate_up: for every expert-sorted row r of expert e
+ * (slot s = sorted_slots[r], token t = s / K),
+ * h[r,:] = gelu_tanh(gate[e] x_t) * (up[e] x_t); h: [T*K, I] act dtype (bf16 path:
+ * rounded to bf16).  moe_expert_down: y_slots[s,:] = topk_w[s] * down[e] h[r,:]. */
+int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,
+                       const int32_t* expert_offsets, const int32_t* sorted_slots, void* h,
+                       void* stream);
+int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* w_down,
+                    const float* topk_w, const int32_t* expert_offsets,
+                    const int32_t* sorted_slots, void* y_slots, void* stream);
+
 /* The experts' scatter-add: out[t] = sum_{k=0..K-1} y_slots[t,k] (fp32, k
  * ascending, no atomics) + addend[t] (if addend is not NULL).
  * y_slots slot dtype; addend and out act dtype. */

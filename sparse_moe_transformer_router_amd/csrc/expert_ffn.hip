@@ -369,6 +369,7 @@ int row_tile_bound(bool ident, int rows, int T, int E, int bm) {
 
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
+  if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_gate_up_stream(a, s);
   if (a.bf16) {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, 64), (a.N + 63) / 64);
     hipLaunchKernelGGL(gate_up_bf16_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.K, a.rows,
@@ -387,6 +388,7 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
 
 hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
+  if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_down_stream(a, s);
   if (a.bf16) {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, 64), (a.H + 127) / 128);
     const bf16* hb = static_cast<const bf16*>(a.h);

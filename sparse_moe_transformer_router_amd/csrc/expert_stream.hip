@@ -1,0 +1,283 @@
+// Decode-sized grouped expert GEMMs (few rows per expert): weight streaming.
+//
+// At decode batch sizes an expert sees a handful of rows, so the two expert
+// GEMMs are bound by reading each touched expert's weights from HBM once
+// (gate_up [2I, H] and down [H, I] of the page "Porting a 128-expert MoE
+// (Gemma-4 26B-A4B) to AWS Inferentia2", section "The architecture: a
+// dual-path FFN nobody warned me about").  These kernels keep the weight
+// operand out of LDS: every lane loads 32 contiguous bytes of one weight row
+// per 64-wide k-block straight into registers (four lanes cover a 128-byte
+// line) and feeds them to v_mfma_f32_16x16x32_bf16 as two 8-element operands;
+// the activation rows (at most 16 * MB per tile, resident in L2) are loaded
+// the same way.  The next k-block's loads are issued before the current one's
+// MFMAs.  A block's waves split the contraction; their partial sums meet in
+// LDS and are added in wave order (deterministic), then the epilogue applies
+// GELU-tanh(gate) * up (gate_up) or the routing weight and the slot scatter
+// (down).
+//
+// k mapping: in k-block kb, lane l (row or column l % 16, group g = l / 16)
+// holds k = 64 kb + 16 g + [0, 16); MFMA j of the block uses its elements
+// [8 j, 8 j + 8).  A and B use the same mapping, so each MFMA pair sums over
+// all 64 k of the block.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+union Frag {
+  uint4 u[2];
+  bf16x8 v[2];
+};
+
+__device__ __forceinline__ void ld_frag(Frag& f, const bf16* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  f.u[0] = q[0];
+  f.u[1] = q[1];
+}
+
+__device__ __forceinline__ void zero_frag(Frag& f) {
+  f.u[0] = make_uint4(0, 0, 0, 0);
+  f.u[1] = make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bool stream_tile(bool ident, int rows, const int32_t* offsets, int E,
+                                            int bm, int& e, int& row0, int& row1) {
+  if (ident) {
+    e = 0;
+    row0 = blockIdx.x * bm;
+    row1 = min(row0 + bm, rows);
+    return row0 < rows;
+  }
+  return find_row_tile(offsets, E, bm, blockIdx.x, e, row0, row1);
+}
+
+// gate_up: one block = one row tile (<= 16 * MB rows) x 16 gate + 16 up
+// columns; its WK waves split H.
+template <int WK, int MB>
+__global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
+    int H, int N, int E, int K, int rows, int ident, const bf16* __restrict__ x,
+    const bf16* __restrict__ wg, const bf16* __restrict__ wu, long long w_stride,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
+    bf16* __restrict__ h) {
+  __shared__ f32x4 red[WK][MB][2][kWave];
+  int e, row0, row1;
+  if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int fr = lane % 16, fg = lane / 16;
+  const int n = blockIdx.y * 16 + fr;
+  const bool nvalid = n < N;
+  const size_t woff = (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * H + 16 * fg;
+  const bf16* gp = wg + woff;
+  const bf16* up = wu + woff;
+  const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
+  const bf16* ap[MB];
+  bool av[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = row0 + 16 * mb + fr;
+    av[mb] = r < row1;
+    const int tok = av[mb] ? (ident ? r : sorted_slots[r] / K) : 0;
+    ap[mb] = x + (size_t)tok * H + 16 * fg;
+  }
+  const int KB = H / 64;
+  const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
+
+  f32x4 accg[MB], accu[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accg[mb] = f32x4{0, 0, 0, 0};
+    accu[mb] = f32x4{0, 0, 0, 0};
+  }
+  Frag cg, cu, ca[MB], ng, nu, na[MB];
+  auto load = [&](int kb, Frag& g, Frag& u, Frag (&a)[MB]) {
+    const int k = kb * 64;
+    if (nvalid) {
+      ld_frag(g, gp + k);
+      ld_frag(u, up + k);
+    } else {
+      zero_frag(g);
+      zero_frag(u);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb < nmb && av[mb]) ld_frag(a[mb], ap[mb] + k);
+      else zero_frag(a[mb]);
+    }
+  };
+  if (kb0 < kb1) load(kb0, cg, cu, ca);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    if (kb + 1 < kb1) load(kb + 1, ng, nu, na);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb < nmb) {
+          accg[mb] = mfma16(ca[mb].v[j], cg.v[j], accg[mb]);
+          accu[mb] = mfma16(ca[mb].v[j], cu.v[j], accu[mb]);
+        }
+    cg = ng;
+    cu = nu;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ca[mb] = na[mb];
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    red[wave][mb][0][lane] = accg[mb];
+    red[wave][mb][1][lane] = accu[mb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nmb) break;
+    f32x4 g = red[0][mb][0][lane], u = red[0][mb][1][lane];
+#pragma unroll
+    for (int w = 1; w < WK; ++w) {
+      g += red[w][mb][0][lane];
+      u += red[w][mb][1][lane];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 16 * mb + 4 * fg + r;
+      if (row < row1 && nvalid) h[(size_t)row * N + n] = (bf16)(gelu_tanh(g[r]) * u[r]);
+    }
+  }
+}
+
+// down: one block = one row tile x 16 * WN output columns; WK waves split
+// the contraction (the intermediate width N).
+template <int WN, int WK, int MB, typename YT>
+__global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
+    int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
+    const bf16* __restrict__ wd, long long w_stride, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
+    YT* __restrict__ y) {
+  __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][kWave];
+  int e, row0, row1;
+  if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wn = wave % WN, wk = wave / WN;
+  const int fr = lane % 16, fg = lane / 16;
+  const int n = blockIdx.y * 16 * WN + 16 * wn + fr;
+  const bool nvalid = n < H;
+  const bf16* bp = wd + (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * N + 16 * fg;
+  const int nmb = (row1 - row0 + 15) / 16;
+  const bf16* ap[MB];
+  bool av[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = row0 + 16 * mb + fr;
+    av[mb] = r < row1;
+    ap[mb] = hbuf + (size_t)(av[mb] ? r : 0) * N + 16 * fg;
+  }
+  const int KB = (N + 63) / 64;
+  const int kb0 = wk * KB / WK, kb1 = (wk + 1) * KB / WK;
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0, 0, 0, 0};
+  Frag cb, ca[MB], nbf, na[MB];
+  auto load = [&](int kb, Frag& b, Frag (&a)[MB]) {
+    const int k = kb * 64;
+    const bool kv = k + 16 * fg < N;  // N % 32 == 0: a 16-wide group is all in or all out
+    if (nvalid && kv) ld_frag(b, bp + k);
+    else zero_frag(b);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb < nmb && av[mb] && kv) ld_frag(a[mb], ap[mb] + k);
+      else zero_frag(a[mb]);
+    }
+  };
+  if (kb0 < kb1) load(kb0, cb, ca);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    if (kb + 1 < kb1) load(kb + 1, nbf, na);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb < nmb) acc[mb] = mfma16(ca[mb].v[j], cb.v[j], acc[mb]);
+    cb = nbf;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ca[mb] = na[mb];
+  }
+  if constexpr (WK > 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      acc[mb] = red[wn][mb][lane];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) acc[mb] += red[wn + w * WN][mb][lane];
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nmb) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 16 * mb + 4 * fg + r;
+      if (row >= row1 || !nvalid) continue;
+      const int slot = ident ? row : sorted_slots[row];
+      const float sc = ident ? 1.0f : topk_w[slot];
+      y[(size_t)slot * H + n] = from_f32<YT>(sc * acc[mb][r]);
+    }
+  }
+}
+
+int tile_bound(bool ident, int rows, int T, int E, int bm) {
+  if (ident) return (rows + bm - 1) / bm;
+  long long a = ((long long)rows + (long long)E * (bm - 1)) / bm;
+  long long b = (long long)E * ((T + bm - 1) / bm);
+  return (int)(a < b ? a : b);
+}
+
+template <int WK, int MB>
+void launch_gu(const GateUpArgs& a, hipStream_t s) {
+  dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.N + 15) / 16);
+  hipLaunchKernelGGL((gate_up_stream_kernel<WK, MB>), grid, dim3(64 * WK), 0, s, a.H, a.N, a.E,
+                     a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
+                     static_cast<const bf16*>(a.w_gate), static_cast<const bf16*>(a.w_up),
+                     a.w_stride, a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
+}
+
+template <int WN, int WK, int MB, typename YT>
+void launch_dn(const DownArgs& a, hipStream_t s) {
+  dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.H + 16 * WN - 1) / (16 * WN));
+  hipLaunchKernelGGL((down_stream_kernel<WN, WK, MB, YT>), grid, dim3(64 * WN * WK), 0, s, a.H,
+                     a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
+                     static_cast<const bf16*>(a.w_down), a.w_stride, a.offsets, a.sorted_slots,
+                     a.topk_w, static_cast<YT*>(a.y));
+}
+
+template <typename YT>
+void launch_dn_t(const DownArgs& a, hipStream_t s) {
+  if (a.T <= 8) launch_dn<2, 2, 1, YT>(a, s);
+  else if (a.T <= 16) launch_dn<4, 1, 1, YT>(a, s);
+  else launch_dn<4, 1, 2, YT>(a, s);
+}
+
+}  // namespace
+
+bool use_stream_kernels(int T, bool ident) { return T <= (ident ? 32 : 64); }
+
+hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
+  if (a.T <= 8) launch_gu<8, 1>(a, s);
+  else if (a.T <= 16) launch_gu<4, 1>(a, s);
+  else launch_gu<4, 2>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_stream(const DownArgs& a, hipStream_t s) {
+  if (a.y_bf16) launch_dn_t<bf16>(a, s);
+  else launch_dn_t<float>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

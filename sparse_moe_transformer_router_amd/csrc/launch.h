@@ -75,6 +75,11 @@ struct DownArgs {
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
+// Decode-sized variants (few rows per group): weight-streaming kernels.
+bool use_stream_kernels(int T, bool ident);
+hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s);
+hipError_t launch_down_stream(const DownArgs& a, hipStream_t s);
+
 struct CombineArgs {
   int T, H, K;
   bool y_bf16, act_bf16;

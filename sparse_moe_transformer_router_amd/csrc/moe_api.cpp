@@ -163,10 +163,8 @@ int run_dispatch(const moe_dims* d, int32_t T, const int32_t* idx, int32_t* coun
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dispatch");
 }
 
-int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_gate_up,
-                   const void* w_down, const float* topk_w, const int32_t* offsets,
-                   const int32_t* sorted, void* y, void* ws, hipStream_t s) {
-  const Layout L = layout(d, T);
+int run_gate_up(const moe_dims* d, int32_t T, const void* x, const void* w_gate_up,
+                const int32_t* offsets, const int32_t* sorted, void* h, hipStream_t s) {
   const size_t act = dtype_size(d->act_dtype);
   const long long H = d->hidden, I = d->expert_inter;
   moe::GateUpArgs g{};
@@ -176,17 +174,31 @@ int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_ga
   g.w_gate = w_gate_up;
   g.w_up = static_cast<const char*>(w_gate_up) + act * I * H;
   g.w_stride = 2 * I * H;
-  g.offsets = offsets; g.sorted_slots = sorted;
-  g.h = at<void>(ws, L.h);
+  g.offsets = offsets; g.sorted_slots = sorted; g.h = h;
   hipError_t e = moe::launch_gate_up(g, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn (gate_up)");
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert gate_up");
+}
+
+int run_down(const moe_dims* d, int32_t T, const void* h, const void* w_down,
+             const float* topk_w, const int32_t* offsets, const int32_t* sorted, void* y,
+             hipStream_t s) {
   moe::DownArgs dn{};
   dn.T = T; dn.H = d->hidden; dn.N = d->expert_inter; dn.E = d->num_experts; dn.K = d->top_k;
-  dn.rows = g.rows; dn.ident = false; dn.bf16 = g.bf16; dn.y_bf16 = d->slot_dtype == MOE_BF16;
-  dn.h = g.h; dn.w_down = w_down; dn.w_stride = H * I;
+  dn.rows = T * d->top_k; dn.ident = false; dn.bf16 = d->act_dtype == MOE_BF16;
+  dn.y_bf16 = d->slot_dtype == MOE_BF16;
+  dn.h = h; dn.w_down = w_down; dn.w_stride = (long long)d->hidden * d->expert_inter;
   dn.offsets = offsets; dn.sorted_slots = sorted; dn.topk_w = topk_w; dn.y = y;
-  e = moe::launch_down(dn, s);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn (down)");
+  hipError_t e = moe::launch_down(dn, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down");
+}
+
+int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_gate_up,
+                   const void* w_down, const float* topk_w, const int32_t* offsets,
+                   const int32_t* sorted, void* y, void* ws, hipStream_t s) {
+  void* h = at<void>(ws, layout(d, T).h);
+  int rc = run_gate_up(d, T, x, w_gate_up, offsets, sorted, h, s);
+  if (rc) return rc;
+  return run_down(d, T, h, w_down, topk_w, offsets, sorted, y, s);
 }
 
 int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend, void* out,
@@ -254,6 +266,32 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w
   if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
   return run_expert_ffn(dims, T, x, w_gate_up, w_down, topk_w, expert_offsets, sorted_slots,
                         y_slots, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,
+                       const int32_t* expert_offsets, const int32_t* sorted_slots, void* h,
+                       void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(h);
+  return run_gate_up(dims, T, x, w_gate_up, expert_offsets, sorted_slots, h,
+                     static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* w_down,
+                    const float* topk_w, const int32_t* expert_offsets,
+                    const int32_t* sorted_slots, void* y_slots, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(h); REQUIRE_PTR(w_down); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
+  return run_down(dims, T, h, w_down, topk_w, expert_offsets, sorted_slots, y_slots,
+                  static_cast<hipStream_t>(stream));
 }
 
 int moe_combine(const moe_dims* dims, int32_t T, const void* y_slots, const void* addend,

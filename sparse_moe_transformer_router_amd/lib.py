@@ -55,12 +55,14 @@ def _load():
     L.moe_router.argtypes = [D, I32] + [P] * 8 + [SZ, P]
     L.moe_dispatch.argtypes = [D, I32] + [P] * 5 + [SZ, P]
     L.moe_expert_ffn.argtypes = [D, I32] + [P] * 8 + [SZ, P]
+    L.moe_expert_gate_up.argtypes = [D, I32] + [P] * 6
+    L.moe_expert_down.argtypes = [D, I32] + [P] * 7
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
         [SZ, P]
-    for f in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-              "gemma4_ffn_block"):
+    for f in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+              "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -134,6 +136,17 @@ def moe_expert_ffn(d, T, x, w_gate_up, w_down, topk_w, offsets, sorted_slots, y_
     _check(_lib.moe_expert_ffn(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
                                _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots), _ptr(y_slots),
                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_expert_gate_up(d, T, x, w_gate_up, offsets, sorted_slots, h, stream=None):
+    _check(_lib.moe_expert_gate_up(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up), _ptr(offsets),
+                                   _ptr(sorted_slots), _ptr(h), _stream(stream)))
+
+
+def moe_expert_down(d, T, h, w_down, topk_w, offsets, sorted_slots, y_slots, stream=None):
+    _check(_lib.moe_expert_down(ctypes.byref(d), T, _ptr(h), _ptr(w_down), _ptr(topk_w),
+                                _ptr(offsets), _ptr(sorted_slots), _ptr(y_slots),
+                                _stream(stream)))
 
 
 def moe_combine(d, T, y_slots, addend, out, stream=None):

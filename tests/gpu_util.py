@@ -50,3 +50,35 @@ def ws_logits_view(ws: torch.Tensor, T: int, E: int) -> torch.Tensor:
     a = lambda n: (n + 255) // 256 * 256  # noqa: E731
     off = 2 * a(4 * T)
     return ws[off: off + 4 * T * E].view(torch.float32).view(T, E)
+
+
+def bf16_path_bound(x, gate_up, down, idx, w):
+    """Per-element error bound of the bf16 expert path against the exact result.
+
+    The bf16 path rounds twice: h = gelu(gate) * up is rounded to bf16 before
+    the down projection, and the combined output is rounded to bf16.  A bf16
+    round-to-nearest moves a value v by at most 2^-8 |v| (8 significant bits),
+    so |gpu - exact| <= 2^-8 |out| + sum_k |w_k| (|W_d[e_k]| @ |h_k|) 2^-8, plus
+    fp32 accumulation error (taken as 1e-5 of the summed magnitudes).  Inputs
+    are the exactly widened bf16 values.  Returns (bound [T,H], exact [T,H])."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    E, I2, _ = gate_up.shape
+    I = I2 // 2
+    K = idx.shape[1]
+    exact = np.zeros((T, H))
+    hterm = np.zeros((T, H))
+    mag = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            gu = gate_up[e].astype(np.float64) @ x[t]
+            g, u = gu[:I], gu[I:]
+            hh = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))) * u
+            wd = down[e].astype(np.float64)
+            exact[t] += float(w[t, k]) * (wd @ hh)
+            a = abs(float(w[t, k])) * (np.abs(wd) @ np.abs(hh))
+            hterm[t] += a
+            mag[t] += a
+    bound = 2.0 ** -8 * np.abs(exact) * 1.001 + 2.0 ** -8 * hterm + 1e-5 * mag
+    return bound, exact
