@@ -2,8 +2,8 @@
 """Throughput of the Gemma-4 26B-A4B mixture-of-experts block on one MI355X.
 
 One step = one pass of the experts-only hot path over one batch of decode
-tokens: router -> dispatch -> expert gate_up -> expert down -> combine, each a
-call into libmoe (the C ABI) on the current stream.  The workload is the 26B-A4B
+tokens: route (router + dispatch) -> expert gate_up -> expert down -> combine,
+each a call into libmoe (the C ABI) on the current stream.  The workload is the 26B-A4B
 layer's experts (128 experts, top-8, hidden 2816, expert intermediate 704,
 bf16 weights, fp32 router) at a decode batch of 64 tokens; batches of 1, 8 and
 32 and a 4096-token prefill are measured the same way and reported in the same
@@ -41,9 +41,9 @@ BF16_PEAK_TFLOPS = 2500.0
 GATE_UP_BYTES = 2 * I * H * 2     # one expert's gate_up, bf16
 DOWN_BYTES = H * I * 2            # one expert's down, bf16
 ROUTER_BYTES = E * H * 4 + H * 4 + E * 4
-KERNEL_SRC = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc", "expert_ffn.hip")
+KERNEL_SRC = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc", "expert_stream.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_decode_b64_traffic.txt")
-SEGMENTS = ("router", "dispatch", "gate_up", "down", "combine")
+SEGMENTS = ("route", "gate_up", "down", "combine")
 
 
 def parse():
@@ -112,16 +112,15 @@ class Runner:
         rw, rs, pes, gu, dn = copy
         rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
         rec(0)
-        lib.moe_router(d, T, x, rw, rs, pes, None, self.idx, self.w, self.ws)
+        lib.moe_route(d, T, x, rw, rs, pes, None, self.idx, self.w, self.counts, self.offsets,
+                      self.sorted, self.ws)
         rec(1)
-        lib.moe_dispatch(d, T, self.idx, self.counts, self.offsets, self.sorted, self.ws)
-        rec(2)
         lib.moe_expert_gate_up(d, T, x, gu, self.offsets, self.sorted, self.h)
-        rec(3)
+        rec(2)
         lib.moe_expert_down(d, T, self.h, dn, self.w, self.offsets, self.sorted, self.y)
-        rec(4)
+        rec(3)
         lib.moe_combine(d, T, self.y, None, self.out)
-        rec(5)
+        rec(4)
 
 
 def time_steps(torch, runner, xs, copies, steps, warmup):
@@ -280,7 +279,7 @@ def main():
                    "tokens": args.batch, "experts": E, "top_k": K, "hidden": H,
                    "expert_inter": I, "weights": "bf16", "router": "fp32",
                    "weight_copies_rotated": args.copies, "input_batches_rotated": args.xbatches},
-        "roofline": {"bound": "hbm", "kernel": "gate_up_bf16 (expert gate_up + GELU)",
+        "roofline": {"bound": "hbm", "kernel": "gate_up_stream_kernel (expert gate_up + GELU, decode)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(),
                      "algorithmic_bytes_per_launch": head["gate_up_bytes"],

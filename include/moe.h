@@ -138,6 +138,15 @@ int moe_router(const moe_dims* dims, int32_t T, const void* x, const float* rout
                const float* pre_norm_gain, int32_t* topk_idx, float* topk_w,
                void* ws, size_t ws_bytes, void* stream);
 
+/* moe_router followed by moe_dispatch of its result, in one call (for small
+ * batches the dispatch runs inside the router's top-K kernel).  Outputs are
+ * those of the two calls. */
+int moe_route(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+              const float* router_scale, const float* per_expert_scale,
+              const float* pre_norm_gain, int32_t* topk_idx, float* topk_w,
+              int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots, void* ws,
+              size_t ws_bytes, void* stream);
+
 /* Groups the T*K token-slots by expert (the gather side of the experts'
  * sparse loop): expert_counts[e] = #slots with topk_idx == e, expert_offsets
  * their exclusive prefix sum (expert_offsets[E] = T*K), sorted_slots the slot
@@ -175,8 +184,8 @@ int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* 
 int moe_combine(const moe_dims* dims, int32_t T, const void* y_slots, const void* addend,
                 void* out, void* stream);
 
-/* Experts-only path in one call: moe_router (no pre-norm), moe_dispatch,
- * moe_expert_ffn, moe_combine (no addend).  If topk_idx / topk_w are not NULL
+/* Experts-only path in one call: moe_route (no pre-norm), moe_expert_ffn,
+ * moe_combine (no addend).  If topk_idx / topk_w are not NULL
  * the routing is also written there. */
 int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
                 const float* router_scale, const float* per_expert_scale,

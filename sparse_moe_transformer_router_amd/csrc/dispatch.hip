@@ -9,126 +9,40 @@
 //
 // Slots are cut into chunks of 1024 (one 16-wave block each).  Inside a
 // wave, a slot's rank among equal experts is the popcount of the lanes below
-// it that carry the same expert (found with 8 ballots over the bits of the
-// expert id).  Per-wave counts are scanned across the block's waves; per-block
-// counts are scanned across blocks by a single-block kernel, which also forms
-// the expert offsets.  A lone chunk (T*K <= 1024, every decode batch) runs all
-// of it in one kernel.
-#include "common.h"
+// it that carry the same expert (8 ballots over the bits of the expert id).
+// Per-wave counts are scanned across the block's waves; per-block counts are
+// scanned across blocks by a single-block kernel, which also forms the expert
+// offsets.  A lone chunk (T*K <= 1024, every decode batch) runs all of it in
+// one kernel; the router can also run that lone-chunk dispatch itself, right
+// after its top-K (see the router kernels).
 #include "launch.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
 
-constexpr int kChunkSlots = 1024;
-constexpr int kWaves = kChunkSlots / kWave;  // 16
-constexpr int kMaxE = 256;
-
-// Rank of this lane's expert among the lanes below it holding the same
-// expert, and whether this lane is the last of its group.  Invalid lanes
-// (valid == false) take part in no group.
-__device__ __forceinline__ void wave_match_rank(int e, bool valid, int& rank, int& group_count,
-                                                bool& last) {
-  const int lane = lane_id();
-  unsigned long long m = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bool bit = (e >> b) & 1;
-    const unsigned long long bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  rank = __popcll(m & below);
-  group_count = __popcll(m);
-  const unsigned long long above = (lane == kWave - 1) ? 0ull : (m >> (lane + 1));
-  last = valid && above == 0ull;
-}
-
-// Per-chunk work shared by both paths: fills wave_base[w][e] (exclusive scan
-// over the chunk's waves of each expert's count), block totals in
-// totals[e], and returns the slot's rank within the chunk among equal
-// experts.  Must be called by all 1024 threads.
-__device__ __forceinline__ int chunk_rank(const int32_t* __restrict__ topk_idx, int S, int E,
-                                          int chunk, int (*wave_base)[kMaxE], int* totals,
-                                          int& e_out, bool& valid_out) {
-  const int tid = threadIdx.x, wave = tid / kWave;
-  for (int i = tid; i < kWaves * kMaxE; i += kChunkSlots) (&wave_base[0][0])[i] = 0;
-  __syncthreads();
-  const int s = chunk * kChunkSlots + tid;
-  const bool valid = s < S;
-  const int e = valid ? topk_idx[s] : 0;
-  int rank, cnt;
-  bool last;
-  wave_match_rank(e, valid, rank, cnt, last);
-  if (last) wave_base[wave][e] = cnt;
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = wave_base[w][tid];
-      wave_base[w][tid] = run;
-      run += c;
-    }
-    totals[tid] = run;
-  }
-  __syncthreads();
-  e_out = e;
-  valid_out = valid;
-  return valid ? wave_base[wave][e] + rank : 0;
-}
-
-// Exclusive scan of counts[0..E) into offsets[0..E] by one wave (E <= 256).
-__device__ __forceinline__ void wave_offsets(const int* counts, int E, int32_t* offsets) {
-  const int lane = lane_id();
-  int c[4], local = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane * 4 + j;
-    c[j] = e < E ? counts[e] : 0;
-    local += c[j];
-  }
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  int run = incl - local;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane * 4 + j;
-    if (e < E) offsets[e] = run;
-    run += c[j];
-  }
-  if (lane == kWave - 1) offsets[E] = incl;
-}
-
 __global__ __launch_bounds__(kChunkSlots) void dispatch_single_kernel(
     const int32_t* __restrict__ topk_idx, int S, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots) {
-  __shared__ int wave_base[kWaves][kMaxE];
+  __shared__ int wave_base[kChunkWaves][kMaxE];
   __shared__ int totals[kMaxE];
   __shared__ int offs[kMaxE + 1];
-  int e;
-  bool valid;
-  const int r = chunk_rank(topk_idx, S, E, 0, wave_base, totals, e, valid);
-  if (threadIdx.x < kWave) wave_offsets(totals, E, offs);
-  __syncthreads();
-  if (valid) sorted_slots[offs[e] + r] = threadIdx.x;
-  if (threadIdx.x < E) counts[threadIdx.x] = totals[threadIdx.x];
-  if (threadIdx.x <= E) offsets[threadIdx.x] = offs[threadIdx.x];
+  const bool valid = (int)threadIdx.x < S;
+  const int e = valid ? topk_idx[threadIdx.x] : 0;
+  dispatch_lone_chunk(e, valid, E, counts, offsets, sorted_slots, wave_base, totals, offs);
 }
 
 __global__ __launch_bounds__(kChunkSlots) void dispatch_rank_kernel(
     const int32_t* __restrict__ topk_idx, int S, int E, int32_t* __restrict__ blk_counts,
     int32_t* __restrict__ local_rank) {
-  __shared__ int wave_base[kWaves][kMaxE];
+  __shared__ int wave_base[kChunkWaves][kMaxE];
   __shared__ int totals[kMaxE];
-  int e;
-  bool valid;
-  const int r = chunk_rank(topk_idx, S, E, blockIdx.x, wave_base, totals, e, valid);
-  if (valid) local_rank[blockIdx.x * kChunkSlots + threadIdx.x] = r;
-  if (threadIdx.x < E) blk_counts[(size_t)blockIdx.x * E + threadIdx.x] = totals[threadIdx.x];
+  const int s = blockIdx.x * kChunkSlots + threadIdx.x;
+  const bool valid = s < S;
+  const int e = valid ? topk_idx[s] : 0;
+  const int r = chunk_rank(e, valid, E, wave_base, totals);
+  if (valid) local_rank[s] = r;
+  if ((int)threadIdx.x < E) blk_counts[(size_t)blockIdx.x * E + threadIdx.x] = totals[threadIdx.x];
 }
 
 // One block: per expert, exclusive scan of the chunk counts (in place), the

@@ -11,11 +11,12 @@
 // tile.  The dense MLP of the layer runs through the same kernels as a single
 // group whose rows are the tokens themselves.
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 with fp32 accumulation; A rows are
-// gathered from the token matrix while they are staged into LDS; weight tiles
-// are double-buffered in LDS.  gate_up's epilogue applies GELU(gate) * up and
-// rounds h to bf16; down's epilogue multiplies each row by its routing weight
-// and writes it to the slot-major output.
+// bf16 path at prefill sizes (decode sizes use the weight-streaming kernels):
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation on 128 x 128 block tiles;
+// A rows are gathered from the token matrix while they are staged into LDS;
+// A and weight tiles are double-buffered in LDS.  gate_up's epilogue applies
+// GELU(gate) * up and rounds h to bf16; down's epilogue multiplies each row by
+// its routing weight and writes it to the slot-major output.
 // fp32 path (debug): the same tiling idea on the vector ALUs in fp32.
 #include "common.h"
 #include "launch.h"
@@ -55,196 +56,200 @@ __device__ __forceinline__ bf16x8 lds_frag(const bf16* base, int row, int k) {
   return *reinterpret_cast<const bf16x8*>(base + row * kPitch + k);
 }
 
-// gate_up: tile 64 rows x (64 gate + 64 up) columns, 4 waves in 2 x 2, each
-// wave 32 rows x (32 gate + 32 up).
-__global__ __launch_bounds__(256) void gate_up_bf16_kernel(
-    int H, int N, int E, int K, int rows, int ident, const bf16* __restrict__ x,
+// Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8);
+// give each XCD a contiguous range of work items so that neighbouring items
+// (row tiles of the same expert on the same column tile, which read the same
+// weight slab) run on one XCD at about the same time and share its L2.
+__device__ __forceinline__ int xcd_item(int b, int nb) {
+  const int q = nb / 8, r = nb % 8, x = b % 8;
+  return x * q + min(x, r) + b / 8;
+}
+
+constexpr int TBM = 128, TBK = 64, TP = TBK + 8;  // LDS pitch in bf16 (144 B)
+
+__device__ __forceinline__ void ld64(uint4 (&r)[4], const bf16* p, bool valid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = valid ? *reinterpret_cast<const uint4*>(p + 8 * i) : make_uint4(0, 0, 0, 0);
+}
+__device__ __forceinline__ void st64(bf16* p, const uint4 (&r)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(p + 8 * i) = r[i];
+}
+
+// gate_up, prefill sizes: block tile 128 rows x (64 gate + 64 up) columns,
+// BK = 64, double-buffered LDS; 4 waves in 2 x 2, each 64 rows x (32 gate +
+// 32 up).  Work item = (column tile, row tile), row tiles fastest.
+__global__ __launch_bounds__(256, 2) void gate_up_tiled_kernel(
+    int H, int N, int E, int K, int rows, int ident, int RT, const bf16* __restrict__ x,
     const bf16* __restrict__ wg, const bf16* __restrict__ wu, long long w_stride,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     bf16* __restrict__ h) {
-  constexpr int BM = 64, BN = 64;
-  __shared__ bf16 As[2][BM * kPitch];
-  __shared__ bf16 Gs[2][BN * kPitch];
-  __shared__ bf16 Us[2][BN * kPitch];
-
+  __shared__ bf16 As[2][TBM * TP];
+  __shared__ bf16 Bs[2][TBM * TP];  // rows [0,64) gate, [64,128) up
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int nt = item / RT, rti = item % RT;
   RowTile rt;
-  if (!get_row_tile(ident, rows, offsets, E, BM, rt)) return;
-  const int n0 = blockIdx.y * BN;
+  if (ident) {
+    rt.e = 0;
+    rt.row0 = rti * TBM;
+    rt.row1 = min(rt.row0 + TBM, rows);
+    if (rt.row0 >= rows) return;
+  } else if (!find_row_tile(offsets, E, TBM, rti, rt.e, rt.row0, rt.row1)) {
+    return;
+  }
+  const int n0 = nt * 64;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
 
-  // staging assignment: row tid/4, 16 elements at (tid%4)*16
-  const int lr = tid / 4, lk = (tid % 4) * 16;
-  const int arow = rt.row0 + lr;
-  const bool avalid = arow < rt.row1;
-  const bf16* ap = x;
-  if (avalid) {
-    const int tok = ident ? arow : sorted_slots[arow] / K;
-    ap = x + (size_t)tok * H + lk;
-  }
-  const int wrow = n0 + lr;
-  const bool wvalid = wrow < N;
-  const bf16* gp = wg + (size_t)rt.e * w_stride + (size_t)(wvalid ? wrow : 0) * H + lk;
-  const bf16* up = wu + (size_t)rt.e * w_stride + (size_t)(wvalid ? wrow : 0) * H + lk;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // staging: thread -> row tid / 2, 32 k at (tid % 2) * 32, for A and for B
+  const int sr = tid / 2, sk = (tid % 2) * 32;
+  const int arow = rt.row0 + sr;
+  const bool av = arow < rt.row1;
+  const bf16* ap = x + (size_t)(av ? (ident ? arow : sorted_slots[arow] / K) : 0) * H + sk;
+  const int bn = n0 + (sr & 63);
+  const bool bv = bn < N;
+  const bf16* bp = (sr < 64 ? wg : wu) + (size_t)rt.e * w_stride + (size_t)(bv ? bn : 0) * H + sk;
 
-  uint4 ra[2], rg[2], ru[2];
-  auto gload = [&](int k0) {
+  f32x4 accg[4][2], accu[4][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ra[j] = avalid ? ld16(ap + k0 + j * 8) : zero;
-      rg[j] = wvalid ? ld16(gp + k0 + j * 8) : zero;
-      ru[j] = wvalid ? ld16(up + k0 + j * 8) : zero;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      st16(&As[buf][lr * kPitch + lk + j * 8], ra[j]);
-      st16(&Gs[buf][lr * kPitch + lk + j * 8], rg[j]);
-      st16(&Us[buf][lr * kPitch + lk + j * 8], ru[j]);
-    }
-  };
-
-  f32x4 accg[2][2], accu[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       accg[i][j] = f32x4{0, 0, 0, 0};
       accu[i][j] = f32x4{0, 0, 0, 0};
     }
-
-  const int nk = H / kBK;
-  gload(0);
-  lstore(0);
+  uint4 ra[4], rb[4];
+  const int nk = H / TBK;
+  ld64(ra, ap, av);
+  ld64(rb, bp, bv);
+  st64(&As[0][sr * TP + sk], ra);
+  st64(&Bs[0][sr * TP + sk], rb);
   __syncthreads();
   const int fr = lane % 16, fk = (lane / 16) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    if (kt + 1 < nk) {
+      ld64(ra, ap + (kt + 1) * TBK, av);
+      ld64(rb, bp + (kt + 1) * TBK, bv);
+    }
+    const bf16* A = As[buf];
+    const bf16* B = Bs[buf];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 a[2], g[2], u[2];
+    for (int kk = 0; kk < TBK; kk += 32) {
+      bf16x8 a[4], g[2], u[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = lds_frag(As[buf], wm * 32 + i * 16 + fr, kk + fk);
+      for (int i = 0; i < 4; ++i) a[i] = lds_frag(A, wm * 64 + i * 16 + fr, kk + fk);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        g[j] = lds_frag(Gs[buf], wn * 32 + j * 16 + fr, kk + fk);
-        u[j] = lds_frag(Us[buf], wn * 32 + j * 16 + fr, kk + fk);
+        g[j] = lds_frag(B, wn * 32 + j * 16 + fr, kk + fk);
+        u[j] = lds_frag(B, 64 + wn * 32 + j * 16 + fr, kk + fk);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           accg[i][j] = mfma16(a[i], g[j], accg[i][j]);
           accu[i][j] = mfma16(a[i], u[j], accu[i][j]);
         }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (kt + 1 < nk) {
+      st64(&As[buf ^ 1][sr * TP + sk], ra);
+      st64(&Bs[buf ^ 1][sr * TP + sk], rb);
+    }
     __syncthreads();
   }
-
-  // epilogue: D[(lane/16)*4 + r][lane%16] of each 16x16 sub-tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = rt.row0 + wm * 32 + i * 16 + (lane / 16) * 4 + r;
+        const int row = rt.row0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
         const int col = n0 + wn * 32 + j * 16 + (lane % 16);
         if (row < rt.row1 && col < N)
           h[(size_t)row * N + col] = (bf16)(gelu_tanh(accg[i][j][r]) * accu[i][j][r]);
       }
 }
 
-// down: tile 64 rows x 128 columns, 4 waves in 2 x 2, each wave 32 x 64.
+// down, prefill sizes: block tile 128 rows x 128 columns, BK = 64; 4 waves in
+// 2 x 2, each 64 x 64.  The contraction length N is a multiple of 32; a
+// 32-wide half past the end is staged as zeros.
 template <typename YT>
-__global__ __launch_bounds__(256) void down_bf16_kernel(
-    int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
+__global__ __launch_bounds__(256, 2) void down_tiled_kernel(
+    int H, int N, int E, int rows, int ident, int RT, const bf16* __restrict__ hbuf,
     const bf16* __restrict__ wd, long long w_stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
     YT* __restrict__ y) {
-  constexpr int BM = 64, BN = 128;
-  __shared__ bf16 As[2][BM * kPitch];
-  __shared__ bf16 Bs[2][BN * kPitch];
-
+  __shared__ bf16 As[2][TBM * TP];
+  __shared__ bf16 Bs[2][TBM * TP];
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int nt = item / RT, rti = item % RT;
   RowTile rt;
-  if (!get_row_tile(ident, rows, offsets, E, BM, rt)) return;
-  const int n0 = blockIdx.y * BN;
+  if (ident) {
+    rt.e = 0;
+    rt.row0 = rti * TBM;
+    rt.row1 = min(rt.row0 + TBM, rows);
+    if (rt.row0 >= rows) return;
+  } else if (!find_row_tile(offsets, E, TBM, rti, rt.e, rt.row0, rt.row1)) {
+    return;
+  }
+  const int n0 = nt * 128;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
+  const int sr = tid / 2, sk = (tid % 2) * 32;
+  const int arow = rt.row0 + sr;
+  const bool av = arow < rt.row1;
+  const bf16* ap = hbuf + (size_t)(av ? arow : 0) * N + sk;
+  const int bn = n0 + sr;
+  const bool bv = bn < H;
+  const bf16* bp = wd + (size_t)rt.e * w_stride + (size_t)(bv ? bn : 0) * N + sk;
 
-  const int lr = tid / 4, lk = (tid % 4) * 16;
-  const int arow = rt.row0 + lr;
-  const bool avalid = arow < rt.row1;
-  const bf16* ap = hbuf + (size_t)(avalid ? arow : 0) * N + lk;
-  // weight rows: this thread stages rows lr and lr + 64
-  const bf16* bp[2];
-  bool bvalid[2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + lr + j * 64;
-    bvalid[j] = n < H;
-    bp[j] = wd + (size_t)rt.e * w_stride + (size_t)(bvalid[j] ? n : 0) * N + lk;
-  }
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-
-  uint4 ra[2], rb[2][2];
-  auto gload = [&](int k0) {
-    const bool kv = k0 + lk < N;  // N % 32 == 0: a 16-wide segment is all in or all out
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ra[j] = (avalid && kv) ? ld16(ap + k0 + j * 8) : zero;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) rb[q][j] = (bvalid[q] && kv) ? ld16(bp[q] + k0 + j * 8) : zero;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      st16(&As[buf][lr * kPitch + lk + j * 8], ra[j]);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) st16(&Bs[buf][(lr + q * 64) * kPitch + lk + j * 8], rb[q][j]);
-    }
-  };
-
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-
-  const int nk = (N + kBK - 1) / kBK;
-  gload(0);
-  lstore(0);
+  uint4 ra[4], rb[4];
+  const int nk = (N + TBK - 1) / TBK;
+  ld64(ra, ap, av && sk < N);
+  ld64(rb, bp, bv && sk < N);
+  st64(&As[0][sr * TP + sk], ra);
+  st64(&Bs[0][sr * TP + sk], rb);
   __syncthreads();
   const int fr = lane % 16, fk = (lane / 16) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    if (kt + 1 < nk) {
+      const bool kv = (kt + 1) * TBK + sk < N;
+      ld64(ra, ap + (kt + 1) * TBK, av && kv);
+      ld64(rb, bp + (kt + 1) * TBK, bv && kv);
+    }
+    const bf16* A = As[buf];
+    const bf16* B = Bs[buf];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 a[2], b[4];
+    for (int kk = 0; kk < TBK; kk += 32) {
+      bf16x8 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = lds_frag(As[buf], wm * 32 + i * 16 + fr, kk + fk);
+      for (int i = 0; i < 4; ++i) a[i] = lds_frag(A, wm * 64 + i * 16 + fr, kk + fk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs[buf], wn * 64 + j * 16 + fr, kk + fk);
+      for (int j = 0; j < 4; ++j) b[j] = lds_frag(B, wn * 64 + j * 16 + fr, kk + fk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (kt + 1 < nk) {
+      st64(&As[buf ^ 1][sr * TP + sk], ra);
+      st64(&Bs[buf ^ 1][sr * TP + sk], rb);
+    }
     __syncthreads();
   }
-
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = rt.row0 + wm * 32 + i * 16 + (lane / 16) * 4 + r;
+      const int row = rt.row0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
       if (row >= rt.row1) continue;
       const int slot = ident ? row : sorted_slots[row];
       const float sc = ident ? 1.0f : topk_w[slot];
@@ -371,9 +376,10 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_gate_up_stream(a, s);
   if (a.bf16) {
-    dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, 64), (a.N + 63) / 64);
-    hipLaunchKernelGGL(gate_up_bf16_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.K, a.rows,
-                       (int)a.ident, static_cast<const bf16*>(a.x),
+    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, TBM);
+    const int NT = (a.N + 63) / 64;
+    hipLaunchKernelGGL(gate_up_tiled_kernel, dim3(RT * NT), dim3(256), 0, s, a.H, a.N, a.E, a.K,
+                       a.rows, (int)a.ident, RT, static_cast<const bf16*>(a.x),
                        static_cast<const bf16*>(a.w_gate), static_cast<const bf16*>(a.w_up),
                        a.w_stride, a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
   } else {
@@ -390,17 +396,18 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_down_stream(a, s);
   if (a.bf16) {
-    dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, 64), (a.H + 127) / 128);
+    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, TBM);
+    dim3 grid(RT * ((a.H + 127) / 128));
     const bf16* hb = static_cast<const bf16*>(a.h);
     const bf16* wd = static_cast<const bf16*>(a.w_down);
     if (a.y_bf16)
-      hipLaunchKernelGGL(down_bf16_kernel<bf16>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
-                         (int)a.ident, hb, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w,
-                         static_cast<bf16*>(a.y));
+      hipLaunchKernelGGL(down_tiled_kernel<bf16>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
+                         (int)a.ident, RT, hb, wd, a.w_stride, a.offsets, a.sorted_slots,
+                         a.topk_w, static_cast<bf16*>(a.y));
     else
-      hipLaunchKernelGGL(down_bf16_kernel<float>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
-                         (int)a.ident, hb, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w,
-                         static_cast<float*>(a.y));
+      hipLaunchKernelGGL(down_tiled_kernel<float>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
+                         (int)a.ident, RT, hb, wd, a.w_stride, a.offsets, a.sorted_slots,
+                         a.topk_w, static_cast<float*>(a.y));
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.H + 2 * kFT - 1) / (2 * kFT));
     hipLaunchKernelGGL(down_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,

@@ -22,8 +22,15 @@ struct RouterArgs {
   float* ws_r0;                  // [T]   inverse RMS of x (pre-norm), if pre_gain
   float* ws_r;                   // [T]   inverse RMS of the router input
   float* ws_logits;              // [T,E]
+  // Optional dispatch right after the top-K (all null = router only).
+  int32_t* counts;               // [E]
+  int32_t* offsets;              // [E+1]
+  int32_t* sorted_slots;         // [T*K]
+  int32_t* ws_blk_counts;        // dispatch scratch (multi-chunk path)
+  int32_t* ws_local_rank;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+bool router_fuses_dispatch(int T, int H, int E, int K);
 
 struct DispatchArgs {
   int T, E, K;

@@ -136,9 +136,12 @@ int check_ws(const moe_dims* d, int32_t T, const void* ws, size_t ws_bytes) {
 
 // ---- launch sequences (arguments already checked) -------------------------
 
+// Router, and when counts is not null the dispatch as well (fused into the
+// router's top-K kernel for small batches).
 int run_router(const moe_dims* d, int32_t T, const void* x, const float* router_w,
                const float* router_scale, const float* pes, const float* pre_gain,
-               int32_t* idx, float* w, void* ws, hipStream_t s) {
+               int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
+               void* ws, hipStream_t s) {
   const Layout L = layout(d, T);
   moe::RouterArgs a{};
   a.T = T; a.H = d->hidden; a.E = d->num_experts; a.K = d->top_k; a.eps = d->eps;
@@ -147,8 +150,11 @@ int run_router(const moe_dims* d, int32_t T, const void* x, const float* router_
   a.per_expert_scale = pes; a.topk_idx = idx; a.topk_w = w;
   a.ws_r0 = at<float>(ws, L.r0); a.ws_r = at<float>(ws, L.r);
   a.ws_logits = at<float>(ws, L.logits);
+  a.counts = counts; a.offsets = offsets; a.sorted_slots = sorted;
+  a.ws_blk_counts = at<int32_t>(ws, L.blk_counts);
+  a.ws_local_rank = at<int32_t>(ws, L.local_rank);
   hipError_t e = moe::launch_router(a, s);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router");
+  return e == hipSuccess ? MOE_OK : hip_fail(e, counts ? "moe_route" : "moe_router");
 }
 
 int run_dispatch(const moe_dims* d, int32_t T, const int32_t* idx, int32_t* counts,
@@ -236,7 +242,27 @@ int moe_router(const moe_dims* dims, int32_t T, const void* x, const float* rout
   REQUIRE_PTR(topk_idx); REQUIRE_PTR(topk_w);
   if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
   return run_router(dims, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain,
-                    topk_idx, topk_w, ws, static_cast<hipStream_t>(stream));
+                    topk_idx, topk_w, nullptr, nullptr, nullptr, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
+int moe_route(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+              const float* router_scale, const float* per_expert_scale,
+              const float* pre_norm_gain, int32_t* topk_idx, float* topk_w,
+              int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(router_w); REQUIRE_PTR(router_scale);
+  REQUIRE_PTR(per_expert_scale); OPTIONAL_PTR(pre_norm_gain);
+  REQUIRE_PTR(topk_idx); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_counts);
+  REQUIRE_PTR(expert_offsets); REQUIRE_PTR(sorted_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_router(dims, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain,
+                    topk_idx, topk_w, expert_counts, expert_offsets, sorted_slots, ws,
+                    static_cast<hipStream_t>(stream));
 }
 
 int moe_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
@@ -324,10 +350,9 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   void* y = at<void>(ws, L.y);
-  if ((rc = run_router(dims, T, x, router_w, router_scale, per_expert_scale, nullptr, idx, w, ws,
-                       s)))
+  if ((rc = run_router(dims, T, x, router_w, router_scale, per_expert_scale, nullptr, idx, w,
+                       counts, offsets, sorted, ws, s)))
     return rc;
-  if ((rc = run_dispatch(dims, T, idx, counts, offsets, sorted, ws, s))) return rc;
   if ((rc = run_expert_ffn(dims, T, x, w_gate_up, w_down, w, offsets, sorted, y, ws, s)))
     return rc;
   return run_combine(dims, T, y, nullptr, out, s);
@@ -374,9 +399,8 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
   if (e != hipSuccess) return hip_fail(e, "gemma4_ffn_block (prenorm)");
 
   if ((rc = run_router(dims, T, residual, wt->router_w, wt->router_scale, wt->per_expert_scale,
-                       wt->g_pre2, idx, w, ws, s)))
+                       wt->g_pre2, idx, w, counts, offsets, sorted, ws, s)))
     return rc;
-  if ((rc = run_dispatch(dims, T, idx, counts, offsets, sorted, ws, s))) return rc;
   if ((rc = run_expert_ffn(dims, T, xm, wt->w_gate_up, wt->w_down, w, offsets, sorted, y, ws, s)))
     return rc;
 

@@ -11,19 +11,29 @@
 // rounded ones (HIP's default for sqrtf and '/'), and contraction is off in
 // this file so that products written separately stay separate.
 //
-// Three kernels:
+// Small batches (T <= 64, H <= 4096) take two kernels:
+//   router_logits_small  a block takes up to 4 tokens and 4 * EW experts.  Each
+//                 wave first issues the loads of its EW experts' weights (lane
+//                 c holds chunk c in registers), then one wave per token
+//                 computes the norms (lane c runs chunk c's chain, lane 0 adds
+//                 the chunk results in order) and writes the normalised,
+//                 scaled input to LDS in a padded [chunk][65] layout; every
+//                 lane then runs its chunk's chains against LDS, and one lane
+//                 per (token, expert) adds the chunk results in order;
+//   route_small   one block: top-K of every token (one wave per token), and
+//                 when asked the whole dispatch of the T*K <= 1024 slots.
+// Large batches take three:
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
-//   router_logits the projection.  Small batches: a wave takes a few
-//                 (token, expert) pairs and its lane c owns chunk c of every
-//                 pair; the chunk results meet in LDS and one lane per pair
-//                 adds them in order.  Large batches: a block takes 64 tokens
-//                 x 32 experts, lane = token, so every lane runs whole chunks
-//                 while the expert weights are read as LDS broadcasts;
-//   router_topk   one wave per token: softmax, top-K selection with the
-//                 lowest-index tie break, renormalisation, per-expert scale.
-#include "common.h"
+//   router_logits_tiled  a block takes 64 tokens x 32 experts, lane = token,
+//                 so every lane runs whole chunks while the expert weights are
+//                 read as LDS broadcasts;
+//   router_topk   one wave per token.
+// Top-K (route_dev.h): experts in descending logit order, ties to the lower
+// index, found with wave-wide DPP maxima of order-preserving keys; weights
+// z_k / sum z with z = exp(l - max l), times per_expert_scale.
 #include "launch.h"
+#include "route_dev.h"
 
 #pragma clang fp contract(off)
 
@@ -127,77 +137,115 @@ __device__ __forceinline__ float router_vhat(float x, bool pre, float r0, float 
   return (v * r) * s;
 }
 
-// Small batches: TPW tokens x EPW experts per wave; lane c owns chunk c
-// (requires H / 64 <= 64).
-template <typename XT, int TPW, int EPW>
-__global__ __launch_bounds__(256) void router_logits_pairs_kernel(
-    int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
-    const float* __restrict__ r0v, const float* __restrict__ rv,
+// Small batches: block = TB (<= 4) tokens x 4 * EW experts; lane c owns
+// chunk c (H / 64 <= 64).  Dynamic LDS: vhat [TB][nc][65] + parts
+// [4][TB * EW][65] + norm partials [4][64].
+template <typename XT, int TB, int EW>
+__global__ __launch_bounds__(256) void router_logits_small_kernel(
+    int T, int H, int E, float eps, const XT* __restrict__ x, const float* __restrict__ pre_gain,
     const float* __restrict__ scale, const float* __restrict__ W, float* __restrict__ logits) {
-  constexpr int P = TPW * EPW;
-  __shared__ float parts[4][P][kWave + 1];
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int gw = blockIdx.x * 4 + wave;
-  const int n_eg = (E + EPW - 1) / EPW;
-  const int tg = gw / n_eg, eg = gw % n_eg;
-  const bool active = tg * TPW < T;
+  extern __shared__ float lds[];
+  constexpr int P = TB * EW;
   const int nc = H / kChunk;
+  float* vh = lds;                              // [TB][nc][65]
+  float* parts = vh + TB * nc * (kChunk + 1);   // [4][P][65]
+  float* normp = parts + 4 * P * (kChunk + 1);  // [4][64]
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t0 = blockIdx.x * TB;
+  const int e0 = blockIdx.y * 4 * EW + wave * EW;
   const bool pre = pre_gain != nullptr;
+  const bool lc = lane < nc;
 
-  float acc[TPW][EPW];
+  // 1. this wave's experts: chunk `lane` of each, straight into registers
+  float wr[EW][kChunk];
 #pragma unroll
-  for (int a = 0; a < TPW; ++a)
+  for (int b = 0; b < EW; ++b) {
+    const float* src = W + (size_t)min(e0 + b, E - 1) * H + lane * kChunk;
 #pragma unroll
-    for (int b = 0; b < EPW; ++b) acc[a][b] = 0.0f;
-
-  if (active && lane < nc) {
-    const XT* xr[TPW];
-    float rt[TPW], r0t[TPW];
-#pragma unroll
-    for (int a = 0; a < TPW; ++a) {
-      int t = min(tg * TPW + a, T - 1);
-      xr[a] = x + (size_t)t * H;
-      rt[a] = rv[t];
-      r0t[a] = pre ? r0v[t] : 0.0f;
-    }
-    const float* wr[EPW];
-#pragma unroll
-    for (int b = 0; b < EPW; ++b) wr[b] = W + (size_t)min(eg * EPW + b, E - 1) * H;
-    const int h0 = lane * kChunk;
     for (int i = 0; i < kChunk; i += 8) {
-      float s[8], g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      load8(scale + h0 + i, s);
-      if (pre) load8(pre_gain + h0 + i, g);
-      float vh[TPW][8];
+      if (lc) load8(src + i, &wr[b][i]);
+      else {
 #pragma unroll
-      for (int a = 0; a < TPW; ++a) {
-        float xv[8];
-        load8(xr[a] + h0 + i, xv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vh[a][j] = router_vhat(xv[j], pre, r0t[a], g[j], rt[a], s[j]);
-      }
-#pragma unroll
-      for (int b = 0; b < EPW; ++b) {
-        float wv[8];
-        load8(wr[b] + h0 + i, wv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int a = 0; a < TPW; ++a) acc[a][b] = __builtin_fmaf(vh[a][j], wv[j], acc[a][b]);
+        for (int j = 0; j < 8; ++j) wr[b][i + j] = 0.0f;
       }
     }
+  }
+
+  // 2. norms and the normalised input: wave w takes token t0 + w
+  const int tw = t0 + wave;
+  const bool tok = wave < TB && tw < T;
+  float xv[kChunk];
+  float part = 0.0f;
+  if (tok && lc) {
+    const XT* xr = x + (size_t)tw * H + lane * kChunk;
 #pragma unroll
-    for (int a = 0; a < TPW; ++a)
+    for (int i = 0; i < kChunk; i += 8) load8(xr + i, &xv[i]);
 #pragma unroll
-      for (int b = 0; b < EPW; ++b) parts[wave][a * EPW + b][lane] = acc[a][b];
+    for (int i = 0; i < kChunk; ++i) part = __builtin_fmaf(xv[i], xv[i], part);
+  }
+  normp[wave * kWave + lane] = part;
+  __syncthreads();
+  float r = 0.0f;
+  if (tok && lane == 0) r = inv_rms_from_parts(normp + wave * kWave, nc, H, eps);
+  r = __shfl(r, 0, kWave);
+  if (pre) {
+    float g[kChunk];
+    part = 0.0f;
+    if (tok && lc) {
+#pragma unroll
+      for (int i = 0; i < kChunk; i += 8) load8(pre_gain + lane * kChunk + i, &g[i]);
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        xv[i] = (xv[i] * r) * g[i];
+        part = __builtin_fmaf(xv[i], xv[i], part);
+      }
+    }
+    __syncthreads();
+    normp[wave * kWave + lane] = part;
+    __syncthreads();
+    if (tok && lane == 0) r = inv_rms_from_parts(normp + wave * kWave, nc, H, eps);
+    r = __shfl(r, 0, kWave);
+  }
+  if (wave < TB && lc) {
+    float s[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; i += 8) load8(scale + lane * kChunk + i, &s[i]);
+    float* dst = vh + (wave * nc + lane) * (kChunk + 1);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) dst[i] = tok ? (xv[i] * r) * s[i] : 0.0f;
   }
   __syncthreads();
-  if (active && lane < P) {
-    const int a = lane / EPW, b = lane % EPW;
-    const int t = tg * TPW + a, e = eg * EPW + b;
+
+  // 3. chunk chains: acc[t][b] over chunk `lane`, ascending index from +0
+  float acc[TB][EW];
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int b = 0; b < EW; ++b) acc[t][b] = 0.0f;
+  if (lc) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const float v = vh[(t * nc + lane) * (kChunk + 1) + i];
+#pragma unroll
+        for (int b = 0; b < EW; ++b) acc[t][b] = __builtin_fmaf(v, wr[b][i], acc[t][b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int b = 0; b < EW; ++b) parts[(wave * P + t * EW + b) * (kChunk + 1) + lane] = acc[t][b];
+  __syncthreads();
+
+  // 4. one lane per (token, expert) adds the chunk results in chunk order
+  if (lane < P) {
+    const int t = t0 + lane / EW, e = e0 + lane % EW;
     if (t < T && e < E) {
+      const float* pp = parts + (wave * P + lane) * (kChunk + 1);
       float total = 0.0f;
-      for (int c = 0; c < nc; ++c) total = total + parts[wave][lane][c];
+      for (int c = 0; c < nc; ++c) total = total + pp[c];
       logits[(size_t)t * E + e] = total;
     }
   }
@@ -273,87 +321,98 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(
   }
 }
 
-// One wave per token: softmax over E (<= 256) logits, top-K by logit with
-// ties to the lower index, weights z_k / sum_j z_j * per_expert_scale.
+// One wave per token.
 __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int K,
                                                           const float* __restrict__ logits,
                                                           const float* __restrict__ pes,
                                                           int32_t* __restrict__ idx,
                                                           float* __restrict__ w) {
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;  // no block barrier below
-  float l[4], z[4];
-  bool taken[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + kWave * j;
-    taken[j] = e >= E;
-    l[j] = taken[j] ? -INFINITY : logits[(size_t)t * E + e];
-  }
-  float m = wave_max(fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) z[j] = taken[j] ? 0.0f : expf(l[j] - m);
-
-  int my_idx = 0;
-  float my_z = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + kWave * j;
-      if (!taken[j] && (l[j] > bv || (l[j] == bv && e < bi))) { bv = l[j]; bi = e; }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, kWave);
-      int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    const int owner = bi & (kWave - 1), slot = bi / kWave;
-    float zw = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane == owner && j == slot) { taken[j] = true; zw = z[j]; }
-    zw = __shfl(zw, owner, kWave);
-    if (lane == k) { my_idx = bi; my_z = zw; }
-  }
-  float q = 0.0f;
-  for (int k = 0; k < K; ++k) q = q + __shfl(my_z, k, kWave);
-  if (lane < K) {
-    idx[(size_t)t * K + lane] = my_idx;
-    w[(size_t)t * K + lane] = (my_z / q) * pes[my_idx];
-  }
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;  // whole wave; no block barrier below
+  wave_topk(logits + (size_t)t * E, E, K, pes, idx + (size_t)t * K, w + (size_t)t * K, nullptr);
 }
+
+// One block for T*K <= 1024 and T*E <= 8192: the logits and per-expert
+// scales are first staged in LDS (one coalesced pass), then the top-K of every
+// token (wave w takes tokens w, w + 16, ...), then, if counts is not null,
+// the dispatch of all slots.  Dynamic LDS: [T*E + E] floats.
+__global__ __launch_bounds__(kChunkSlots) void route_small_kernel(
+    int T, int E, int K, const float* __restrict__ logits, const float* __restrict__ pes,
+    int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots) {
+  extern __shared__ float dyn[];
+  __shared__ int sidx[kChunkSlots];
+  __shared__ int wave_base[kChunkWaves][kMaxE];
+  __shared__ int totals[kMaxE];
+  __shared__ int offs[kMaxE + 1];
+  float* slog = dyn;
+  float* spes = dyn + T * E;
+  for (int i = threadIdx.x; i < T * E; i += kChunkSlots) slog[i] = logits[i];
+  for (int i = threadIdx.x; i < E; i += kChunkSlots) spes[i] = pes[i];
+  __syncthreads();
+  const int wave = threadIdx.x / kWave;
+  for (int t = wave; t < T; t += kChunkWaves)
+    wave_topk(slog + t * E, E, K, spes, idx + (size_t)t * K, w + (size_t)t * K, sidx + t * K);
+  if (counts == nullptr) return;  // uniform
+  __syncthreads();
+  const bool valid = (int)threadIdx.x < T * K;
+  const int e = valid ? sidx[threadIdx.x] : 0;
+  dispatch_lone_chunk(e, valid, E, counts, offsets, sorted_slots, wave_base, totals, offs);
+}
+
+template <typename XT, int TB, int EW>
+void launch_small(const RouterArgs& a, hipStream_t s) {
+  const int nc = a.H / kChunk;
+  const size_t lds = sizeof(float) * ((size_t)TB * nc * (kChunk + 1) +
+                                      4 * TB * EW * (kChunk + 1) + 4 * kWave);
+  dim3 grid((a.T + TB - 1) / TB, (a.E + 4 * EW - 1) / (4 * EW));
+  hipLaunchKernelGGL((router_logits_small_kernel<XT, TB, EW>), grid, dim3(256), lds, s, a.T, a.H,
+                     a.E, a.eps, static_cast<const XT*>(a.x), a.pre_gain, a.router_scale,
+                     a.router_w, a.ws_logits);
+}
+
+}  // namespace
+
+// Small-batch path (two kernels, dispatch inside the top-K kernel): up to 64
+// tokens, T*K <= 1024 slots, T*E <= 8192, H <= 3072 (LDS within 64 KB).
+bool router_fuses_dispatch(int T, int H, int E, int K) {
+  return H / kChunk <= 48 && T <= 64 && T * K <= kChunkSlots && T * E <= 8192;
+}
+
+namespace {
 
 template <typename XT>
 hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const XT* x = static_cast<const XT*>(a.x);
   const int nc = a.H / kChunk;
+  if (router_fuses_dispatch(a.T, a.H, a.E, a.K)) {
+    if (a.T == 1) launch_small<XT, 1, 1>(a, s);
+    else if (a.T <= 8) launch_small<XT, 2, 1>(a, s);
+    else launch_small<XT, 4, 2>(a, s);
+    const size_t lds = sizeof(float) * ((size_t)a.T * a.E + a.E);
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kChunkSlots), lds, s, a.T, a.E, a.K,
+                       a.ws_logits, a.per_expert_scale, a.topk_idx, a.topk_w, a.counts,
+                       a.offsets, a.sorted_slots);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
                      a.eps, x, a.pre_gain, a.ws_r0, a.ws_r);
-  if (nc <= kWave && a.T < 8) {
-    const int waves = a.T * ((a.E + 3) / 4);
-    hipLaunchKernelGGL((router_logits_pairs_kernel<XT, 1, 4>), dim3((waves + 3) / 4), dim3(256),
-                       0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
-                       a.router_w, a.ws_logits);
-  } else if (nc <= kWave && a.T <= 256) {
-    const int waves = ((a.T + 3) / 4) * ((a.E + 3) / 4);
-    hipLaunchKernelGGL((router_logits_pairs_kernel<XT, 4, 4>), dim3((waves + 3) / 4), dim3(256),
-                       0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
-                       a.router_w, a.ws_logits);
-  } else {
-    hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
-                       dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,
-                       a.router_scale, a.router_w, a.ws_logits);
-  }
+  hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
+                     dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,
+                     a.router_scale, a.router_w, a.ws_logits);
   hipLaunchKernelGGL(router_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.E, a.K,
                      a.ws_logits, a.per_expert_scale, a.topk_idx, a.topk_w);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.counts == nullptr) return e;
+  DispatchArgs d{};
+  d.T = a.T; d.E = a.E; d.K = a.K; d.topk_idx = a.topk_idx; d.counts = a.counts;
+  d.offsets = a.offsets; d.sorted_slots = a.sorted_slots; d.ws_blk_counts = a.ws_blk_counts;
+  d.ws_local_rank = a.ws_local_rank;
+  return launch_dispatch(d, s);
 }
 
 }  // namespace
+
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   return a.x_bf16 ? launch_router_t<bf16>(a, s) : launch_router_t<float>(a, s);

@@ -53,6 +53,7 @@ def _load():
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_router.argtypes = [D, I32] + [P] * 8 + [SZ, P]
+    L.moe_route.argtypes = [D, I32] + [P] * 11 + [SZ, P]
     L.moe_dispatch.argtypes = [D, I32] + [P] * 5 + [SZ, P]
     L.moe_expert_ffn.argtypes = [D, I32] + [P] * 8 + [SZ, P]
     L.moe_expert_gate_up.argtypes = [D, I32] + [P] * 6
@@ -61,7 +62,7 @@ def _load():
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
         [SZ, P]
-    for f in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+    for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -123,6 +124,14 @@ def moe_router(d, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain,
                            _ptr(per_expert_scale), _ptr(pre_norm_gain), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(ws), ws.numel() if ws is not None else 0,
                            _stream(stream)))
+
+
+def moe_route(d, T, x, router_w, router_scale, per_expert_scale, pre_norm_gain, topk_idx, topk_w,
+              counts, offsets, sorted_slots, ws, stream=None):
+    _check(_lib.moe_route(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(router_scale),
+                          _ptr(per_expert_scale), _ptr(pre_norm_gain), _ptr(topk_idx),
+                          _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_slots), _ptr(ws),
+                          ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_dispatch(d, T, topk_idx, counts, offsets, sorted_slots, ws, stream=None):

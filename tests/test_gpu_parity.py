@@ -64,7 +64,7 @@ def test_router_tiny_fp32():
     _check_router(synth.tiny_case())
 
 
-@pytest.mark.parametrize("T", [1, 3, 8, 32, 64, 200])
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 32, 63, 64, 200])
 def test_router_decode_sizes(T):
     _check_router(synth.moe_case(T, seed=T, I=32, router_scale_std=0.05))
 
@@ -84,6 +84,36 @@ def test_router_with_pre_norm(T):
 def test_router_fp32_large_hidden_and_k_equals_e():
     c = synth.tiny_case(seed=3, T=70, H=4608, E=16, K=16, I=32)
     _check_router(c)
+
+
+@pytest.mark.parametrize("T,skew,pre", [(1, False, False), (13, False, True), (64, False, False),
+                                        (65, False, False), (300, True, True)])
+def test_route_fused(T, skew, pre):
+    """moe_route (router + dispatch in one call; fused into one kernel for
+    small batches) against the oracle's router and dispatch."""
+    c = synth.moe_case(T, seed=20 + T, I=32, skew=skew, router_scale_std=0.05)
+    g = (1 + 0.05 * np.random.default_rng(1).standard_normal(c.H)).astype(np.float32) if pre \
+        else None
+    note(f"route T={T} skew={skew} pre={pre}")
+    d = _dims(c)
+    ws = lib.workspace(d, c.T)
+    idx = torch.empty(T, c.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, c.K, dtype=torch.float32, device="cuda")
+    counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(c.E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * c.K, dtype=torch.int32, device="cuda")
+    lib.moe_route(d, T, dev_tensor(c.x, True), dev_f32(c.router_w), dev_f32(c.router_scale),
+                  dev_f32(c.per_expert_scale), None if g is None else dev_f32(g), idx, w, counts,
+                  offsets, ss, ws)
+    torch.cuda.synchronize()
+    oi, ow = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps,
+                           pre_gain=g)
+    assert np.array_equal(host(idx), oi)
+    np.testing.assert_allclose(host(w), ow, rtol=1e-6, atol=0)
+    oc, oo, os_ = oracle.dispatch(oi, c.E)
+    assert np.array_equal(host(counts), oc)
+    assert np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(ss), os_)
 
 
 # ---------------------------------------------------------------------------
