@@ -45,53 +45,72 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // Row tiles of a grouped GEMM.  Expert e owns rows [offsets[e], offsets[e+1])
 // of the expert-sorted slot order; it is cut into ceil(count / bm) tiles of
-// bm rows.  Tile number `tile` (counting experts in ascending order) is mapped
-// to its expert and row range by one wave: each lane takes a run of
-// consecutive experts, the lanes' tile totals are scanned, and the owner is
-// found.  Returns false if `tile` is past the last tile.  Every lane of the
-// calling wave gets the same answer.  Requires E <= 4 * 64.
-__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E,
-                                              int bm, int tile, int& e_out, int& row0,
-                                              int& row1) {
+// bm rows.  Tiles are numbered expert by expert in ascending order.  One wave
+// scans the per-expert tile counts (each lane takes a run of consecutive
+// experts) and can then map a tile number to its expert and row range.  Every
+// lane of the calling wave gets the same answers.  Requires E <= 4 * 64.
+struct RowTileScan {
+  int cnt[4];     // this lane's experts' tile counts
+  int base;       // this lane's first expert
+  int excl, incl; // exclusive / inclusive prefix of the lanes' totals
+  int total;      // tiles over all experts
+};
+
+__device__ __forceinline__ void row_tile_scan(const int32_t* __restrict__ offsets, int E, int bm,
+                                              RowTileScan& s) {
   const int lane = lane_id();
   const int per = (E + kWave - 1) / kWave;  // experts per lane (<= 4)
-  int base = lane * per;
-  int cnt[4];
+  s.base = lane * per;
   int local = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int e = base + j;
+    const int e = s.base + j;
     int c = 0;
     if (j < per && e < E) c = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    cnt[j] = c;
+    s.cnt[j] = c;
     local += c;
   }
-  // inclusive scan of the lane totals
   int incl = local;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(incl, o, kWave);
+    const int t = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += t;
   }
-  int excl = incl - local;
-  int total = __shfl(incl, kWave - 1, kWave);
-  if (tile >= total) return false;
-  // the lane whose range holds `tile`
-  unsigned long long hit = __ballot(tile >= excl && tile < incl);
-  int owner = __ffsll((long long)hit) - 1;
+  s.incl = incl;
+  s.excl = incl - local;
+  s.total = __shfl(incl, kWave - 1, kWave);
+}
+
+// Tile `tile` (< s.total) -> expert and row range.
+__device__ __forceinline__ void row_tile_lookup(const RowTileScan& s,
+                                                const int32_t* __restrict__ offsets, int bm,
+                                                int tile, int& e_out, int& row0, int& row1) {
+  const int lane = lane_id();
+  const unsigned long long hit = __ballot(tile >= s.excl && tile < s.incl);
+  const int owner = __ffsll((long long)hit) - 1;
   int e_found = 0, t_in = 0;
   if (lane == owner) {
-    int rem = tile - excl;
+    int rem = tile - s.excl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (rem >= 0 && rem < cnt[j]) { e_found = base + j; t_in = rem; }
-      rem -= cnt[j];
+      if (rem >= 0 && rem < s.cnt[j]) { e_found = s.base + j; t_in = rem; }
+      rem -= s.cnt[j];
     }
   }
   e_out = __shfl(e_found, owner, kWave);
   t_in = __shfl(t_in, owner, kWave);
   row0 = offsets[e_out] + t_in * bm;
   row1 = min(row0 + bm, offsets[e_out + 1]);
+}
+
+// Returns false if `tile` is past the last tile.
+__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E,
+                                              int bm, int tile, int& e_out, int& row0,
+                                              int& row1) {
+  RowTileScan s;
+  row_tile_scan(offsets, E, bm, s);
+  if (tile >= s.total) return false;
+  row_tile_lookup(s, offsets, bm, tile, e_out, row0, row1);
   return true;
 }
 

@@ -18,17 +18,13 @@
 // GELU(gate) * up and rounds h to bf16; down's epilogue multiplies each row by
 // its routing weight and writes it to the slot-major output.
 // fp32 path (debug): the same tiling idea on the vector ALUs in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernels
-// ---------------------------------------------------------------------------
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 (144 B: conflict-free 16 B reads)
 
 struct RowTile {
   int e, row0, row1;
@@ -45,221 +41,263 @@ __device__ __forceinline__ bool get_row_tile(bool ident, int rows, const int32_t
   return find_row_tile(offsets, E, bm, blockIdx.x, rt.e, rt.row0, rt.row1);
 }
 
-__device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(bf16* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// ---------------------------------------------------------------------------
+// bf16 grouped GEMM, prefill sizes
+// ---------------------------------------------------------------------------
+// Block tile: 256 rows x 256 output columns (gate_up: 128 gate columns and the
+// matching 128 up columns), k-tile 32.  Each k-tile of A (gathered rows) and B
+// (weight rows) goes global -> LDS directly (global_load_lds, 16 B per lane)
+// into a ring of NSTAGE stages of 32 KB, NSTAGE - 1 tiles in flight while one
+// is consumed.  An LDS row is 64 B (32 k values); the 16-B chunk c of row r is
+// stored at position c ^ ((r >> 2) & 3), which keeps the fragment reads of
+// v_mfma_f32_32x32x16_bf16 free of bank conflicts.  WM x WN waves each own a
+// (256 / WM) x (256 / WN) sub-tile.  In a fixed issue order, a wave reads the
+// fragments of the next half k-tile and issues its share of the next
+// global -> LDS copies between its MFMAs, so that LDS and memory latency hide
+// behind the matrix pipe; one barrier per k-tile.
+constexpr int GM = 256, GN = 256, GK = 32;
+constexpr int kStageBytes = (GM + GN) * GK * 2;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ int gswz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// s_waitcnt vmcnt(N) with the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Work items are (row tile, column tile) pairs, column tiles fastest.  Block
+// b runs on XCD b % 8; each XCD takes a contiguous range of the real items so
+// that items sharing gathered rows or a weight slab run on one XCD at about
+// the same time and share its L2.  Blocks past an XCD's range get -1.  Needs
+// gridDim.x >= n_items.
+__device__ __forceinline__ int xcd_item(int b, int n_items) {
+  const int x = b % 8, l = b / 8;
+  const int q = n_items / 8, r = n_items % 8;
+  const int cnt = q + (x < r ? 1 : 0);
+  return l < cnt ? x * q + min(x, r) + l : -1;
 }
 
-__device__ __forceinline__ bf16x8 lds_frag(const bf16* base, int row, int k) {
-  return *reinterpret_cast<const bf16x8*>(base + row * kPitch + k);
-}
-
-// Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8);
-// give each XCD a contiguous range of work items so that neighbouring items
-// (row tiles of the same expert on the same column tile, which read the same
-// weight slab) run on one XCD at about the same time and share its L2.
-__device__ __forceinline__ int xcd_item(int b, int nb) {
-  const int q = nb / 8, r = nb % 8, x = b % 8;
-  return x * q + min(x, r) + b / 8;
-}
-
-constexpr int TBM = 128, TBK = 64, TP = TBK + 8;  // LDS pitch in bf16 (144 B)
-
-__device__ __forceinline__ void ld64(uint4 (&r)[4], const bf16* p, bool valid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = valid ? *reinterpret_cast<const uint4*>(p + 8 * i) : make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ void st64(bf16* p, const uint4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(p + 8 * i) = r[i];
-}
-
-// gate_up, prefill sizes: block tile 128 rows x (64 gate + 64 up) columns,
-// BK = 64, double-buffered LDS; 4 waves in 2 x 2, each 64 rows x (32 gate +
-// 32 up).  Work item = (column tile, row tile), row tiles fastest.
-__global__ __launch_bounds__(256, 2) void gate_up_tiled_kernel(
-    int H, int N, int E, int K, int rows, int ident, int RT, const bf16* __restrict__ x,
-    const bf16* __restrict__ wg, const bf16* __restrict__ wu, long long w_stride,
+// GU: h[row] = GELU(A[row] . W0[n]) * (A[row] . W1[n]) for the block's 128
+// columns n, A row = token of the slot (or the row itself when ident).
+// !GU: y[slot] = w[slot] * (h[row] . W0[n]) for the block's 256 columns n.
+template <bool GU, int WM, int WN, int NSTAGE, typename YT>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
+    int Kd, int Nout, int E, int K, int rows, int ident, int NT, const bf16* __restrict__ A,
+    const bf16* __restrict__ W0, const bf16* __restrict__ W1, long long w_stride,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
-    bf16* __restrict__ h) {
-  __shared__ bf16 As[2][TBM * TP];
-  __shared__ bf16 Bs[2][TBM * TP];  // rows [0,64) gate, [64,128) up
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int nt = item / RT, rti = item % RT;
-  RowTile rt;
-  if (ident) {
-    rt.e = 0;
-    rt.row0 = rti * TBM;
-    rt.row1 = min(rt.row0 + TBM, rows);
-    if (rt.row0 >= rows) return;
-  } else if (!find_row_tile(offsets, E, TBM, rti, rt.e, rt.row0, rt.row1)) {
-    return;
+    const float* __restrict__ topk_w, bf16* __restrict__ hout, YT* __restrict__ yout) {
+  constexpr int NW = WM * WN, ROWS = GM + GN, LPW = ROWS / 16 / NW;
+  constexpr int WR = GM / WM, WC = GN / WN, TM = WR / 32, TN = WC / 32;
+  constexpr int NF = TM + TN, NMF = TM * TN;
+  static_assert(LPW * NW * 16 == ROWS && NF <= NMF && LPW <= NMF, "tile shape");
+  static_assert(!GU || TN % 2 == 0, "gate_up waves need gate/up column pairs");
+  static_assert(NSTAGE >= 3 && NSTAGE * kStageBytes <= 160 * 1024, "LDS ring");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  int e = 0, row0, row1, nt;
+  {
+    RowTileScan sc;
+    int R;
+    if (ident) {
+      R = (rows + GM - 1) / GM;
+    } else {
+      row_tile_scan(offsets, E, GM, sc);
+      R = sc.total;
+    }
+    const int item = xcd_item(blockIdx.x, R * NT);
+    if (item < 0) return;  // uniform over the block
+    const int rt = item / NT;
+    nt = item % NT;
+    if (ident) {
+      row0 = rt * GM;
+      row1 = min(row0 + GM, rows);
+    } else {
+      row_tile_lookup(sc, offsets, GM, rt, e, row0, row1);
+    }
   }
-  const int n0 = nt * 64;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nbase = GU ? nt * (GN / 2) : nt * GN;
 
-  // staging: thread -> row tid / 2, 32 k at (tid % 2) * 32, for A and for B
-  const int sr = tid / 2, sk = (tid % 2) * 32;
-  const int arow = rt.row0 + sr;
-  const bool av = arow < rt.row1;
-  const bf16* ap = x + (size_t)(av ? (ident ? arow : sorted_slots[arow] / K) : 0) * H + sk;
-  const int bn = n0 + (sr & 63);
-  const bool bv = bn < N;
-  const bf16* bp = (sr < 64 ? wg : wu) + (size_t)rt.e * w_stride + (size_t)(bv ? bn : 0) * H + sk;
-
-  f32x4 accg[4][2], accu[4][2];
+  // Copy q of a stage fills LDS rows 16 q .. 16 q + 15; lane -> row 16 q +
+  // lane / 4, position lane % 4.  This lane's LPW copies per k-tile:
+  const bf16* src[LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      accg[i][j] = f32x4{0, 0, 0, 0};
-      accu[i][j] = f32x4{0, 0, 0, 0};
-    }
-  uint4 ra[4], rb[4];
-  const int nk = H / TBK;
-  ld64(ra, ap, av);
-  ld64(rb, bp, bv);
-  st64(&As[0][sr * TP + sk], ra);
-  st64(&Bs[0][sr * TP + sk], rb);
-  __syncthreads();
-  const int fr = lane % 16, fk = (lane / 16) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      ld64(ra, ap + (kt + 1) * TBK, av);
-      ld64(rb, bp + (kt + 1) * TBK, bv);
-    }
-    const bf16* A = As[buf];
-    const bf16* B = Bs[buf];
-#pragma unroll
-    for (int kk = 0; kk < TBK; kk += 32) {
-      bf16x8 a[4], g[2], u[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_frag(A, wm * 64 + i * 16 + fr, kk + fk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        g[j] = lds_frag(B, wn * 32 + j * 16 + fr, kk + fk);
-        u[j] = lds_frag(B, 64 + wn * 32 + j * 16 + fr, kk + fk);
+  for (int j = 0; j < LPW; ++j) {
+    const int q = wave * LPW + j;
+    const int r = 16 * q + lane / 4;
+    const int c = gswz(r, lane % 4);
+    const bf16* p;
+    if (r < GM) {
+      int gr = row0 + r;
+      if (gr >= row1) gr = row0;  // past the tile: re-read a valid row, output dropped
+      const int arow = GU && !ident ? sorted_slots[gr] / K : gr;
+      p = A + (size_t)arow * Kd;
+    } else {
+      const int br = r - GM;
+      int n;
+      const bf16* base;
+      if (GU) {
+        n = nbase + br % (GN / 2);
+        base = br < GN / 2 ? W0 : W1;
+      } else {
+        n = nbase + br;
+        base = W0;
       }
+      if (n >= Nout) n = 0;  // past the last column: valid row, output dropped
+      p = base + (size_t)e * w_stride + (size_t)n * Kd;
+    }
+    src[j] = p + c * 8;
+  }
+  const int nk = Kd / GK;
+  // One copy per (k-tile, j); past the last k-tile the last tile is copied
+  // again into the (free) ring slot, so that every k-tile issues the same
+  // number of copies and the vmcnt waits below are constants.
+  auto copy = [&](int kt, int j) {
+    const int ktc = kt < nk ? kt : nk - 1;
+    const int q = wave * LPW + j;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src[j] + ktc * GK,
+                                     (void*)(smem + (kt % NSTAGE) * kStageBytes + q * 1024), 16,
+                                     0, 0);
+#endif
+  };
+
+  // Fragment byte offsets within a stage, per k16 half s: A sub-tiles 0..TM-1,
+  // then B sub-tiles (gate_up: gate halves first, then up).
+  const int fr = lane % 32, fq = lane / 32;
+  int off[2][NF];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          accg[i][j] = mfma16(a[i], g[j], accg[i][j]);
-          accu[i][j] = mfma16(a[i], u[j], accu[i][j]);
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WR + i * 32 + fr;
+      off[s][i] = r * 64 + gswz(r, 2 * s + fq) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int r;
+      if (GU) {
+        constexpr int half = TN / 2;
+        r = GM + (j < half ? 0 : GN / 2) + wn * (WC / 2) + (j % half) * 32 + fr;
+      } else {
+        r = GM + wn * WC + j * 32 + fr;
+      }
+      off[s][TM + j] = r * 64 + gswz(r, 2 * s + fq) * 16;
+    }
+  }
+  // 32-row sub-tiles of this wave that hold rows of the tile (wave-uniform).
+  int nv;
+  {
+    const int left = row1 - row0 - wm * WR;
+    nv = left <= 0 ? 0 : min(TM, (left + 31) / 32);
+    nv = __builtin_amdgcn_readfirstlane(nv);
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  bf16x8 f0[NF], f1[NF];
+  auto rd = [&](const unsigned char* st, int s, int f, bf16x8 (&fr_)[NF]) {
+    fr_[f] = *reinterpret_cast<const bf16x8*>(st + off[s][f]);
+  };
+
+  auto mainloop = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    auto mf = [&](int m, bf16x8 (&c)[NF]) {
+      const int i = m / TN, j = m % TN;
+      if (FULL || i < nv)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c[i], c[TM + j], acc[i][j], 0, 0, 0);
+    };
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) copy(s, j);
+    wait_vmem<(NSTAGE - 2) * LPW>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < NF; ++f) rd(smem, 0, f, f0);
+    wait_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const unsigned char* st = smem + (kt % NSTAGE) * kStageBytes;
+      const unsigned char* sn = smem + ((kt + 1) % NSTAGE) * kStageBytes;
+      // first half: MFMAs on f0, reads of this tile's second-half fragments
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        if (m < NF) rd(st, 1, m, f1);
+        mf(m, f0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lds();
+      // tile kt+1 has landed for every wave; ring slot (kt-1) % NSTAGE is free
+      wait_vmem<(NSTAGE - 3) * LPW>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // second half: MFMAs on f1, reads of tile kt+1's first-half fragments,
+      // copies of tile kt+NSTAGE-1
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        if (m < NF) rd(sn, 0, m, f0);
+        mf(m, f1);
+        if (m >= NMF - LPW) copy(kt + NSTAGE - 1, m - (NMF - LPW));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lds();
+    }
+    wait_vmem<0>();
+  };
+  if (nv == TM)
+    mainloop(std::true_type{});
+  else
+    mainloop(std::false_type{});
+
+  if constexpr (GU) {
+    constexpr int half = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= nv) break;
+#pragma unroll
+      for (int j = 0; j < half; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = row0 + wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
+          const int col = nbase + wn * (WC / 2) + j * 32 + fr;
+          if (row < row1 && col < Nout)
+            hout[(size_t)row * Nout + col] = (bf16)(gelu_tanh(acc[i][j][q]) * acc[i][j + half][q]);
         }
     }
-    if (kt + 1 < nk) {
-      st64(&As[buf ^ 1][sr * TP + sk], ra);
-      st64(&Bs[buf ^ 1][sr * TP + sk], rb);
-    }
-    __syncthreads();
-  }
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i) {
+      if (i >= nv) break;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int q = 0; q < 16; ++q) {
+        const int row = row0 + wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
+        if (row >= row1) continue;
+        const int slot = ident ? row : sorted_slots[row];
+        const float sc = ident ? 1.0f : topk_w[slot];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rt.row0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
-        const int col = n0 + wn * 32 + j * 16 + (lane % 16);
-        if (row < rt.row1 && col < N)
-          h[(size_t)row * N + col] = (bf16)(gelu_tanh(accg[i][j][r]) * accu[i][j][r]);
-      }
-}
-
-// down, prefill sizes: block tile 128 rows x 128 columns, BK = 64; 4 waves in
-// 2 x 2, each 64 x 64.  The contraction length N is a multiple of 32; a
-// 32-wide half past the end is staged as zeros.
-template <typename YT>
-__global__ __launch_bounds__(256, 2) void down_tiled_kernel(
-    int H, int N, int E, int rows, int ident, int RT, const bf16* __restrict__ hbuf,
-    const bf16* __restrict__ wd, long long w_stride, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
-    YT* __restrict__ y) {
-  __shared__ bf16 As[2][TBM * TP];
-  __shared__ bf16 Bs[2][TBM * TP];
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int nt = item / RT, rti = item % RT;
-  RowTile rt;
-  if (ident) {
-    rt.e = 0;
-    rt.row0 = rti * TBM;
-    rt.row1 = min(rt.row0 + TBM, rows);
-    if (rt.row0 >= rows) return;
-  } else if (!find_row_tile(offsets, E, TBM, rti, rt.e, rt.row0, rt.row1)) {
-    return;
-  }
-  const int n0 = nt * 128;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  const int sr = tid / 2, sk = (tid % 2) * 32;
-  const int arow = rt.row0 + sr;
-  const bool av = arow < rt.row1;
-  const bf16* ap = hbuf + (size_t)(av ? arow : 0) * N + sk;
-  const int bn = n0 + sr;
-  const bool bv = bn < H;
-  const bf16* bp = wd + (size_t)rt.e * w_stride + (size_t)(bv ? bn : 0) * N + sk;
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-  uint4 ra[4], rb[4];
-  const int nk = (N + TBK - 1) / TBK;
-  ld64(ra, ap, av && sk < N);
-  ld64(rb, bp, bv && sk < N);
-  st64(&As[0][sr * TP + sk], ra);
-  st64(&Bs[0][sr * TP + sk], rb);
-  __syncthreads();
-  const int fr = lane % 16, fk = (lane / 16) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      const bool kv = (kt + 1) * TBK + sk < N;
-      ld64(ra, ap + (kt + 1) * TBK, av && kv);
-      ld64(rb, bp + (kt + 1) * TBK, bv && kv);
-    }
-    const bf16* A = As[buf];
-    const bf16* B = Bs[buf];
-#pragma unroll
-    for (int kk = 0; kk < TBK; kk += 32) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_frag(A, wm * 64 + i * 16 + fr, kk + fk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_frag(B, wn * 64 + j * 16 + fr, kk + fk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      st64(&As[buf ^ 1][sr * TP + sk], ra);
-      st64(&Bs[buf ^ 1][sr * TP + sk], rb);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rt.row0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
-      if (row >= rt.row1) continue;
-      const int slot = ident ? row : sorted_slots[row];
-      const float sc = ident ? 1.0f : topk_w[slot];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane % 16);
-        if (col < H) y[(size_t)slot * H + col] = from_f32<YT>(sc * acc[i][j][r]);
+        for (int j = 0; j < TN; ++j) {
+          const int col = nbase + wn * WC + j * 32 + fr;
+          if (col < Nout) yout[(size_t)slot * Nout + col] = from_f32<YT>(sc * acc[i][j][q]);
+        }
       }
     }
+  }
 }
+
+// gate_up: 8 waves (4 x 2), 5 stages; down: 16 waves (4 x 4), 4 stages.
+constexpr int kGuWM = 4, kGuWN = 2, kGuStages = 5;
+constexpr int kDnWM = 4, kDnWN = 4, kDnStages = 4;
 
 // ---------------------------------------------------------------------------
 // fp32 kernels (debug path)
@@ -376,12 +414,18 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_gate_up_stream(a, s);
   if (a.bf16) {
-    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, TBM);
-    const int NT = (a.N + 63) / 64;
-    hipLaunchKernelGGL(gate_up_tiled_kernel, dim3(RT * NT), dim3(256), 0, s, a.H, a.N, a.E, a.K,
-                       a.rows, (int)a.ident, RT, static_cast<const bf16*>(a.x),
+    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, GM);
+    const int NT = (a.N + GN / 2 - 1) / (GN / 2);
+    auto kf = gemm256_kernel<true, kGuWM, kGuWN, kGuStages, float>;
+    const int lds = kGuStages * kStageBytes;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kf, dim3(RT * NT), dim3(64 * kGuWM * kGuWN), lds, s, a.H, a.N, a.E, a.K,
+                       a.rows, (int)a.ident, NT, static_cast<const bf16*>(a.x),
                        static_cast<const bf16*>(a.w_gate), static_cast<const bf16*>(a.w_up),
-                       a.w_stride, a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
+                       a.w_stride, a.offsets, a.sorted_slots, nullptr, static_cast<bf16*>(a.h),
+                       nullptr);
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.N + kFT - 1) / kFT);
     hipLaunchKernelGGL(gate_up_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.K, a.rows,
@@ -396,18 +440,29 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_down_stream(a, s);
   if (a.bf16) {
-    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, TBM);
-    dim3 grid(RT * ((a.H + 127) / 128));
+    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, GM);
+    const int NT = (a.H + GN - 1) / GN;
+    const int lds = kDnStages * kStageBytes;
+    const dim3 grid(RT * NT), block(64 * kDnWM * kDnWN);
     const bf16* hb = static_cast<const bf16*>(a.h);
     const bf16* wd = static_cast<const bf16*>(a.w_down);
-    if (a.y_bf16)
-      hipLaunchKernelGGL(down_tiled_kernel<bf16>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
-                         (int)a.ident, RT, hb, wd, a.w_stride, a.offsets, a.sorted_slots,
-                         a.topk_w, static_cast<bf16*>(a.y));
-    else
-      hipLaunchKernelGGL(down_tiled_kernel<float>, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
-                         (int)a.ident, RT, hb, wd, a.w_stride, a.offsets, a.sorted_slots,
-                         a.topk_w, static_cast<float*>(a.y));
+    if (a.y_bf16) {
+      auto kf = gemm256_kernel<false, kDnWM, kDnWN, kDnStages, bf16>;
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL(kf, grid, block, lds, s, a.N, a.H, a.E, a.K, a.rows, (int)a.ident, NT, hb,
+                         wd, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr,
+                         static_cast<bf16*>(a.y));
+    } else {
+      auto kf = gemm256_kernel<false, kDnWM, kDnWN, kDnStages, float>;
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL(kf, grid, block, lds, s, a.N, a.H, a.E, a.K, a.rows, (int)a.ident, NT, hb,
+                         wd, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr,
+                         static_cast<float*>(a.y));
+    }
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.H + 2 * kFT - 1) / (2 * kFT));
     hipLaunchKernelGGL(down_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
