@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
   constexpr int NF = TM + TN, NMF = TM * TN;
   static_assert(LPW * NW * 16 == ROWS && NF <= NMF && LPW <= NMF, "tile shape");
   static_assert(!GU || TN % 2 == 0, "gate_up waves need gate/up column pairs");
-  static_assert(NSTAGE >= 3 && NSTAGE * kStageBytes <= 160 * 1024, "LDS ring");
+  static_assert(NSTAGE >= 3 && NSTAGE * kStageBytes + (GU ? 0 : GM * 8) <= 160 * 1024, "LDS");
   extern __shared__ __align__(16) unsigned char smem[];
 
   int e = 0, row0, row1, nt;
@@ -122,6 +122,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int nbase = GU ? nt * (GN / 2) : nt * GN;
+  // down: output slot and routing weight of each of the tile's rows, fetched
+  // now (behind the main loop) into LDS past the ring, for the epilogue
+  int* row_slot = reinterpret_cast<int*>(smem + NSTAGE * kStageBytes);
+  float* row_w = reinterpret_cast<float*>(row_slot + GM);
+  if constexpr (!GU) {
+    if (threadIdx.x < GM) {
+      const int row = row0 + threadIdx.x;
+      int slot = row;
+      float w = 1.0f;
+      if (!ident && row < row1) {
+        slot = sorted_slots[row];
+        w = topk_w[slot];
+      }
+      row_slot[threadIdx.x] = slot;
+      row_w[threadIdx.x] = w;
+    }
+  }
 
   // Copy q of a stage fills LDS rows 16 q .. 16 q + 15; lane -> row 16 q +
   // lane / 4, position lane % 4.  This lane's LPW copies per k-tile:
@@ -281,10 +298,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
       if (i >= nv) break;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int row = row0 + wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
-        if (row >= row1) continue;
-        const int slot = ident ? row : sorted_slots[row];
-        const float sc = ident ? 1.0f : topk_w[slot];
+        const int r = wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
+        if (row0 + r >= row1) continue;
+        const int slot = row_slot[r];
+        const float sc = row_w[r];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col = nbase + wn * WC + j * 32 + fr;
@@ -442,7 +459,7 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.bf16) {
     const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, GM);
     const int NT = (a.H + GN - 1) / GN;
-    const int lds = kDnStages * kStageBytes;
+    const int lds = kDnStages * kStageBytes + GM * 8;  // ring + per-row slot and weight
     const dim3 grid(RT * NT), block(64 * kDnWM * kDnWN);
     const bf16* hb = static_cast<const bf16*>(a.h);
     const bf16* wd = static_cast<const bf16*>(a.w_down);

@@ -22,6 +22,7 @@ struct RouterArgs {
   float* ws_r0;                  // [T]   inverse RMS of x (pre-norm), if pre_gain
   float* ws_r;                   // [T]   inverse RMS of the router input
   float* ws_logits;              // [T,E]
+  float* ws_wt;                  // [H,E] transposed weights (large batches) or nullptr
   // Optional dispatch right after the top-K (all null = router only).
   int32_t* counts;               // [E]
   int32_t* offsets;              // [E+1]

@@ -25,9 +25,15 @@
 // Large batches take three:
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
-//   router_logits_tiled  a block takes 64 tokens x 32 experts, lane = token,
-//                 so every lane runs whole chunks while the expert weights are
-//                 read as LDS broadcasts;
+//   router_transpose  the weights [E, H] -> [H, E] (when E % 4 == 0);
+//   router_logits_wide  a block takes 16 tokens x 128 experts, a thread 2
+//                 tokens x 4 experts (8 chains).  Per chunk the normalised,
+//                 scaled input (computed once per block) and the transposed
+//                 weights are staged in LDS, double-buffered, and every thread
+//                 runs its 8 chains over the chunk with one 8-B and one 16-B
+//                 LDS read per 8 fmas;
+//   router_logits_tiled  (E % 4 != 0) a block takes 64 tokens x 32 experts,
+//                 lane = token, the expert weights read as LDS broadcasts;
 //   router_topk   one wave per token.
 // Top-K (route_dev.h): experts in descending logit order, ties to the lower
 // index, found with wave-wide DPP maxima of order-preserving keys; weights
@@ -321,6 +327,155 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(
   }
 }
 
+// W [E, H] -> WT [H, E]; 32 x 32 tiles through LDS.
+__global__ __launch_bounds__(256) void router_transpose_kernel(int E, int H,
+                                                               const float* __restrict__ W,
+                                                               float* __restrict__ WT) {
+  __shared__ float tile[32][33];
+  const int h0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+#pragma unroll
+  for (int i = ty; i < 32; i += 8) {
+    const int e = e0 + i, h = h0 + tx;
+    tile[i][tx] = (e < E && h < H) ? W[(size_t)e * H + h] : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = ty; i < 32; i += 8) {
+    const int h = h0 + i, e = e0 + tx;
+    if (h < H && e < E) WT[(size_t)h * E + e] = tile[tx][i];
+  }
+}
+
+__device__ __forceinline__ void load4(const float* p, float v[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float v[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void load2(const float* p, float v[2]) {
+  const float2 a = *reinterpret_cast<const float2*>(p);
+  v[0] = a.x; v[1] = a.y;
+}
+__device__ __forceinline__ void load2(const bf16* p, float v[2]) {
+  const unsigned u = *reinterpret_cast<const unsigned*>(p);
+  v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xffff0000u);
+}
+
+// Large batches, E % 4 == 0: block = 8 * TPT tokens x 128 experts; thread
+// (tp, eq) = TPT tokens x experts 4 eq .. 4 eq + 3.  LDS per buffer: the
+// transposed weights of the chunk [64][128] and the router input of the chunk
+// [64][8 * TPT] (row pitch chosen for conflict-free stores and aligned pair
+// loads), in one array with the input first.
+constexpr int kWideE = 128;
+template <typename XT, int TPT>
+__global__ __launch_bounds__(256) void router_logits_wide_kernel(
+    int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
+    const float* __restrict__ r0v, const float* __restrict__ rv,
+    const float* __restrict__ scale, const float* __restrict__ WT, float* __restrict__ logits) {
+  static_assert(TPT == 1 || TPT == 2, "tokens per thread");
+  constexpr int BT = 8 * TPT;                 // tokens per block
+  constexpr int NV = kChunk * BT / 256;       // input values staged per thread per chunk
+  constexpr int VP = TPT == 2 ? 20 : 12;      // input row pitch (floats)
+  __shared__ __align__(16) float lds[2 * kChunk * VP + 2 * kChunk * kWideE];
+  auto vl = reinterpret_cast<float(*)[kChunk][VP]>(lds);
+  auto wl = reinterpret_cast<float(*)[kChunk][kWideE]>(lds + 2 * kChunk * VP);
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * kWideE;
+  const int tp = tid / 32, eq = tid % 32;
+  const bool pre = pre_gain != nullptr;
+  // staging of the input: token st, k values sk .. sk + NV - 1 of the chunk
+  const int st = tid % BT, sk = (tid / BT) * NV;
+  const int tcl = min(t0 + st, T - 1);
+  const float r0 = pre ? r0v[tcl] : 0.0f, r = rv[tcl];
+  const XT* xr = x + (size_t)tcl * H + sk;
+  const int nc = H / kChunk;
+
+  float4 wreg[8];
+  float xv[NV], gv[NV], sv[NV];
+  auto gload = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = j * 256 + tid, k = f / 32, e = e0 + 4 * (f % 32);
+      wreg[j] = e < E ? *reinterpret_cast<const float4*>(WT + (size_t)(c * kChunk + k) * E + e)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    if constexpr (NV == 4) load4(xr + c * kChunk, xv);
+    else load2(xr + c * kChunk, xv);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      sv[i] = scale[c * kChunk + sk + i];
+      gv[i] = pre ? pre_gain[c * kChunk + sk + i] : 0.0f;
+    }
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = j * 256 + tid;
+      *reinterpret_cast<float4*>(&wl[b][f / 32][4 * (f % 32)]) = wreg[j];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vl[b][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
+  };
+
+  float total[TPT][4];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) total[i][j] = 0.0f;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nc) gload(c + 1);
+    float part[TPT][4];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[i][j] = 0.0f;
+#pragma unroll 16
+    for (int k = 0; k < kChunk; ++k) {
+      const float4 w = *reinterpret_cast<const float4*>(&wl[b][k][4 * eq]);
+      float v[TPT];
+      if constexpr (TPT == 2) {
+        const float2 vv = *reinterpret_cast<const float2*>(&vl[b][k][2 * tp]);
+        v[0] = vv.x;
+        v[1] = vv.y;
+      } else {
+        v[0] = vl[b][k][tp];
+      }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        part[i][0] = __builtin_fmaf(v[i], w.x, part[i][0]);
+        part[i][1] = __builtin_fmaf(v[i], w.y, part[i][1]);
+        part[i][2] = __builtin_fmaf(v[i], w.z, part[i][2]);
+        part[i][3] = __builtin_fmaf(v[i], w.w, part[i][3]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + part[i][j];
+    if (c + 1 < nc) lstore(b ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = t0 + TPT * tp + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 4 * eq + j;
+      if (e < E) logits[(size_t)t * E + e] = total[i][j];
+    }
+  }
+}
+
 // One wave per token.
 __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int K,
                                                           const float* __restrict__ logits,
@@ -375,6 +530,13 @@ void launch_small(const RouterArgs& a, hipStream_t s) {
 
 // Small-batch path (two kernels, dispatch inside the top-K kernel): up to 64
 // tokens, T*K <= 1024 slots, T*E <= 8192, H <= 3072 (LDS within 64 KB).
+// Two tokens per thread halve the LDS reads per fma but also the block
+// count; they pay off once 16-token blocks alone give two blocks per CU.
+static int wide_tokens_per_thread(int T, int E) {
+  const long long blocks16 = (long long)((T + 15) / 16) * ((E + kWideE - 1) / kWideE);
+  return blocks16 >= 512 ? 2 : 1;
+}
+
 bool router_fuses_dispatch(int T, int H, int E, int K) {
   return H / kChunk <= 48 && T <= 64 && T * K <= kChunkSlots && T * E <= 8192;
 }
@@ -397,9 +559,23 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
                      a.eps, x, a.pre_gain, a.ws_r0, a.ws_r);
-  hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
-                     dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,
-                     a.router_scale, a.router_w, a.ws_logits);
+  if (a.E % 4 == 0 && a.ws_wt != nullptr) {
+    hipLaunchKernelGGL(router_transpose_kernel, dim3((a.H + 31) / 32, (a.E + 31) / 32), dim3(256),
+                       0, s, a.E, a.H, a.router_w, a.ws_wt);
+    const dim3 eg(1, (a.E + kWideE - 1) / kWideE);
+    if (wide_tokens_per_thread(a.T, a.E) == 2)
+      hipLaunchKernelGGL((router_logits_wide_kernel<XT, 2>), dim3((a.T + 15) / 16, eg.y), dim3(256),
+                         0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
+                         a.ws_wt, a.ws_logits);
+    else
+      hipLaunchKernelGGL((router_logits_wide_kernel<XT, 1>), dim3((a.T + 7) / 8, eg.y), dim3(256),
+                         0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
+                         a.ws_wt, a.ws_logits);
+  } else {
+    hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
+                       dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,
+                       a.router_scale, a.router_w, a.ws_logits);
+  }
   hipLaunchKernelGGL(router_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.E, a.K,
                      a.ws_logits, a.per_expert_scale, a.topk_idx, a.topk_w);
   hipError_t e = hipGetLastError();
