@@ -81,6 +81,15 @@ def test_router_with_pre_norm(T):
     _check_router(c, pre_gain=g)
 
 
+@pytest.mark.parametrize("T,H,E,K,bf16", [
+    (150, 128, 6, 2, False),    # E % 4 != 0: lane-per-token tiled kernel
+    (150, 192, 132, 4, True),   # wide kernel, 1 token per thread, two expert blocks, ragged
+    (4100, 64, 256, 8, False),  # wide kernel, 2 tokens per thread, ragged token tail
+])
+def test_router_large_batch_kernels(T, H, E, K, bf16):
+    _check_router(synth.tiny_case(seed=T + E, T=T, H=H, E=E, K=K, I=32, bf16=bf16))
+
+
 def test_router_fp32_large_hidden_and_k_equals_e():
     c = synth.tiny_case(seed=3, T=70, H=4608, E=16, K=16, I=32)
     _check_router(c)
