@@ -85,6 +85,7 @@ struct Layout {
   size_t idx, w, counts, offsets, sorted, y;  // experts-only path / layer
   size_t xd, xm, hd, dn;            // layer only
   size_t wt;                        // router weights transposed
+  size_t counter;                   // small-batch top-K completion counter
   size_t total;
 };
 
@@ -116,6 +117,7 @@ Layout layout(const moe_dims* d, long long T) {
   L.hd = take(act * T * d->dense_inter);
   L.dn = take(slot * T * d->hidden);
   L.wt = take(4 * (size_t)d->num_experts * d->hidden);
+  L.counter = take(4);
   L.total = o;
   return L;
 }
@@ -153,6 +155,7 @@ int run_router(const moe_dims* d, int32_t T, const void* x, const float* router_
   a.ws_r0 = at<float>(ws, L.r0); a.ws_r = at<float>(ws, L.r);
   a.ws_logits = at<float>(ws, L.logits);
   a.ws_wt = at<float>(ws, L.wt);
+  a.ws_counter = at<unsigned>(ws, L.counter);
   a.counts = counts; a.offsets = offsets; a.sorted_slots = sorted;
   a.ws_blk_counts = at<int32_t>(ws, L.blk_counts);
   a.ws_local_rank = at<int32_t>(ws, L.local_rank);

@@ -37,6 +37,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // w_k = z_k / sum_j z_j with z = exp(l - max l), times per_expert_scale.
 // (Equal, in exact arithmetic, to renormalising the full softmax over the K.)
 // Writes idx_out[0..K) and w_out[0..K); if sidx is not null also sidx[0..K).
+// Value of v in lane src (src the same in every lane): v_readlane, no LDS
+// round trip.
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, int K,
                                           const float* __restrict__ pes,
                                           int32_t* __restrict__ idx_out,
@@ -63,7 +69,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
     float mine = l[0];
 #pragma unroll
     for (int j = 1; j < 4; ++j) if (j == jj) mine = l[j];
-    lmax = __shfl(mine, src, kWave);
+    lmax = lane_value(mine, src);
   }
   int my_e = 0;
   float my_z = 0.0f;
@@ -81,11 +87,11 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int E, i
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j == wj && lane == wl) { lv = l[j]; key[j] = 0u; }
-    lv = __shfl(lv, wl, kWave);
+    lv = lane_value(lv, wl);
     if (lane == k) { my_e = win; my_z = expf(lv - lmax); }
   }
   float q = 0.0f;
-  for (int k = 0; k < K; ++k) q = q + __shfl(my_z, k, kWave);
+  for (int k = 0; k < K; ++k) q = q + lane_value(my_z, k);
   if (lane < K) {
     idx_out[lane] = my_e;
     w_out[lane] = (my_z / q) * pes[my_e];

@@ -20,8 +20,8 @@
 //                 scaled input to LDS in a padded [chunk][65] layout; every
 //                 lane then runs its chunk's chains against LDS, and one lane
 //                 per (token, expert) adds the chunk results in order;
-//   route_small   one block: top-K of every token (one wave per token), and
-//                 when asked the whole dispatch of the T*K <= 1024 slots.
+//   route_topk_dispatch  one wave per token over several blocks; when asked,
+//                 the last block to finish groups the T*K <= 1024 slots.
 // Large batches take three:
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
@@ -149,9 +149,13 @@ __device__ __forceinline__ float router_vhat(float x, bool pre, float r0, float 
 template <typename XT, int TB, int EW>
 __global__ __launch_bounds__(256) void router_logits_small_kernel(
     int T, int H, int E, float eps, const XT* __restrict__ x, const float* __restrict__ pre_gain,
-    const float* __restrict__ scale, const float* __restrict__ W, float* __restrict__ logits) {
+    const float* __restrict__ scale, const float* __restrict__ W, float* __restrict__ logits,
+    unsigned* __restrict__ done_counter) {
   extern __shared__ float lds[];
   constexpr int P = TB * EW;
+  // the completion counter of the top-K kernel that follows on the stream
+  if (done_counter != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    *done_counter = 0u;
   const int nc = H / kChunk;
   float* vh = lds;                              // [TB][nc][65]
   float* parts = vh + TB * nc * (kChunk + 1);   // [4][P][65]
@@ -487,31 +491,36 @@ __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int K,
   wave_topk(logits + (size_t)t * E, E, K, pes, idx + (size_t)t * K, w + (size_t)t * K, nullptr);
 }
 
-// One block for T*K <= 1024 and T*E <= 8192: the logits and per-expert
-// scales are first staged in LDS (one coalesced pass), then the top-K of every
-// token (wave w takes tokens w, w + 16, ...), then, if counts is not null,
-// the dispatch of all slots.  Dynamic LDS: [T*E + E] floats.
-__global__ __launch_bounds__(kChunkSlots) void route_small_kernel(
+// Small batches: one wave per token, kTopkTok tokens per 1024-thread block,
+// so the top-K of the batch is spread over many CUs.  With counts != null
+// the last block to finish (a completion counter, zeroed by the logits kernel
+// of the same call) groups all T*K <= 1024 slots by expert.  The counter only
+// orders the blocks; every result is computed in one fixed order.
+constexpr int kTopkTok = 4;
+__global__ __launch_bounds__(kChunkSlots) void route_topk_dispatch_kernel(
     int T, int E, int K, const float* __restrict__ logits, const float* __restrict__ pes,
     int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots) {
-  extern __shared__ float dyn[];
-  __shared__ int sidx[kChunkSlots];
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
+    unsigned* __restrict__ done_counter) {
   __shared__ int wave_base[kChunkWaves][kMaxE];
   __shared__ int totals[kMaxE];
   __shared__ int offs[kMaxE + 1];
-  float* slog = dyn;
-  float* spes = dyn + T * E;
-  for (int i = threadIdx.x; i < T * E; i += kChunkSlots) slog[i] = logits[i];
-  for (int i = threadIdx.x; i < E; i += kChunkSlots) spes[i] = pes[i];
-  __syncthreads();
+  __shared__ int last;
   const int wave = threadIdx.x / kWave;
-  for (int t = wave; t < T; t += kChunkWaves)
-    wave_topk(slog + t * E, E, K, spes, idx + (size_t)t * K, w + (size_t)t * K, sidx + t * K);
+  const int t = blockIdx.x * kTopkTok + wave;
+  if (wave < kTopkTok && t < T)
+    wave_topk(logits + (size_t)t * E, E, K, pes, idx + (size_t)t * K, w + (size_t)t * K, nullptr);
   if (counts == nullptr) return;  // uniform
   __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();  // release: the block's idx stores (ordered by the barrier) go device-wide
+    last = atomicAdd(done_counter, 1u) == gridDim.x - 1;
+    if (last) __threadfence();  // acquire: the other blocks' idx stores
+  }
+  __syncthreads();
+  if (!last) return;  // uniform
   const bool valid = (int)threadIdx.x < T * K;
-  const int e = valid ? sidx[threadIdx.x] : 0;
+  const int e = valid ? __builtin_nontemporal_load(idx + threadIdx.x) : 0;
   dispatch_lone_chunk(e, valid, E, counts, offsets, sorted_slots, wave_base, totals, offs);
 }
 
@@ -523,13 +532,13 @@ void launch_small(const RouterArgs& a, hipStream_t s) {
   dim3 grid((a.T + TB - 1) / TB, (a.E + 4 * EW - 1) / (4 * EW));
   hipLaunchKernelGGL((router_logits_small_kernel<XT, TB, EW>), grid, dim3(256), lds, s, a.T, a.H,
                      a.E, a.eps, static_cast<const XT*>(a.x), a.pre_gain, a.router_scale,
-                     a.router_w, a.ws_logits);
+                     a.router_w, a.ws_logits, a.counts != nullptr ? a.ws_counter : nullptr);
 }
 
 }  // namespace
 
 // Small-batch path (two kernels, dispatch inside the top-K kernel): up to 64
-// tokens, T*K <= 1024 slots, T*E <= 8192, H <= 3072 (LDS within 64 KB).
+// tokens, T*K <= 1024 slots, H <= 3072 (LDS within 64 KB).
 // Two tokens per thread halve the LDS reads per fma but also the block
 // count; they pay off once 16-token blocks alone give two blocks per CU.
 static int wide_tokens_per_thread(int T, int E) {
@@ -538,7 +547,7 @@ static int wide_tokens_per_thread(int T, int E) {
 }
 
 bool router_fuses_dispatch(int T, int H, int E, int K) {
-  return H / kChunk <= 48 && T <= 64 && T * K <= kChunkSlots && T * E <= 8192;
+  return H / kChunk <= 48 && T <= 64 && T * K <= kChunkSlots;
 }
 
 namespace {
@@ -551,10 +560,10 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
     if (a.T == 1) launch_small<XT, 1, 1>(a, s);
     else if (a.T <= 8) launch_small<XT, 2, 1>(a, s);
     else launch_small<XT, 4, 2>(a, s);
-    const size_t lds = sizeof(float) * ((size_t)a.T * a.E + a.E);
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kChunkSlots), lds, s, a.T, a.E, a.K,
-                       a.ws_logits, a.per_expert_scale, a.topk_idx, a.topk_w, a.counts,
-                       a.offsets, a.sorted_slots);
+    hipLaunchKernelGGL(route_topk_dispatch_kernel, dim3((a.T + kTopkTok - 1) / kTopkTok),
+                       dim3(kChunkSlots), 0, s, a.T, a.E, a.K, a.ws_logits, a.per_expert_scale,
+                       a.topk_idx, a.topk_w, a.counts, a.offsets, a.sorted_slots,
+                       a.ws_counter);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
