@@ -16,6 +16,14 @@ would hold one copy of the weights a small batch touches, so the steps rotate
 over several weight copies and several input batches: every step streams its
 experts from HBM.
 
+Also reported in the same line: the tiny fp32 configuration (16 tokens,
+hidden 64, 8 experts, top-2); the whole FFN block (pre-norms, router on the
+normed input, experts, gated dense MLP of width 2112, five norms, residual,
+layer scalar) at 2048 tokens; and a stack of 30 independently seeded blocks
+(decode: 64 tokens, each step's input the previous step's output; prefill:
+8192 tokens once through the stack).  Block norm gains are 1 + N(0, 0.02),
+dense weights N(0, 0.02) bf16, layer scalar 0.06.
+
 Timing: W untimed warm-up steps, then K steps bracketed by device
 synchronisation; HIP events between the calls give each kernel's average
 duration on the stream it runs on.  The oracle (CPU) is timed on a bounded
@@ -44,6 +52,9 @@ ROUTER_BYTES = E * H * 4 + H * 4 + E * 4
 KERNEL_SRC = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc", "expert_stream.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_decode_b64_traffic.txt")
 SEGMENTS = ("route", "gate_up", "down", "combine")
+D = 2112                          # dense MLP width of the block
+DENSE_BYTES = 3 * D * H * 2       # dense gate, up, down, bf16
+LAYERS = 30
 
 
 def parse():
@@ -60,6 +71,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--block", type=int, default=2048, help="whole-block tokens (0 = skip)")
+    ap.add_argument("--stack", type=int, default=LAYERS, help="layers in the stack run (0 = skip)")
+    ap.add_argument("--stack-steps", type=int, default=128, help="timed decode steps of the stack")
+    ap.add_argument("--stack-prefill", type=int, default=8192, help="stack prefill tokens (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
 
@@ -172,18 +187,196 @@ def decode_measure(torch, wl, T, steps, warmup, xbatches, seed):
 
 
 def prefill_measure(torch, wl, T, steps, warmup, seed):
+    """The prefill batch with imbalanced expert load: a per-expert logit bias
+    b_e ~ N(0, 1), realised through the data as channel 0 of every token set
+    to 1 and router weight column 0 set to b."""
     runner = Runner(wl, T)
     xs = wl.batches(T, 2, seed + 1)
-    ms, seg, _ = time_steps(torch, runner, xs, wl.copies, steps, warmup)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_099 * seed + 3)
+    bias = torch.randn(E, generator=g, device="cuda")
+    for x in xs:
+        x[:, 0] = 1.0
+    copies = []
+    for rw, rs, pes, gu, dn in wl.copies:
+        rwb = rw.clone()
+        rwb[:, 0] = bias
+        copies.append((rwb, rs, pes, gu, dn))
+    ms, seg, _ = time_steps(torch, runner, xs, copies, steps, warmup)
+    runner.step(xs[0], copies[0])
+    torch.cuda.synchronize()
+    counts = runner.counts.cpu()
     flops = T * K * 6 * H * I
     gemm_ms = seg["gate_up"] + seg["down"]
     return {
         "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "kernel_ms": seg,
+        "expert_load": {"max": int(counts.max()), "empty": int((counts == 0).sum()),
+                        "top8_share": float(counts.sort(descending=True).values[:8].sum() / (T * K))},
         "grouped_gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12,
         "grouped_gemm_mfma_frac": flops / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "gate_up_tflops": flops * 2 / 3 / (seg["gate_up"] * 1e-3) / 1e12,
         "down_tflops": flops / 3 / (seg["down"] * 1e-3) / 1e12,
     }
+
+
+class BlockLayer:
+    """One block's weights (resident on the GPU) and its C-ABI weight struct."""
+
+    def __init__(self, torch, lib, seed, layer):
+        dev = torch.device("cuda")
+        g = torch.Generator(device=dev)
+        g.manual_seed(1_000_037 * seed + 104_729 * layer + 17)
+        rnd = lambda *shape: torch.randn(*shape, generator=g, device=dev)  # noqa: E731
+        self.gains = [rnd(H).mul_(0.02).add_(1.0) for _ in range(5)]
+        self.dense = [rnd(D, H).mul_(0.02).to(torch.bfloat16), rnd(D, H).mul_(0.02).to(torch.bfloat16),
+                      rnd(H, D).mul_(0.02).to(torch.bfloat16)]
+        self.rw = rnd(E, H).mul_(0.02)
+        self.rs = torch.ones(H, device=dev)
+        self.pes = torch.rand(E, generator=g, device=dev).add_(0.5)
+        self.gu = rnd(E, 2 * I, H).mul_(0.02).to(torch.bfloat16)
+        self.dn = rnd(E, H, I).mul_(0.02).to(torch.bfloat16)
+        self.w = lib.ffn_weights(*self.gains, *self.dense, self.rw, self.rs, self.pes, self.gu,
+                                 self.dn, 0.06)
+
+
+class BlockRunner:
+    """Buffers for the whole block at T tokens."""
+
+    def __init__(self, torch, lib, T):
+        self.lib, self.T = lib, T
+        self.dims = lib.dims(H, E, K, I, D, 1e-6, lib.MOE_BF16, lib.MOE_F32)
+        self.ws = lib.workspace(self.dims, T)
+        self.idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+
+    def step(self, x, layer, out):
+        self.lib.gemma4_ffn_block(self.dims, self.T, x, layer.w, out, None, self.idx, self.w,
+                                  self.ws)
+
+
+def block_bytes(U, T):
+    """Algorithmic HBM bytes of one block call: the touched experts, the dense
+    MLP, the router, the input and the output."""
+    return U * (GATE_UP_BYTES + DOWN_BYTES) + DENSE_BYTES + ROUTER_BYTES + 2 * T * H * 2
+
+
+def block_flops(T):
+    return T * K * 6 * H * I + T * 6 * H * D
+
+
+def block_measure(torch, lib, T, steps, warmup, seed, layers):
+    """The whole block at T tokens, rotating over the given layers' weights."""
+    br = BlockRunner(torch, lib, T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_039 * seed + T)
+    xs = [torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    for i in range(warmup):
+        br.step(xs[i % 2], layers[i % len(layers)], out)
+    torch.cuda.synchronize()
+    us = []
+    for i in range(len(layers)):
+        br.step(xs[0], layers[i], out)
+        torch.cuda.synchronize()
+        us.append(int(torch.unique(br.idx).numel()))
+    U = sum(us) / len(us)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        br.step(xs[i % 2], layers[i % len(layers)], out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    byts, fl = block_bytes(U, T), block_flops(T)
+    return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "distinct_experts": U, "hbm_bytes": byts, "flops": fl,
+            "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "binding": "hbm" if byts / HBM_PEAK_GBS * 1e3 > fl / BF16_PEAK_TFLOPS else "mfma"}
+
+
+def stack_measure(torch, lib, layers, T_dec, steps, T_pre, seed):
+    """A stack of independently seeded blocks: decode steps whose input is the
+    previous step's output, and one prefill pass."""
+    n = len(layers)
+    res = {"layers": n}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_081 * seed + 5)
+    br = BlockRunner(torch, lib, T_dec)
+    x = torch.randn(T_dec, H, generator=g, device="cuda").to(torch.bfloat16)
+    bufs = [x.clone(), torch.empty_like(x)]
+
+    def one_step(cur):
+        for li, layer in enumerate(layers):
+            br.step(bufs[(cur + li) % 2], layer, bufs[(cur + li + 1) % 2])
+        return (cur + n) % 2
+
+    cur = 0
+    us = []
+    for li, layer in enumerate(layers):  # warm-up step; distinct experts per layer
+        br.step(bufs[(cur + li) % 2], layer, bufs[(cur + li + 1) % 2])
+        us.append(int(torch.unique(br.idx).numel()))
+    cur = n % 2
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        cur = one_step(cur)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    finite = bool(torch.isfinite(bufs[cur].float()).all().item())
+    U = sum(us) / len(us)
+    byts = n * block_bytes(U, T_dec)
+    res["decode"] = {"tokens": T_dec, "steps": steps, "ms_per_step": ms,
+                     "tokens_per_s": T_dec / (ms * 1e-3), "output_finite": finite,
+                     "distinct_experts_per_layer": U, "hbm_bytes_per_step": byts,
+                     "per_layer_hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del br, bufs
+    if T_pre > 0:
+        br = BlockRunner(torch, lib, T_pre)
+        x = torch.randn(T_pre, H, generator=g, device="cuda").to(torch.bfloat16)
+        bufs = [x, torch.empty_like(x)]
+        for li, layer in enumerate(layers):  # warm-up pass
+            br.step(bufs[li % 2], layer, bufs[(li + 1) % 2])
+        torch.cuda.synchronize()
+        a.record()
+        for li, layer in enumerate(layers):
+            br.step(bufs[li % 2], layer, bufs[(li + 1) % 2])
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        fl = n * block_flops(T_pre)
+        res["prefill"] = {"tokens": T_pre, "ms": ms, "tokens_per_s": T_pre / (ms * 1e-3),
+                          "flops": fl, "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del br, bufs
+    return res
+
+
+def tiny_measure(torch, lib, steps, warmup):
+    """The tiny fp32 configuration (16 tokens, hidden 64, 8 experts, top-2,
+    intermediate 32) through moe_forward."""
+    from sparse_moe_transformer_router_amd import synth
+    c = synth.tiny_case(seed=0)
+    f = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    d = lib.dims(c.H, c.E, c.K, c.I, 0, c.eps, lib.MOE_F32, lib.MOE_F32)
+    ws = lib.workspace(d, c.T)
+    x, rw, rs, pes = f(c.x.f32), f(c.router_w), f(c.router_scale), f(c.per_expert_scale)
+    gu, dn = f(c.gate_up.f32), f(c.down.f32)
+    out = torch.empty(c.T, c.H, device="cuda")
+    idx = torch.empty(c.T, c.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(c.T, c.K, device="cuda")
+    call = lambda: lib.moe_forward(d, c.T, x, rw, rs, pes, gu, dn, out, idx, w, ws)  # noqa: E731
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"tokens": c.T, "ms_per_step": ms, "tokens_per_s": c.T / (ms * 1e-3),
+            "dtype": "f32", "timing": "host clock around the launches (launch-bound)"}
 
 
 def cpu_baseline(torch, wl, xs, T, seconds):
@@ -209,6 +402,43 @@ def cpu_baseline(torch, wl, xs, T, seconds):
     return {"value": n / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"router + sparse experts (fp64 loop) on the first {T}-token decode batch of "
                       f"weight copy 0, repeated {n // T}x over {el:.1f} s"}
+
+
+def cpu_oracle_configs(torch, layer, seconds):
+    """Oracle rates on the other configurations (bounded samples): the tiny fp32
+    experts-only case and the whole block on 16 tokens of the 2048-token input."""
+    import oracle
+    from sparse_moe_transformer_router_amd import synth
+
+    res = {"cores": oracle.num_threads(), "kind": "oracle"}
+    c = synth.tiny_case(seed=0)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K)
+        oracle.experts(c.x.f32, c.gate_up.f32, c.down.f32, idx, w)
+        n += c.T
+        el = time.perf_counter() - t0
+        if el >= seconds / 4:
+            break
+    res["tiny_f32"] = {"tokens_per_s": n / el, "sample": f"{n // c.T} calls of the 16-token case"}
+    if layer is not None:
+        f = lambda t: t.float().cpu().numpy()  # noqa: E731
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        x = f(torch.randn(16, H, generator=g, device="cuda").to(torch.bfloat16))
+        args = [f(t) for t in (*layer.gains, *layer.dense, layer.rw, layer.rs, layer.pes, layer.gu,
+                               layer.dn)]
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.block(x, *args, 0.06, K)
+            n += x.shape[0]
+            el = time.perf_counter() - t0
+            if el >= seconds * 3 / 4:
+                break
+        res["block"] = {"tokens_per_s": n / el,
+                        "sample": f"whole block on 16 tokens, {n // 16} calls over {el:.1f} s"}
+        del args
+    return res
 
 
 def traffic_from_profile():
@@ -257,9 +487,26 @@ def main():
         prefill = prefill_measure(torch, wl, args.prefill, max(5, args.steps // 5),
                                   max(2, args.warmup // 5), args.seed)
 
+    tiny = tiny_measure(torch, lib, args.steps, args.warmup)
+
+    block, layers = None, []
+    if args.block > 0 or args.stack > 0:
+        layers = [BlockLayer(torch, lib, args.seed, l) for l in range(max(2, args.stack))]
+        torch.cuda.synchronize()
+    if args.block > 0:
+        block = block_measure(torch, lib, args.block, max(5, args.steps // 5),
+                              max(2, args.warmup // 5), args.seed, layers[:2])
+    stack = None
+    if args.stack > 0:
+        stack = stack_measure(torch, lib, layers[:args.stack], args.batch, args.stack_steps,
+                              args.stack_prefill, args.seed)
+
     cpu = None
+    cpu_configs = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, wl, xs, args.batch, args.cpu_seconds)
+        cpu_configs = cpu_oracle_configs(torch, layers[0] if layers else None,
+                                         args.cpu_seconds / 2)
 
     achieved = head["gate_up_gbs"]
     line = {
@@ -287,6 +534,10 @@ def main():
         "cpu_baseline": cpu,
         "decode": {str(args.batch): head, **sweep},
         "prefill": prefill,
+        "tiny_f32": tiny,
+        "block": block,
+        "stack": stack,
+        "cpu_oracle_other_configs": cpu_configs,
     }
     print(json.dumps(line), flush=True)
 

@@ -280,16 +280,27 @@ void launch_dn_t(const DownArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool use_stream_kernels(int T, bool ident) { return T <= (ident ? 32 : 64); }
+bool use_stream_kernels(int T, bool ident) { return T <= 64; }
 
+// The dense branch (ident) at <= 64 tokens takes 32-row tiles (its weights
+// are streamed once per tile, the second time mostly from L2); its down
+// projection splits the contraction over 4 waves to keep enough loads in
+// flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
-  launch_gu<8, 1, 3>(a, s);
+  if (a.ident) launch_gu<8, 2, 2>(a, s);
+  else launch_gu<8, 1, 3>(a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s) {
-  if (a.y_bf16) launch_dn_t<bf16>(a, s);
-  else launch_dn_t<float>(a, s);
+  if (a.ident) {
+    if (a.y_bf16) launch_dn<2, 4, 2, 2, bf16>(a, s);
+    else launch_dn<2, 4, 2, 2, float>(a, s);
+  } else if (a.y_bf16) {
+    launch_dn_t<bf16>(a, s);
+  } else {
+    launch_dn_t<float>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -331,6 +331,19 @@ def test_block_small(bf16):
     assert rel_max_err(out, r["out"]) <= tol
 
 
+def test_block_26b_decode():
+    """The full-size layer at a decode batch (64 tokens: the dense branch and
+    the experts take the weight-streaming kernels); every row checked."""
+    b = synth.block_case(64, seed=4)
+    note("block 26B T=64")
+    out, ffn, idx, w = _run_block(b, True)
+    r = _oracle_block(b)
+    assert np.array_equal(idx, r["idx"])
+    np.testing.assert_allclose(w, r["w"], rtol=1e-6)
+    assert rel_max_err(ffn, r["o"]) <= BF16_TOL
+    assert rel_max_err(out, r["out"]) <= BF16_TOL
+
+
 def test_block_26b_sampled():
     """The full-size layer (2048 tokens); the oracle evaluates a sample of rows."""
     b = synth.block_case(2048, seed=0)
