@@ -44,19 +44,20 @@ __device__ __forceinline__ bool get_row_tile(bool ident, int rows, const int32_t
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM, prefill sizes
 // ---------------------------------------------------------------------------
-// Block tile: 256 rows x 256 output columns (gate_up: 128 gate columns and the
-// matching 128 up columns), k-tile 32.  Each k-tile of A (gathered rows) and B
+// Block tile: BM (256 or 128) rows x 256 output columns (gate_up: 128 gate
+// columns and the matching 128 up columns), k-tile 32.  Each k-tile of A (gathered rows) and B
 // (weight rows) goes global -> LDS directly (global_load_lds, 16 B per lane)
 // into a ring of NSTAGE stages of 32 KB, NSTAGE - 1 tiles in flight while one
 // is consumed.  An LDS row is 64 B (32 k values); the 16-B chunk c of row r is
 // stored at position c ^ ((r >> 2) & 3), which keeps the fragment reads of
 // v_mfma_f32_32x32x16_bf16 free of bank conflicts.  WM x WN waves each own a
-// (256 / WM) x (256 / WN) sub-tile.  In a fixed issue order, a wave reads the
+// (BM / WM) x (256 / WN) sub-tile.  In a fixed issue order, a wave reads the
 // fragments of the next half k-tile and issues its share of the next
 // global -> LDS copies between its MFMAs, so that LDS and memory latency hide
 // behind the matrix pipe; one barrier per k-tile.
-constexpr int GM = 256, GN = 256, GK = 32;
-constexpr int kStageBytes = (GM + GN) * GK * 2;
+constexpr int GN = 256, GK = 32;
+template <int BM>
+constexpr int stage_bytes() { return (BM + GN) * GK * 2; }
 
 __device__ __forceinline__ int gswz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
@@ -84,18 +85,19 @@ __device__ __forceinline__ int xcd_item(int b, int n_items) {
 // GU: h[row] = GELU(A[row] . W0[n]) * (A[row] . W1[n]) for the block's 128
 // columns n, A row = token of the slot (or the row itself when ident).
 // !GU: y[slot] = w[slot] * (h[row] . W0[n]) for the block's 256 columns n.
-template <bool GU, int WM, int WN, int NSTAGE, typename YT>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
+template <bool GU, int BM, int WM, int WN, int NSTAGE, typename YT>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
     int Kd, int Nout, int E, int K, int rows, int ident, int NT, const bf16* __restrict__ A,
     const bf16* __restrict__ W0, const bf16* __restrict__ W1, long long w_stride,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     const float* __restrict__ topk_w, bf16* __restrict__ hout, YT* __restrict__ yout) {
-  constexpr int NW = WM * WN, ROWS = GM + GN, LPW = ROWS / 16 / NW;
-  constexpr int WR = GM / WM, WC = GN / WN, TM = WR / 32, TN = WC / 32;
+  constexpr int SB = stage_bytes<BM>();
+  constexpr int NW = WM * WN, ROWS = BM + GN, LPW = ROWS / 16 / NW;
+  constexpr int WR = BM / WM, WC = GN / WN, TM = WR / 32, TN = WC / 32;
   constexpr int NF = TM + TN, NMF = TM * TN;
   static_assert(LPW * NW * 16 == ROWS && NF <= NMF && LPW <= NMF, "tile shape");
   static_assert(!GU || TN % 2 == 0, "gate_up waves need gate/up column pairs");
-  static_assert(NSTAGE >= 3 && NSTAGE * kStageBytes + (GU ? 0 : GM * 8) <= 160 * 1024, "LDS");
+  static_assert(NSTAGE >= 3 && NSTAGE * SB + (GU ? 0 : BM * 8) <= 160 * 1024, "LDS");
   extern __shared__ __align__(16) unsigned char smem[];
 
   int e = 0, row0, row1, nt;
@@ -103,9 +105,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
     RowTileScan sc;
     int R;
     if (ident) {
-      R = (rows + GM - 1) / GM;
+      R = (rows + BM - 1) / BM;
     } else {
-      row_tile_scan(offsets, E, GM, sc);
+      row_tile_scan(offsets, E, BM, sc);
       R = sc.total;
     }
     const int item = xcd_item(blockIdx.x, R * NT);
@@ -113,10 +115,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
     const int rt = item / NT;
     nt = item % NT;
     if (ident) {
-      row0 = rt * GM;
-      row1 = min(row0 + GM, rows);
+      row0 = rt * BM;
+      row1 = min(row0 + BM, rows);
     } else {
-      row_tile_lookup(sc, offsets, GM, rt, e, row0, row1);
+      row_tile_lookup(sc, offsets, BM, rt, e, row0, row1);
     }
   }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -124,10 +126,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
   const int nbase = GU ? nt * (GN / 2) : nt * GN;
   // down: output slot and routing weight of each of the tile's rows, fetched
   // now (behind the main loop) into LDS past the ring, for the epilogue
-  int* row_slot = reinterpret_cast<int*>(smem + NSTAGE * kStageBytes);
-  float* row_w = reinterpret_cast<float*>(row_slot + GM);
+  int* row_slot = reinterpret_cast<int*>(smem + NSTAGE * SB);
+  float* row_w = reinterpret_cast<float*>(row_slot + BM);
   if constexpr (!GU) {
-    if (threadIdx.x < GM) {
+    if (threadIdx.x < BM) {
       const int row = row0 + threadIdx.x;
       int slot = row;
       float w = 1.0f;
@@ -149,13 +151,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
     const int r = 16 * q + lane / 4;
     const int c = gswz(r, lane % 4);
     const bf16* p;
-    if (r < GM) {
+    if (r < BM) {
       int gr = row0 + r;
       if (gr >= row1) gr = row0;  // past the tile: re-read a valid row, output dropped
       const int arow = GU && !ident ? sorted_slots[gr] / K : gr;
       p = A + (size_t)arow * Kd;
     } else {
-      const int br = r - GM;
+      const int br = r - BM;
       int n;
       const bf16* base;
       if (GU) {
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
     const int q = wave * LPW + j;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(src[j] + ktc * GK,
-                                     (void*)(smem + (kt % NSTAGE) * kStageBytes + q * 1024), 16,
+                                     (void*)(smem + (kt % NSTAGE) * SB + q * 1024), 16,
                                      0, 0);
 #endif
   };
@@ -200,9 +202,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
       int r;
       if (GU) {
         constexpr int half = TN / 2;
-        r = GM + (j < half ? 0 : GN / 2) + wn * (WC / 2) + (j % half) * 32 + fr;
+        r = BM + (j < half ? 0 : GN / 2) + wn * (WC / 2) + (j % half) * 32 + fr;
       } else {
-        r = GM + wn * WC + j * 32 + fr;
+        r = BM + wn * WC + j * 32 + fr;
       }
       off[s][TM + j] = r * 64 + gswz(r, 2 * s + fq) * 16;
     }
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
     wait_lds();
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < nk; ++kt) {
-      const unsigned char* st = smem + (kt % NSTAGE) * kStageBytes;
-      const unsigned char* sn = smem + ((kt + 1) % NSTAGE) * kStageBytes;
+      const unsigned char* st = smem + (kt % NSTAGE) * SB;
+      const unsigned char* sn = smem + ((kt + 1) % NSTAGE) * SB;
       // first half: MFMAs on f0, reads of this tile's second-half fragments
 #pragma unroll
       for (int m = 0; m < NMF; ++m) {
@@ -312,9 +314,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm256_kernel(
   }
 }
 
-// gate_up: 8 waves (4 x 2), 5 stages; down: 16 waves (4 x 4), 4 stages.
-constexpr int kGuWM = 4, kGuWN = 2, kGuStages = 5;
-constexpr int kDnWM = 4, kDnWN = 4, kDnStages = 4;
+// Configurations (256-row tiles): gate_up 8 waves (4 x 2), 5 stages; down 16
+// waves (4 x 4), 4 stages.  128-row tiles measured slower on every shape
+// tried (groups of ~128 rows at 2048 tokens included): the per-barrier MFMA
+// count halves, and weights are read from HBM once per tile either way.
 
 // ---------------------------------------------------------------------------
 // fp32 kernels (debug path)
@@ -427,22 +430,50 @@ int row_tile_bound(bool ident, int rows, int T, int E, int bm) {
 
 }  // namespace
 
+namespace {
+
+template <bool GU, int BM, int WM, int WN, int NSTAGE, typename YT>
+hipError_t launch_grouped(int Kd, int Nout, int E, int K, int rows, bool ident, int RT, int NT,
+                          const bf16* A, const bf16* W0, const bf16* W1, long long w_stride,
+                          const int32_t* offsets, const int32_t* sorted_slots,
+                          const float* topk_w, bf16* hout, YT* yout, hipStream_t s) {
+  auto kf = grouped_gemm_kernel<GU, BM, WM, WN, NSTAGE, YT>;
+  const int lds = NSTAGE * stage_bytes<BM>() + (GU ? 0 : BM * 8);  // ring (+ row slots, weights)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kf, dim3(RT * NT), dim3(64 * WM * WN), lds, s, Kd, Nout, E, K, rows,
+                     (int)ident, NT, A, W0, W1, w_stride, offsets, sorted_slots, topk_w, hout,
+                     yout);
+  return hipSuccess;
+}
+
+template <typename YT>
+hipError_t launch_down_tiled(const DownArgs& a, hipStream_t s) {
+  const int NT = (a.H + GN - 1) / GN;
+  const bf16* hb = static_cast<const bf16*>(a.h);
+  const bf16* wd = static_cast<const bf16*>(a.w_down);
+  YT* y = static_cast<YT*>(a.y);
+  return launch_grouped<false, 256, 4, 4, 4, YT>(
+      a.N, a.H, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT, hb,
+      wd, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr, y, s);
+}
+
+}  // namespace
+
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_gate_up_stream(a, s);
   if (a.bf16) {
-    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, GM);
     const int NT = (a.N + GN / 2 - 1) / (GN / 2);
-    auto kf = gemm256_kernel<true, kGuWM, kGuWN, kGuStages, float>;
-    const int lds = kGuStages * kStageBytes;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kf, dim3(RT * NT), dim3(64 * kGuWM * kGuWN), lds, s, a.H, a.N, a.E, a.K,
-                       a.rows, (int)a.ident, NT, static_cast<const bf16*>(a.x),
-                       static_cast<const bf16*>(a.w_gate), static_cast<const bf16*>(a.w_up),
-                       a.w_stride, a.offsets, a.sorted_slots, nullptr, static_cast<bf16*>(a.h),
-                       nullptr);
+    const bf16* x = static_cast<const bf16*>(a.x);
+    const bf16* wg = static_cast<const bf16*>(a.w_gate);
+    const bf16* wu = static_cast<const bf16*>(a.w_up);
+    bf16* h = static_cast<bf16*>(a.h);
+    const hipError_t e = launch_grouped<true, 256, 4, 2, 5, float>(
+          a.H, a.N, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
+          x, wg, wu, a.w_stride, a.offsets, a.sorted_slots, nullptr, h, nullptr, s);
+    if (e != hipSuccess) return e;
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.N + kFT - 1) / kFT);
     hipLaunchKernelGGL(gate_up_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.K, a.rows,
@@ -457,29 +488,8 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_down_stream(a, s);
   if (a.bf16) {
-    const int RT = row_tile_bound(a.ident, a.rows, a.T, a.E, GM);
-    const int NT = (a.H + GN - 1) / GN;
-    const int lds = kDnStages * kStageBytes + GM * 8;  // ring + per-row slot and weight
-    const dim3 grid(RT * NT), block(64 * kDnWM * kDnWN);
-    const bf16* hb = static_cast<const bf16*>(a.h);
-    const bf16* wd = static_cast<const bf16*>(a.w_down);
-    if (a.y_bf16) {
-      auto kf = gemm256_kernel<false, kDnWM, kDnWN, kDnStages, bf16>;
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL(kf, grid, block, lds, s, a.N, a.H, a.E, a.K, a.rows, (int)a.ident, NT, hb,
-                         wd, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr,
-                         static_cast<bf16*>(a.y));
-    } else {
-      auto kf = gemm256_kernel<false, kDnWM, kDnWN, kDnStages, float>;
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL(kf, grid, block, lds, s, a.N, a.H, a.E, a.K, a.rows, (int)a.ident, NT, hb,
-                         wd, wd, a.w_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr,
-                         static_cast<float*>(a.y));
-    }
+    const hipError_t e = a.y_bf16 ? launch_down_tiled<bf16>(a, s) : launch_down_tiled<float>(a, s);
+    if (e != hipSuccess) return e;
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.H + 2 * kFT - 1) / (2 * kFT));
     hipLaunchKernelGGL(down_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
