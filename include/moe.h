@@ -200,7 +200,12 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
  *   out = (o + x) * layer_scalar
  * residual x and out: [T,H] act dtype.  ffn_out (optional, [T,H] fp32) receives
  * o, the layer's output before the residual; topk_idx / topk_w (optional)
- * receive the routing.  Requires dims->dense_inter > 0. */
+ * receive the routing.  Requires dims->dense_inter > 0.
+ * The dense branch runs on a stream owned by the library (one per device,
+ * created on the first call and kept until the process ends), forked from
+ * `stream` after the pre-norms and joined back before the epilogue, so it
+ * overlaps the router and the experts; all work is still ordered after the
+ * earlier work on `stream`, and later work on `stream` waits for all of it. */
 int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
                      const gemma4_ffn_weights* weights, void* out, float* ffn_out,
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,

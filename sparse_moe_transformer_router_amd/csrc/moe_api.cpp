@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -120,6 +121,32 @@ Layout layout(const moe_dims* d, long long T) {
   L.counter = take(4);
   L.total = o;
   return L;
+}
+
+// The block's dense branch runs on a library-owned side stream (one per
+// device, default priority, created on first use and kept), forked from and
+// joined back into the caller's stream with two events.  A mutex keeps one
+// call's record / wait sequence from interleaving with another thread's.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(SideStream*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr) {
+    if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  out = &ss;
+  return hipSuccess;
 }
 
 template <typename P>
@@ -404,25 +431,39 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
   hipError_t e = moe::launch_prenorm(pn, s);
   if (e != hipSuccess) return hip_fail(e, "gemma4_ffn_block (prenorm)");
 
-  if ((rc = run_router(dims, T, residual, wt->router_w, wt->router_scale, wt->per_expert_scale,
-                       wt->g_pre2, idx, w, counts, offsets, sorted, ws, s)))
-    return rc;
-  if ((rc = run_expert_ffn(dims, T, xm, wt->w_gate_up, wt->w_down, w, offsets, sorted, y, ws, s)))
-    return rc;
+  // dense branch on the side stream, after the pre-norms
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  if ((e = side_stream(side)) != hipSuccess) return hip_fail(e, "gemma4_ffn_block (side stream)");
+  hipStream_t s2 = side->stream;
+  if ((e = hipEventRecord(side->fork, s)) != hipSuccess ||
+      (e = hipStreamWaitEvent(s2, side->fork, 0)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (fork)");
 
   moe::GateUpArgs g{};
   g.T = T; g.H = dims->hidden; g.N = dims->dense_inter; g.E = 1; g.K = 1; g.rows = T;
   g.ident = true; g.bf16 = bf; g.x = xd; g.w_gate = wt->dense_gate; g.w_up = wt->dense_up;
   g.w_stride = 0; g.offsets = nullptr; g.sorted_slots = nullptr; g.h = hd;
-  if ((e = moe::launch_gate_up(g, s)) != hipSuccess)
+  if ((e = moe::launch_gate_up(g, s2)) != hipSuccess)
     return hip_fail(e, "gemma4_ffn_block (dense gate_up)");
   moe::DownArgs dd{};
   dd.T = T; dd.H = dims->hidden; dd.N = dims->dense_inter; dd.E = 1; dd.K = 1; dd.rows = T;
   dd.ident = true; dd.bf16 = bf; dd.y_bf16 = dims->slot_dtype == MOE_BF16; dd.h = hd;
   dd.w_down = wt->dense_down; dd.w_stride = 0; dd.offsets = nullptr; dd.sorted_slots = nullptr;
   dd.topk_w = nullptr; dd.y = dn;
-  if ((e = moe::launch_down(dd, s)) != hipSuccess)
+  if ((e = moe::launch_down(dd, s2)) != hipSuccess)
     return hip_fail(e, "gemma4_ffn_block (dense down)");
+  if ((e = hipEventRecord(side->join, s2)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (join)");
+
+  // router and experts on the caller's stream, meanwhile
+  if ((rc = run_router(dims, T, residual, wt->router_w, wt->router_scale, wt->per_expert_scale,
+                       wt->g_pre2, idx, w, counts, offsets, sorted, ws, s)))
+    return rc;
+  if ((rc = run_expert_ffn(dims, T, xm, wt->w_gate_up, wt->w_down, w, offsets, sorted, y, ws, s)))
+    return rc;
+  if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess)
+    return hip_fail(e, "gemma4_ffn_block (join)");
 
   moe::EpilogueArgs ep{};
   ep.T = T; ep.H = dims->hidden; ep.K = dims->top_k; ep.eps = dims->eps;
