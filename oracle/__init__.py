@@ -61,6 +61,10 @@ def lib():
         L.oracle_block.argtypes = ([_I] * 6 + [ctypes.c_float] + [_P] * 15 +
                                    [ctypes.c_double] + [_P] * 5)
         L.oracle_block.restype = None
+        L.oracle_quantize_rows.argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
+        L.oracle_quantize_rows.restype = None
+        L.oracle_dequantize_rows.argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
+        L.oracle_dequantize_rows.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _I
         _lib = L
@@ -173,3 +177,30 @@ def block(x, g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, dens
                        _p(gu), _p(dn), float(layer_scalar), _p(idx), _p(w), _p(out), _p(o),
                        _p(moe))
     return {"out": out, "o": o, "moe": moe, "idx": idx, "w": w}
+
+
+def quantize_int8(w):
+    """Per-row symmetric int8: returns (q int8 same shape, s fp32 [rows...]).
+    The last axis is the channel's input dimension."""
+    w = _f32(w)
+    shape = w.shape
+    rows = int(np.prod(shape[:-1]))
+    q = np.zeros(shape, np.int8)
+    s = np.zeros(shape[:-1], np.float32)
+    lib().oracle_quantize_rows(rows, shape[-1], _p(w), _p(q), _p(s))
+    return q, s
+
+
+def dequantize_int8(q, s):
+    """q * s rounded once to fp32, shape of q."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = _f32(s)
+    out = np.zeros(q.shape, np.float32)
+    lib().oracle_dequantize_rows(int(np.prod(q.shape[:-1])), q.shape[-1], _p(q), _p(s), _p(out))
+    return out
+
+
+def experts_int8(xin, gate_up_q, gate_up_s, down_q, down_s, idx, w):
+    """The sparse expert loop (fp64) on the dequantized int8 weights."""
+    return experts(xin, dequantize_int8(gate_up_q, gate_up_s), dequantize_int8(down_q, down_s),
+                   idx, w)

@@ -304,6 +304,45 @@ void oracle_block(int T, int H, int E, int K, int I, int D, float eps,
   free(xd); free(xm); free(dn); free(t1); free(t2);
 }
 
+/* ---------------------------------------------------------------------------
+ * int8 per-channel symmetric weights (the int8-expert variant on the page
+ * "Porting a 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section
+ * "Can it run on a smaller box? Yes, no, and "deeper than it looks"").
+ * Reading: a channel is one output row of an [out, in] weight; its scale is
+ * s = max |w| / 127 (fp32 division), its codes q = round-half-to-even(w / s)
+ * (fp32 division) clamped to [-127, 127]; a row of zeros gets s = 0, q = 0.
+ * The dequantized weight is q * s.
+ * ------------------------------------------------------------------------- */
+void oracle_quantize_rows(long long rows, int cols, const float* w, int8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    const float* wr = w + r * cols;
+    float amax = 0.0f;
+    for (int c = 0; c < cols; ++c) {
+      const float a = fabsf(wr[c]);
+      if (a > amax) amax = a;
+    }
+    const float sc = amax / 127.0f;
+    s[r] = sc;
+    for (int c = 0; c < cols; ++c) {
+      float v = 0.0f;
+      if (sc > 0.0f) v = rintf(wr[c] / sc);
+      if (v > 127.0f) v = 127.0f;
+      if (v < -127.0f) v = -127.0f;
+      q[r * cols + c] = (int8_t)v;
+    }
+  }
+}
+
+/* Dequantized weights as fp32: out = q * s rounded once to fp32. */
+void oracle_dequantize_rows(long long rows, int cols, const int8_t* q, const float* s,
+                            float* out) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c)
+      out[r * cols + c] = (float)((double)q[r * cols + c] * (double)s[r]);
+}
+
 /* Number of OpenMP threads the parallel loops use. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
