@@ -178,6 +178,30 @@ int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* 
                     const float* topk_w, const int32_t* expert_offsets,
                     const int32_t* sorted_slots, void* y_slots, void* stream);
 
+/* int8 per-channel symmetric weights, the int8-expert variant on the page
+ * "Porting a 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section
+ * "Can it run on a smaller box? Yes, no, and "deeper than it looks"".
+ * moe_quantize_int8: w is rows x cols bf16 (row-major; a row is one output
+ * channel, cols % 8 == 0); writes scale[r] = max_c |w[r,c]| / 127 and
+ * q[r,c] = round-half-to-even(w[r,c] / scale[r]) clamped to [-127, 127]
+ * (fp32 divisions; a zero row gives scale 0 and codes 0).  For the experts:
+ * quantize gate_up as E*2I rows of H and down as E*H rows of I.  Deterministic
+ * and exact: codes and scales are the same on any IEEE machine.  Device
+ * pointers, 16-byte aligned; returns MOE_ERR_ARG on bad sizes or pointers.
+ *
+ * moe_expert_ffn_int8: moe_expert_ffn with the experts' weights as int8 codes
+ * and per-row scales (gate_up: codes [E,2I,H], scales [E,2I]; down: codes
+ * [E,H,I], scales [E,H]).  The code rows enter bf16 MFMAs exactly and each
+ * output channel is multiplied by its scale after the k-sum.  Decode
+ * batches only (T <= 64, act dtype bf16), else MOE_ERR_UNSUPPORTED. */
+int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
+                      void* stream);
+int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
+                        const int8_t* w_gate_up_q, const float* w_gate_up_scale,
+                        const int8_t* w_down_q, const float* w_down_scale, const float* topk_w,
+                        const int32_t* expert_offsets, const int32_t* sorted_slots,
+                        void* y_slots, void* ws, size_t ws_bytes, void* stream);
+
 /* The experts' scatter-add: out[t] = sum_{k=0..K-1} y_slots[t,k] (fp32, k
  * ascending, no atomics) + addend[t] (if addend is not NULL).
  * y_slots slot dtype; addend and out act dtype. */

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_stream.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_stream.hip", "combine.hip", "quant.hip",
+           "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 vector instructions are disabled: plain fp32 code is compiled

@@ -49,6 +49,38 @@ __device__ __forceinline__ void zero_frag(Frag& f) {
   for (int i = 0; i < 2; ++i) f.u[i] = make_uint4(0, 0, 0, 0);
 }
 
+// One lane's weights for one k-block, held raw in the register ring until
+// its MFMAs: 16 bf16 (32 B), or 16 int8 codes (16 B) that become bf16 at use
+// (exact: |q| <= 127 needs 7 significant bits).
+template <typename WQ> struct WRaw;
+template <> struct WRaw<bf16> {
+  Frag f;
+  __device__ __forceinline__ void load(const bf16* p) { ld_frag(f, p); }
+  __device__ __forceinline__ void zero() { zero_frag(f); }
+  __device__ __forceinline__ Frag frag() const { return f; }
+};
+template <> struct WRaw<int8_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const int8_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ Frag frag() const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t word = w[m / 2];
+      const int b0 = 2 * (m % 2);  // bytes b0, b0 + 1 of word: elements 2m, 2m + 1
+      const float lo = (float)((int32_t)(word << (24 - 8 * b0)) >> 24);
+      const float hi = (float)((int32_t)(word << (16 - 8 * b0)) >> 24);
+      o[m] = (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
+    }
+    Frag f;
+    f.u[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    f.u[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    return f;
+  }
+};
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -66,10 +98,11 @@ __device__ __forceinline__ bool stream_tile(bool ident, int rows, const int32_t*
 
 // gate_up: one block = one row tile (<= 16 * MB rows) x 16 gate + 16 up
 // columns; its WK waves split H.
-template <int WK, int MB, int NS>
+template <typename WQ, int WK, int MB, int NS>
 __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     int H, int N, int E, int K, int rows, int ident, const bf16* __restrict__ x,
-    const bf16* __restrict__ wg, const bf16* __restrict__ wu, long long w_stride,
+    const WQ* __restrict__ wg, const WQ* __restrict__ wu, long long w_stride,
+    const float* __restrict__ sg, const float* __restrict__ su, long long s_stride,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     bf16* __restrict__ h) {
   __shared__ f32x4 red[WK][MB][2][kWave];
@@ -80,8 +113,8 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
   const int n = blockIdx.y * 16 + fr;
   const bool nvalid = n < N;
   const size_t woff = (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * H + 16 * fg;
-  const bf16* gp = wg + woff;
-  const bf16* up = wu + woff;
+  const WQ* gp = wg + woff;
+  const WQ* up = wu + woff;
   const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
   const bf16* ap[MB];
   bool av[MB];
@@ -101,16 +134,17 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     accg[mb] = f32x4{0, 0, 0, 0};
     accu[mb] = f32x4{0, 0, 0, 0};
   }
-  Frag bg[NS], bu[NS], ba[NS][MB];
-  auto load = [&](int kb, Frag& g, Frag& u, Frag (&a)[MB]) {
+  WRaw<WQ> bg[NS], bu[NS];
+  Frag ba[NS][MB];
+  auto load = [&](int kb, WRaw<WQ>& g, WRaw<WQ>& u, Frag (&a)[MB]) {
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < H;
     if (nvalid && kv) {
-      ld_frag(g, gp + k);
-      ld_frag(u, up + k);
+      g.load(gp + k);
+      u.load(up + k);
     } else {
-      zero_frag(g);
-      zero_frag(u);
+      g.zero();
+      u.zero();
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -127,13 +161,14 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
       if (kl < kb1) load(kl, bg[(s + NS - 1) % NS], bu[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
+      const Frag fgt = bg[s].frag(), fup = bu[s].frag();
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           if (mb < nmb) {
-            accg[mb] = mfma16(ba[s][mb].v[j], bg[s].v[j], accg[mb]);
-            accu[mb] = mfma16(ba[s][mb].v[j], bu[s].v[j], accu[mb]);
+            accg[mb] = mfma16(ba[s][mb].v[j], fgt.v[j], accg[mb]);
+            accu[mb] = mfma16(ba[s][mb].v[j], fup.v[j], accu[mb]);
           }
     }
   }
@@ -153,6 +188,10 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
       g += red[w][mb][0][lane];
       u += red[w][mb][1][lane];
     }
+    if (sg != nullptr && nvalid) {  // int8 codes: the channel scales
+      g *= sg[(size_t)e * s_stride + n];
+      u *= su[(size_t)e * s_stride + n];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 16 * mb + 4 * fg + r;
@@ -163,10 +202,11 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
 
 // down: one block = one row tile x 16 * WN output columns; WK waves split
 // the contraction (the intermediate width N).
-template <int WN, int WK, int MB, int NS, typename YT>
+template <typename WQ, int WN, int WK, int MB, int NS, typename YT>
 __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
-    const bf16* __restrict__ wd, long long w_stride, const int32_t* __restrict__ offsets,
+    const WQ* __restrict__ wd, long long w_stride, const float* __restrict__ sd,
+    long long s_stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
     YT* __restrict__ y) {
   __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][kWave];
@@ -177,7 +217,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   const int fr = lane % 16, fg = lane / 16;
   const int n = blockIdx.y * 16 * WN + 16 * wn + fr;
   const bool nvalid = n < H;
-  const bf16* bp = wd + (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * N + 16 * fg;
+  const WQ* bp = wd + (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * N + 16 * fg;
   const int nmb = (row1 - row0 + 15) / 16;
   const bf16* ap[MB];
   bool av[MB];
@@ -193,12 +233,13 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   f32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0, 0, 0, 0};
-  Frag bb[NS], ba[NS][MB];
-  auto load = [&](int kb, Frag& b, Frag (&a)[MB]) {
+  WRaw<WQ> bb[NS];
+  Frag ba[NS][MB];
+  auto load = [&](int kb, WRaw<WQ>& b, Frag (&a)[MB]) {
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < N;
-    if (nvalid && kv) ld_frag(b, bp + k);
-    else zero_frag(b);
+    if (nvalid && kv) b.load(bp + k);
+    else b.zero();
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb < nmb && av[mb] && kv) ld_frag(a[mb], ap[mb] + k);
@@ -214,11 +255,12 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
       if (kl < kb1) load(kl, bb[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
+      const Frag fb = bb[s].frag();
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          if (mb < nmb) acc[mb] = mfma16(ba[s][mb].v[j], bb[s].v[j], acc[mb]);
+          if (mb < nmb) acc[mb] = mfma16(ba[s][mb].v[j], fb.v[j], acc[mb]);
     }
   }
   if constexpr (WK > 1) {
@@ -233,9 +275,11 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       for (int w = 1; w < WK; ++w) acc[mb] += red[wn + w * WN][mb][lane];
     }
   }
+  const float chs = (sd != nullptr && nvalid) ? sd[(size_t)e * s_stride + n] : 1.0f;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (mb >= nmb) break;
+    if (sd != nullptr) acc[mb] *= chs;  // int8 codes: the channel scale
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 16 * mb + 4 * fg + r;
@@ -254,28 +298,31 @@ int tile_bound(bool ident, int rows, int T, int E, int bm) {
   return (int)(a < b ? a : b);
 }
 
-template <int WK, int MB, int NS>
+template <typename WQ, int WK, int MB, int NS>
 void launch_gu(const GateUpArgs& a, hipStream_t s) {
   dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.N + 15) / 16);
-  hipLaunchKernelGGL((gate_up_stream_kernel<WK, MB, NS>), grid, dim3(64 * WK), 0, s, a.H, a.N,
+  hipLaunchKernelGGL((gate_up_stream_kernel<WQ, WK, MB, NS>), grid, dim3(64 * WK), 0, s, a.H, a.N,
                      a.E, a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
-                     static_cast<const bf16*>(a.w_gate), static_cast<const bf16*>(a.w_up),
-                     a.w_stride, a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
+                     static_cast<const WQ*>(a.w_gate), static_cast<const WQ*>(a.w_up), a.w_stride,
+                     a.w_int8 ? a.s_gate : nullptr, a.w_int8 ? a.s_up : nullptr, a.s_stride,
+                     a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
 }
 
-template <int WN, int WK, int MB, int NS, typename YT>
+template <typename WQ, int WN, int WK, int MB, int NS, typename YT>
 void launch_dn(const DownArgs& a, hipStream_t s) {
   dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.H + 16 * WN - 1) / (16 * WN));
-  hipLaunchKernelGGL((down_stream_kernel<WN, WK, MB, NS, YT>), grid, dim3(64 * WN * WK), 0, s,
+  hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, YT>), grid, dim3(64 * WN * WK), 0, s,
                      a.H, a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
-                     static_cast<const bf16*>(a.w_down), a.w_stride, a.offsets, a.sorted_slots,
+                     static_cast<const WQ*>(a.w_down), a.w_stride,
+                     a.w_int8 ? a.s_down : nullptr, a.s_stride, a.offsets, a.sorted_slots,
                      a.topk_w, static_cast<YT*>(a.y));
 }
 
 template <typename YT>
 void launch_dn_t(const DownArgs& a, hipStream_t s) {
-  if (a.T <= 8) launch_dn<2, 2, 1, 2, YT>(a, s);
-  else launch_dn<4, 1, 1, 2, YT>(a, s);
+  if (a.w_int8) launch_dn<int8_t, 4, 1, 1, 4, YT>(a, s);
+  else if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, YT>(a, s);
+  else launch_dn<bf16, 4, 1, 1, 2, YT>(a, s);
 }
 
 }  // namespace
@@ -287,15 +334,16 @@ bool use_stream_kernels(int T, bool ident) { return T <= 64; }
 // projection splits the contraction over 4 waves to keep enough loads in
 // flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
-  if (a.ident) launch_gu<8, 2, 2>(a, s);
-  else launch_gu<8, 1, 3>(a, s);
+  if (a.w_int8) launch_gu<int8_t, 8, 1, 4>(a, s);
+  else if (a.ident) launch_gu<bf16, 8, 2, 2>(a, s);
+  else launch_gu<bf16, 8, 1, 3>(a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s) {
-  if (a.ident) {
-    if (a.y_bf16) launch_dn<2, 4, 2, 2, bf16>(a, s);
-    else launch_dn<2, 4, 2, 2, float>(a, s);
+  if (a.ident && !a.w_int8) {
+    if (a.y_bf16) launch_dn<bf16, 2, 4, 2, 2, bf16>(a, s);
+    else launch_dn<bf16, 2, 4, 2, 2, float>(a, s);
   } else if (a.y_bf16) {
     launch_dn_t<bf16>(a, s);
   } else {

@@ -62,6 +62,12 @@ struct GateUpArgs {
   const int32_t* offsets;      // [E+1] (unused when ident)
   const int32_t* sorted_slots; // [rows] (unused when ident)
   void* h;                     // [rows, N] act dtype, sorted order
+  // int8 weights (decode sizes only): w_gate / w_up hold int8 codes and each
+  // weight row n of group e is scaled by s_gate / s_up[e * s_stride + n].
+  bool w_int8;
+  const float* s_gate;
+  const float* s_up;
+  long long s_stride;
 };
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s);
 
@@ -81,6 +87,9 @@ struct DownArgs {
   const int32_t* sorted_slots;
   const float* topk_w;         // [T*K] (unused when ident)
   void* y;                     // [T*K, H] slot-major (or [T,H] when ident)
+  bool w_int8;                 // int8 codes, row n of group e scaled by s_down[e * s_stride + n]
+  const float* s_down;
+  long long s_stride;
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
@@ -88,6 +97,11 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s);
 bool use_stream_kernels(int T, bool ident);
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s);
+
+// int8 per-channel symmetric quantization of rows x cols bf16 weights
+// (cols % 8 == 0): codes q [rows, cols], scales [rows].
+hipError_t launch_quantize_rows(long long rows, int cols, const void* w, int8_t* q, float* scale,
+                                hipStream_t s);
 
 struct CombineArgs {
   int T, H, K;

@@ -240,6 +240,31 @@ int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_ga
   return run_down(d, T, h, w_down, topk_w, offsets, sorted, y, s);
 }
 
+int run_expert_ffn_int8(const moe_dims* d, int32_t T, const void* x, const int8_t* guq,
+                        const float* gus, const int8_t* dnq, const float* dns,
+                        const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                        void* y, void* ws, hipStream_t s) {
+  void* h = at<void>(ws, layout(d, T).h);
+  const long long H = d->hidden, I = d->expert_inter;
+  moe::GateUpArgs g{};
+  g.T = T; g.H = d->hidden; g.N = d->expert_inter; g.E = d->num_experts; g.K = d->top_k;
+  g.rows = T * d->top_k; g.ident = false; g.bf16 = true;
+  g.x = x; g.w_gate = guq; g.w_up = guq + I * H; g.w_stride = 2 * I * H;
+  g.offsets = offsets; g.sorted_slots = sorted; g.h = h;
+  g.w_int8 = true; g.s_gate = gus; g.s_up = gus + I; g.s_stride = 2 * I;
+  hipError_t e = moe::launch_gate_up_stream(g, s);
+  if (e != hipSuccess) return hip_fail(e, "expert gate_up (int8)");
+  moe::DownArgs dn{};
+  dn.T = T; dn.H = d->hidden; dn.N = d->expert_inter; dn.E = d->num_experts; dn.K = d->top_k;
+  dn.rows = T * d->top_k; dn.ident = false; dn.bf16 = true;
+  dn.y_bf16 = d->slot_dtype == MOE_BF16;
+  dn.h = h; dn.w_down = dnq; dn.w_stride = H * I;
+  dn.offsets = offsets; dn.sorted_slots = sorted; dn.topk_w = topk_w; dn.y = y;
+  dn.w_int8 = true; dn.s_down = dns; dn.s_stride = H;
+  e = moe::launch_down_stream(dn, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down (int8)");
+}
+
 int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend, void* out,
                 hipStream_t s) {
   moe::CombineArgs a{};
@@ -325,6 +350,39 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w
   if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
   return run_expert_ffn(dims, T, x, w_gate_up, w_down, topk_w, expert_offsets, sorted_slots,
                         y_slots, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
+                      void* stream) {
+  g_err.clear();
+  if (rows < 0 || rows > (int64_t)1 << 36) return fail(MOE_ERR_ARG, "rows out of range");
+  if (cols <= 0 || cols % 8 != 0) return fail(MOE_ERR_ARG, "cols must be a positive multiple of 8");
+  if (rows == 0) return MOE_OK;
+  REQUIRE_PTR(w); REQUIRE_PTR(q); REQUIRE_PTR(scale);
+  hipError_t e = moe::launch_quantize_rows(rows, cols, w, q, scale,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_int8");
+}
+
+int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x, const int8_t* w_gate_up_q,
+                        const float* w_gate_up_scale, const int8_t* w_down_q,
+                        const float* w_down_scale, const float* topk_w,
+                        const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (dims->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "int8 experts take bf16 activations");
+  if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "int8 experts: decode batches (T <= 64) only");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
+  REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_expert_ffn_int8(dims, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
+                             topk_w, expert_offsets, sorted_slots, y_slots, ws,
+                             static_cast<hipStream_t>(stream));
 }
 
 int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,

@@ -60,10 +60,13 @@ def _load():
     L.moe_expert_down.argtypes = [D, I32] + [P] * 7
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
+    L.moe_quantize_int8.argtypes = [ctypes.c_int64, I32, P, P, P, P]
+    L.moe_expert_ffn_int8.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
         [SZ, P]
     for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
-              "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block"):
+              "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
+              "moe_quantize_int8", "moe_expert_ffn_int8"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -145,6 +148,23 @@ def moe_expert_ffn(d, T, x, w_gate_up, w_down, topk_w, offsets, sorted_slots, y_
     _check(_lib.moe_expert_ffn(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up), _ptr(w_down),
                                _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots), _ptr(y_slots),
                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_quantize_int8(w, q, scale, stream=None):
+    """Per-row symmetric int8 codes and scales of a bf16 weight whose last axis
+    is the row (input) dimension."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    _check(_lib.moe_quantize_int8(rows, cols, _ptr(w), _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def moe_expert_ffn_int8(d, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale, topk_w,
+                        offsets, sorted_slots, y_slots, ws, stream=None):
+    _check(_lib.moe_expert_ffn_int8(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up_q),
+                                    _ptr(w_gate_up_scale), _ptr(w_down_q), _ptr(w_down_scale),
+                                    _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots),
+                                    _ptr(y_slots), _ptr(ws), ws.numel() if ws is not None else 0,
+                                    _stream(stream)))
 
 
 def moe_expert_gate_up(d, T, x, w_gate_up, offsets, sorted_slots, h, stream=None):

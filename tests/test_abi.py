@@ -133,3 +133,24 @@ def test_other_calls_validate():
     assert L.moe_combine(dp, 4, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
     assert L.moe_forward(dp, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE,
                          1 << 40, None) == lib_mod.MOE_ERR_ARG
+
+
+def test_int8_entry_points_validate_on_the_host():
+    q = L.moe_quantize_int8
+    assert q(0, 64, None, None, None, None) == lib_mod.MOE_OK
+    assert q(-1, 64, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert q(4, 60, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG and "cols" in lib_mod.last_error()
+    assert q(4, 64, None, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert q(4, 64, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
+    f = L.moe_expert_ffn_int8
+    d = D()
+    args = [FAKE] * 10
+    assert f(ctypes.byref(d), 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
+    assert f(ctypes.byref(d), 65, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert "T <= 64" in lib_mod.last_error()
+    d32 = D(act=lib_mod.MOE_F32)
+    assert f(ctypes.byref(d32), 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[2] = None  # gate_up scales
+    assert f(ctypes.byref(d), 4, *bad, 1 << 40, None) == lib_mod.MOE_ERR_ARG
+    assert f(ctypes.byref(d), 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
