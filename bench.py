@@ -219,6 +219,67 @@ def prefill_measure(torch, wl, T, steps, warmup, seed):
     }
 
 
+def int8_decode_measure(torch, lib, wl, T, steps, warmup, xbatches, seed):
+    """Decode with the experts as int8 per-channel symmetric codes (quantized
+    on the GPU from the same weight copies): route, int8 experts, combine."""
+    qcopies = []
+    for rw, rs, pes, gu, dn in wl.copies:
+        guq = torch.empty(gu.shape, dtype=torch.int8, device="cuda")
+        gus = torch.empty(gu.shape[:-1], dtype=torch.float32, device="cuda")
+        dnq = torch.empty(dn.shape, dtype=torch.int8, device="cuda")
+        dns = torch.empty(dn.shape[:-1], dtype=torch.float32, device="cuda")
+        lib.moe_quantize_int8(gu, guq, gus)
+        lib.moe_quantize_int8(dn, dnq, dns)
+        qcopies.append((rw, rs, pes, guq, gus, dnq, dns))
+    torch.cuda.synchronize()
+    r = Runner(wl, T)
+    xs = wl.batches(T, xbatches, seed)
+    d = wl.dims
+
+    def step(i, ev=None):
+        rw, rs, pes, guq, gus, dnq, dns = qcopies[i % len(qcopies)]
+        x = xs[i % len(xs)]
+        if ev is not None:
+            ev[0].record()
+        lib.moe_route(d, T, x, rw, rs, pes, None, r.idx, r.w, r.counts, r.offsets, r.sorted, r.ws)
+        if ev is not None:
+            ev[1].record()
+        lib.moe_expert_ffn_int8(d, T, x, guq, gus, dnq, dns, r.w, r.offsets, r.sorted, r.y, r.ws)
+        if ev is not None:
+            ev[2].record()
+        lib.moe_combine(d, T, r.y, None, r.out)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    seg = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+           for j, name in enumerate(("route", "experts", "combine"))}
+    us = []
+    for i in range(len(qcopies)):
+        step(i)
+        torch.cuda.synchronize()
+        us.append(int((r.counts > 0).sum().item()))
+    U = sum(us) / len(us)
+    per_expert = (GATE_UP_BYTES + DOWN_BYTES) // 2 + (2 * I + H) * 4  # codes + scales
+    expert_bytes = U * per_expert + T * H * 2
+    step_bytes = U * per_expert + ROUTER_BYTES + 2 * T * H * 2
+    return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "distinct_experts": U, "kernel_ms": seg, "weights": "int8 per-channel symmetric",
+            "experts_gbs": expert_bytes / (seg["experts"] * 1e-3) / 1e9,
+            "experts_hbm_frac": expert_bytes / (seg["experts"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 class BlockLayer:
     """One block's weights (resident on the GPU) and its C-ABI weight struct."""
 
@@ -487,6 +548,9 @@ def main():
         prefill = prefill_measure(torch, wl, args.prefill, max(5, args.steps // 5),
                                   max(2, args.warmup // 5), args.seed)
 
+    int8 = int8_decode_measure(torch, lib, wl, args.batch, args.steps, args.warmup,
+                               args.xbatches, args.seed)
+
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
 
     block, layers = None, []
@@ -534,6 +598,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {str(args.batch): head, **sweep},
         "prefill": prefill,
+        "int8_experts_decode": int8,
         "tiny_f32": tiny,
         "block": block,
         "stack": stack,

@@ -320,7 +320,7 @@ void launch_dn(const DownArgs& a, hipStream_t s) {
 
 template <typename YT>
 void launch_dn_t(const DownArgs& a, hipStream_t s) {
-  if (a.w_int8) launch_dn<int8_t, 4, 1, 1, 4, YT>(a, s);
+  if (a.w_int8) launch_dn<int8_t, 2, 2, 1, 2, YT>(a, s);
   else if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, YT>(a, s);
   else launch_dn<bf16, 4, 1, 1, 2, YT>(a, s);
 }
@@ -334,7 +334,7 @@ bool use_stream_kernels(int T, bool ident) { return T <= 64; }
 // projection splits the contraction over 4 waves to keep enough loads in
 // flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
-  if (a.w_int8) launch_gu<int8_t, 8, 1, 4>(a, s);
+  if (a.w_int8) launch_gu<int8_t, 4, 1, 2>(a, s);
   else if (a.ident) launch_gu<bf16, 8, 2, 2>(a, s);
   else launch_gu<bf16, 8, 1, 3>(a, s);
   return hipGetLastError();
