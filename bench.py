@@ -535,23 +535,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def done(leg):
+        print(f"bench: {leg} done", file=sys.stderr, flush=True)
+
     head, runner, xs = decode_measure(torch, wl, args.batch, args.steps, args.warmup,
                                       args.xbatches, args.seed)
+    done(f"decode {args.batch}")
     sweep = {}
     for b in [int(v) for v in args.sweep.split(",") if v.strip()]:
         if b != args.batch:
             r, _, _ = decode_measure(torch, wl, b, args.steps, args.warmup, args.xbatches,
                                      args.seed)
             sweep[str(b)] = r
+            done(f"decode {b}")
     prefill = None
     if args.prefill > 0:
         prefill = prefill_measure(torch, wl, args.prefill, max(5, args.steps // 5),
                                   max(2, args.warmup // 5), args.seed)
+        done(f"prefill {args.prefill}")
 
     int8 = int8_decode_measure(torch, lib, wl, args.batch, args.steps, args.warmup,
                                args.xbatches, args.seed)
+    done("int8 decode")
 
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
+    done("tiny fp32")
 
     block, layers = None, []
     if args.block > 0 or args.stack > 0:
@@ -560,10 +568,12 @@ def main():
     if args.block > 0:
         block = block_measure(torch, lib, args.block, max(5, args.steps // 5),
                               max(2, args.warmup // 5), args.seed, layers[:2])
+        done(f"layer {args.block}")
     stack = None
     if args.stack > 0:
         stack = stack_measure(torch, lib, layers[:args.stack], args.batch, args.stack_steps,
                               args.stack_prefill, args.seed)
+        done(f"stack of {args.stack} layers")
 
     cpu = None
     cpu_configs = None
@@ -571,6 +581,7 @@ def main():
         cpu = cpu_baseline(torch, wl, xs, args.batch, args.cpu_seconds)
         cpu_configs = cpu_oracle_configs(torch, layers[0] if layers else None,
                                          args.cpu_seconds / 2)
+        done("cpu baselines")
 
     achieved = head["gate_up_gbs"]
     line = {
