@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--stack", type=int, default=LAYERS, help="layers in the stack run (0 = skip)")
     ap.add_argument("--stack-steps", type=int, default=128, help="timed decode steps of the stack")
     ap.add_argument("--stack-prefill", type=int, default=8192, help="stack prefill tokens (0 = skip)")
+    ap.add_argument("--dense-mask", type=int, default=1,
+                    help="time the all-experts ablation at the decode and prefill sizes (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
 
@@ -216,6 +218,59 @@ def prefill_measure(torch, wl, T, steps, warmup, seed):
         "grouped_gemm_mfma_frac": flops / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "gate_up_tflops": flops * 2 / 3 / (seg["gate_up"] * 1e-3) / 1e12,
         "down_tflops": flops / 3 / (seg["down"] * 1e-3) / 1e12,
+    }
+
+
+class DenseMaskRunner:
+    """The all-experts form on the same kernels: route (top-K), the
+    all-experts slot layout (every expert takes every token, weight 0 outside
+    the token's top-K), the experts over all T * E slots, and the combine
+    over E slots per token."""
+
+    def __init__(self, wl: Workload, T: int):
+        torch, lib = wl.torch, wl.lib
+        self.wl, self.T = wl, T
+        self.sparse = Runner(wl, T)
+        self.dd = lib.dims(H, E, E, I, 0, 1e-6, lib.MOE_BF16, lib.MOE_F32)
+        self.ws = lib.workspace(self.dd, T)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        self.sorted = torch.empty(T * E, dtype=torch.int32, device="cuda")
+        self.wd = torch.empty(T * E, dtype=torch.float32, device="cuda")
+        self.y = torch.empty(T * E, H, dtype=torch.float32, device="cuda")
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+
+    def step(self, x, copy, ev=None):
+        lib, d, T, sp = self.wl.lib, self.wl.dims, self.T, self.sparse
+        rw, rs, pes, gu, dn = copy
+        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        rec(0)
+        lib.moe_route(d, T, x, rw, rs, pes, None, sp.idx, sp.w, sp.counts, sp.offsets,
+                      sp.sorted, sp.ws)
+        lib.moe_dense_mask_dispatch(d, T, sp.idx, sp.w, self.offsets, self.sorted, self.wd)
+        rec(1)
+        lib.moe_expert_ffn(self.dd, T, x, gu, dn, self.wd, self.offsets, self.sorted, self.y,
+                           self.ws)
+        rec(2)
+        rec(3)
+        lib.moe_combine(self.dd, T, self.y, None, self.out)
+        rec(4)
+
+
+def dense_mask_measure(torch, wl, T, steps, warmup, xbatches, seed, sparse_ms):
+    """The all-experts ablation at T tokens against the sparse path's step time."""
+    runner = DenseMaskRunner(wl, T)
+    xs = wl.batches(T, xbatches, seed)
+    ms, seg, _ = time_steps(torch, runner, xs, wl.copies, steps, warmup)
+    flops = T * E * 6 * H * I
+    return {
+        "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "kernel_ms": {"route_and_layout": seg["route"], "experts": seg["gate_up"],
+                      "combine": seg["combine"]},
+        "expert_flops_executed": flops, "expert_flops_useful": flops * K // E,
+        "experts_tflops_executed": flops / (seg["gate_up"] * 1e-3) / 1e12,
+        "experts_mfma_frac_executed": flops / (seg["gate_up"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "sparse_ms_per_step": sparse_ms,
+        "sparse_speedup": ms / sparse_ms,
     }
 
 
@@ -554,6 +609,17 @@ def main():
                                   max(2, args.warmup // 5), args.seed)
         done(f"prefill {args.prefill}")
 
+    dense_mask = {}
+    if args.dense_mask:
+        dense_mask[str(args.batch)] = dense_mask_measure(
+            torch, wl, args.batch, max(5, args.steps // 5), max(2, args.warmup // 5),
+            args.xbatches, args.seed, head["ms_per_step"])
+        done(f"all-experts ablation {args.batch}")
+        if prefill is not None:
+            dense_mask[str(args.prefill)] = dense_mask_measure(
+                torch, wl, args.prefill, 5, 2, 2, args.seed, prefill["ms_per_step"])
+            done(f"all-experts ablation {args.prefill}")
+
     int8 = int8_decode_measure(torch, lib, wl, args.batch, args.steps, args.warmup,
                                args.xbatches, args.seed)
     done("int8 decode")
@@ -609,6 +675,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {str(args.batch): head, **sweep},
         "prefill": prefill,
+        "dense_masked_ablation": dense_mask or None,
         "int8_experts_decode": int8,
         "tiny_f32": tiny,
         "block": block,

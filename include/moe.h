@@ -156,6 +156,23 @@ int moe_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Slot layout of the all-experts form of the experts (the page "Porting a
+ * 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section "The
+ * traceable trick: compute all experts, mask to top-8"): every expert takes
+ * every token, weighted by the token's routing weight for it, which is 0 for
+ * an expert outside its top-K; the sum over experts equals the sparse form's
+ * sum over its K slots.  From the routing (topk_idx, topk_w [T,K], K =
+ * dims->top_k) it writes, for E = dims->num_experts: expert_offsets[e] = e*T
+ * (e = 0..E), sorted_slots[e*T + t] = t*E + e, w_dense[t*E + e] = topk_w[t,k]
+ * when topk_idx[t,k] == e, else 0.  Pass these to moe_expert_ffn and
+ * moe_combine with top_k = E (those calls take any top_k up to num_experts)
+ * and a workspace sized for that top_k.  Integer and copy work only, exact.
+ * Device pointers, 16-byte aligned; T*E must not exceed 2^20
+ * (MOE_ERR_UNSUPPORTED). */
+int moe_dense_mask_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
+                            const float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                            float* w_dense, void* stream);
+
 /* The experts (Gemma4TextExperts' compute): for every slot s = t*K+k routed
  * to expert e, y_slots[t,k,:] = topk_w[t,k] * down[e] (gelu_tanh(gate[e] x_t)
  * * (up[e] x_t)).  x: [T,H] expert input (act dtype).  bf16 path: bf16 MFMA

@@ -77,7 +77,36 @@ __global__ __launch_bounds__(kChunkSlots) void dispatch_scatter_kernel(
   sorted_slots[offsets[e] + blk_base[(size_t)blockIdx.x * E + e] + local_rank[s]] = s;
 }
 
+// Slot layout of the all-experts form ("Porting a 128-expert MoE (Gemma-4
+// 26B-A4B) to AWS Inferentia2", section "The traceable trick: compute all
+// experts, mask to top-8"): every expert takes every token, slot t * E + e,
+// expert e's rows in token order, each slot weighted by the token's routing
+// weight for e, or 0 when e is not among its top-K.  One thread per slot.
+__global__ __launch_bounds__(256) void dense_mask_kernel(
+    int T, int E, int K, const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
+    float* __restrict__ w_dense) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i <= E) offsets[i] = (int32_t)(i * T);
+  if (i >= (long long)T * E) return;
+  const int t = (int)(i / E), e = (int)(i % E);
+  float w = 0.0f;
+  for (int k = 0; k < K; ++k)
+    if (topk_idx[(size_t)t * K + k] == e) w = topk_w[(size_t)t * K + k];
+  w_dense[i] = w;
+  sorted_slots[(size_t)e * T + t] = (int32_t)i;
+}
+
 }  // namespace
+
+hipError_t launch_dense_mask(int T, int E, int K, const int32_t* topk_idx, const float* topk_w,
+                             int32_t* offsets, int32_t* sorted_slots, float* w_dense,
+                             hipStream_t s) {
+  const long long n = (long long)T * E > E + 1 ? (long long)T * E : E + 1;
+  hipLaunchKernelGGL(dense_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, E,
+                     K, topk_idx, topk_w, offsets, sorted_slots, w_dense);
+  return hipGetLastError();
+}
 
 int dispatch_num_blocks(int S) { return (S + kChunkSlots - 1) / kChunkSlots; }
 

@@ -463,7 +463,7 @@ hipError_t launch_down_tiled(const DownArgs& a, hipStream_t s) {
 
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_gate_up_stream(a, s);
+  if (a.bf16 && use_stream_kernels(a.T, a.rows, a.E, a.ident)) return launch_gate_up_stream(a, s);
   if (a.bf16) {
     const int NT = (a.N + GN / 2 - 1) / (GN / 2);
     const bf16* x = static_cast<const bf16*>(a.x);
@@ -486,7 +486,7 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
 
 hipError_t launch_down(const DownArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  if (a.bf16 && use_stream_kernels(a.T, a.ident)) return launch_down_stream(a, s);
+  if (a.bf16 && use_stream_kernels(a.T, a.rows, a.E, a.ident)) return launch_down_stream(a, s);
   if (a.bf16) {
     const hipError_t e = a.y_bf16 ? launch_down_tiled<bf16>(a, s) : launch_down_tiled<float>(a, s);
     if (e != hipSuccess) return e;

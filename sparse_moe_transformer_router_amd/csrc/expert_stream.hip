@@ -327,7 +327,13 @@ void launch_dn_t(const DownArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool use_stream_kernels(int T, bool ident) { return T <= 64; }
+// Weight streaming pays while every expert's row group is a few 16-row
+// tiles: at most 64 tokens and, for the expert groups, at most 16 rows per
+// expert on average (the top-K layout of 64 tokens has 4; the all-experts
+// layout has T, and takes the tiled GEMMs).
+bool use_stream_kernels(int T, int rows, int E, bool ident) {
+  return T <= 64 && (ident || rows <= 16 * E);
+}
 
 // The dense branch (ident) at <= 64 tokens takes 32-row tiles (its weights
 // are streamed once per tile, the second time mostly from L2); its down

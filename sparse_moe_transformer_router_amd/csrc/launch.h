@@ -45,6 +45,11 @@ struct DispatchArgs {
 };
 int dispatch_num_blocks(int S);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// All-experts slot layout: offsets[e] = e * T, sorted_slots[e * T + t] =
+// t * E + e, w_dense[t * E + e] = the token's weight for e or 0.
+hipError_t launch_dense_mask(int T, int E, int K, const int32_t* topk_idx, const float* topk_w,
+                             int32_t* offsets, int32_t* sorted_slots, float* w_dense,
+                             hipStream_t s);
 
 // Grouped gated-MLP over row groups.  Group e owns rows [offsets[e],
 // offsets[e+1]) of the sorted order; row r reads input row
@@ -94,7 +99,7 @@ struct DownArgs {
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
 // Decode-sized variants (few rows per group): weight-streaming kernels.
-bool use_stream_kernels(int T, bool ident);
+bool use_stream_kernels(int T, int rows, int E, bool ident);
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s);
 

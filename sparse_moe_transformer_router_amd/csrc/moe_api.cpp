@@ -36,14 +36,17 @@ size_t dtype_size(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_dims(const moe_dims* d) {
+// any_k: calls that only see token-slots (experts, combine) take any top_k up
+// to num_experts, e.g. every expert per token; routing needs top_k <= 32.
+int check_dims(const moe_dims* d, bool any_k = false) {
   if (!d) return fail(MOE_ERR_ARG, "dims is NULL");
   if (d->hidden < 64 || d->hidden > 8192 || d->hidden % 64)
     return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: need a multiple of 64 in [64, 8192]", d->hidden);
   if (d->num_experts < 1 || d->num_experts > 256)
     return fail(MOE_ERR_UNSUPPORTED, "num_experts=%d: need 1..256", d->num_experts);
-  if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > 32)
-    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d: need 1..min(num_experts, 32)", d->top_k);
+  if (d->top_k < 1 || d->top_k > d->num_experts || (!any_k && d->top_k > 32))
+    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d: need 1..min(num_experts, %d)", d->top_k,
+                any_k ? d->num_experts : 32);
   if (d->expert_inter < 32 || d->expert_inter > 8192 || d->expert_inter % 32)
     return fail(MOE_ERR_UNSUPPORTED, "expert_inter=%d: need a multiple of 32 in [32, 8192]",
                 d->expert_inter);
@@ -280,7 +283,7 @@ int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend,
 extern "C" {
 
 size_t moe_workspace_size(const moe_dims* dims, int32_t max_tokens) {
-  if (check_dims(dims) != MOE_OK) return 0;
+  if (check_dims(dims, true) != MOE_OK) return 0;
   if (check_tokens(dims, max_tokens) != MOE_OK) return 0;
   return layout(dims, max_tokens).total;
 }
@@ -337,12 +340,30 @@ int moe_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
                       static_cast<hipStream_t>(stream));
 }
 
+int moe_dense_mask_dispatch(const moe_dims* dims, int32_t T, const int32_t* topk_idx,
+                            const float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                            float* w_dense, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if ((long long)T * dims->num_experts > (1 << 20))
+    return fail(MOE_ERR_UNSUPPORTED, "T*num_experts=%lld exceeds 2^20",
+                (long long)T * dims->num_experts);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(topk_idx); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(w_dense);
+  hipError_t e = moe::launch_dense_mask(T, dims->num_experts, dims->top_k, topk_idx, topk_w,
+                                        expert_offsets, sorted_slots, w_dense,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dense_mask_dispatch");
+}
+
 int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,
                    const void* w_down, const float* topk_w, const int32_t* expert_offsets,
                    const int32_t* sorted_slots, void* y_slots, void* ws, size_t ws_bytes,
                    void* stream) {
   int rc;
-  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
   g_err.clear();
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(topk_w);
@@ -370,7 +391,7 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x, const in
                         const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
                         void* ws, size_t ws_bytes, void* stream) {
   int rc;
-  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
   g_err.clear();
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "int8 experts take bf16 activations");
@@ -389,7 +410,7 @@ int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const voi
                        const int32_t* expert_offsets, const int32_t* sorted_slots, void* h,
                        void* stream) {
   int rc;
-  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
   g_err.clear();
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(expert_offsets);
@@ -402,7 +423,7 @@ int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* 
                     const float* topk_w, const int32_t* expert_offsets,
                     const int32_t* sorted_slots, void* y_slots, void* stream) {
   int rc;
-  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
   g_err.clear();
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(h); REQUIRE_PTR(w_down); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
@@ -414,7 +435,7 @@ int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* 
 int moe_combine(const moe_dims* dims, int32_t T, const void* y_slots, const void* addend,
                 void* out, void* stream) {
   int rc;
-  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
   g_err.clear();
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(y_slots); OPTIONAL_PTR(addend); REQUIRE_PTR(out);

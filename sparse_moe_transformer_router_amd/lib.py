@@ -56,6 +56,7 @@ def _load():
     L.moe_route.argtypes = [D, I32] + [P] * 11 + [SZ, P]
     L.moe_dispatch.argtypes = [D, I32] + [P] * 5 + [SZ, P]
     L.moe_expert_ffn.argtypes = [D, I32] + [P] * 8 + [SZ, P]
+    L.moe_dense_mask_dispatch.argtypes = [D, I32] + [P] * 6
     L.moe_expert_gate_up.argtypes = [D, I32] + [P] * 6
     L.moe_expert_down.argtypes = [D, I32] + [P] * 7
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
@@ -66,7 +67,7 @@ def _load():
         [SZ, P]
     for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
-              "moe_quantize_int8", "moe_expert_ffn_int8"):
+              "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -141,6 +142,12 @@ def moe_dispatch(d, T, topk_idx, counts, offsets, sorted_slots, ws, stream=None)
     _check(_lib.moe_dispatch(ctypes.byref(d), T, _ptr(topk_idx), _ptr(counts), _ptr(offsets),
                              _ptr(sorted_slots), _ptr(ws), ws.numel() if ws is not None else 0,
                              _stream(stream)))
+
+
+def moe_dense_mask_dispatch(d, T, topk_idx, topk_w, offsets, sorted_slots, w_dense, stream=None):
+    _check(_lib.moe_dense_mask_dispatch(ctypes.byref(d), T, _ptr(topk_idx), _ptr(topk_w),
+                                        _ptr(offsets), _ptr(sorted_slots), _ptr(w_dense),
+                                        _stream(stream)))
 
 
 def moe_expert_ffn(d, T, x, w_gate_up, w_down, topk_w, offsets, sorted_slots, y_slots, ws,

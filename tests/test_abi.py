@@ -154,3 +154,24 @@ def test_int8_entry_points_validate_on_the_host():
     bad[2] = None  # gate_up scales
     assert f(ctypes.byref(d), 4, *bad, 1 << 40, None) == lib_mod.MOE_ERR_ARG
     assert f(ctypes.byref(d), 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
+
+
+def test_dense_mask_entry_point_and_any_top_k_on_slot_calls():
+    """The all-experts layout call validates on the host; the calls that only
+    see token-slots take top_k up to num_experts, routing keeps top_k <= 32."""
+    f = L.moe_dense_mask_dispatch
+    d = D()
+    dp = ctypes.byref(d)
+    assert f(dp, 0, None, None, None, None, None, None) == lib_mod.MOE_OK
+    assert f(dp, 4, FAKE, None, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert f(dp, 4, FAKE, FAKE, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert f(dp, 8193, FAKE, FAKE, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert "2^20" in lib_mod.last_error()
+    dall = D(top_k=128)
+    pa = ctypes.byref(dall)
+    assert L.moe_workspace_size(pa, 64) > L.moe_workspace_size(dp, 64)
+    assert L.moe_combine(pa, 4, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert L.moe_expert_ffn(pa, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                            None) == lib_mod.MOE_ERR_WORKSPACE
+    assert router(dall, 4) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size(ctypes.byref(D(top_k=129)), 64) == 0

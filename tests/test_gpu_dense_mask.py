@@ -1,0 +1,140 @@
+"""GPU parity of the all-experts form of the experts (the page "Porting a
+128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section "The traceable
+trick: compute all experts, mask to top-8"): every expert runs on every token
+and its output is weighted by the token's routing weight for it, 0 outside the
+top-K, so the sum over experts is the sparse top-K result.
+
+- the slot layout is exact against its definition, on synthetic routings;
+- the all-experts output is within the path's tolerance of the oracle's
+  sparse loop (the identity the page states), at 26B shapes for a decode and
+  a prefill batch and on the fp32 path;
+- as a cross-check of the sparse path: every unselected slot is exactly zero,
+  and where both layouts take the same kernels (16 tokens: the weight-streaming
+  kernels; 256: the tiled GEMMs) the per-slot outputs of the selected experts
+  equal the sparse path's bit for bit, since each output element is one dot
+  product accumulated in the same order whatever rows share its tile.  At 64
+  tokens the sparse layout (4 rows per expert) streams and the all-experts
+  layout (64 rows per expert) takes the tiled GEMMs, so there the slots agree
+  to the bf16 tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_moe_transformer_router_amd import synth
+from tests.gpu_util import BF16_TOL, F32_TOL, dev_f32, dev_tensor, host, note, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_moe_transformer_router_amd import lib
+else:
+    lib = None
+
+
+def _layout_ref(idx, w, E):
+    """The layout from its definition, written out with loops."""
+    T, K = idx.shape
+    offsets = np.arange(E + 1, dtype=np.int64) * T
+    sorted_slots = np.empty(T * E, np.int64)
+    w_dense = np.zeros(T * E, np.float32)
+    for e in range(E):
+        for t in range(T):
+            sorted_slots[e * T + t] = t * E + e
+    for t in range(T):
+        for k in range(K):
+            w_dense[t * E + idx[t, k]] = w[t, k]
+    return offsets, sorted_slots, w_dense
+
+
+def _random_routing(seed, T, E, K):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    return idx, w
+
+
+def _gpu_layout(d, T, idx, w):
+    E = d.num_experts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * E, dtype=torch.int32, device="cuda")
+    wd = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    lib.moe_dense_mask_dispatch(d, T, torch.from_numpy(idx).cuda(), dev_f32(w), offsets, ss, wd)
+    return offsets, ss, wd
+
+
+@pytest.mark.parametrize("T,E,K", [(37, 16, 3), (1, 8, 8), (4096, 128, 8)])
+def test_dense_mask_layout_exact(T, E, K):
+    idx, w = _random_routing(T + E, T, E, K)
+    d = lib.dims(64, E, K, 32, 0, 1e-6, lib.MOE_BF16, lib.MOE_F32)
+    note(f"dense-mask layout T={T} E={E} K={K}")
+    offsets, ss, wd = _gpu_layout(d, T, idx, w)
+    torch.cuda.synchronize()
+    ro, rs, rw = _layout_ref(idx, w, E)
+    assert np.array_equal(host(offsets), ro)
+    assert np.array_equal(host(ss), rs)
+    assert np.array_equal(host(wd).view(np.uint32), rw.view(np.uint32))
+
+
+def _run(c, T, x, idx, w, dense: bool, bf16: bool):
+    """Experts (sparse top-K or all-experts) then combine; returns (y, out)."""
+    dt = lib.MOE_BF16 if bf16 else lib.MOE_F32
+    d = lib.dims(c.H, c.E, c.K, c.I, 0, c.eps, dt, lib.MOE_F32)
+    xg = dev_tensor(x, bf16)
+    gu, dn = dev_tensor(c.gate_up, bf16), dev_tensor(c.down, bf16)
+    idx_g = torch.from_numpy(idx).cuda()
+    if dense:
+        offsets, ss, wd = _gpu_layout(d, T, idx, w)
+        dd = lib.dims(c.H, c.E, c.E, c.I, 0, c.eps, dt, lib.MOE_F32)
+        slots = c.E
+    else:
+        ws0 = lib.workspace(d, T)
+        counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(c.E + 1, dtype=torch.int32, device="cuda")
+        ss = torch.empty(T * c.K, dtype=torch.int32, device="cuda")
+        lib.moe_dispatch(d, T, idx_g, counts, offsets, ss, ws0)
+        wd, dd, slots = dev_f32(w), d, c.K
+    ws = lib.workspace(dd, T)
+    y = torch.empty(T, slots, c.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, c.H, dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    lib.moe_expert_ffn(dd, T, xg, gu, dn, wd, offsets, ss, y, ws)
+    lib.moe_combine(dd, T, y, None, out)
+    torch.cuda.synchronize()
+    return host(y), host(out)
+
+
+def _sub(t: synth.Tensor, T: int) -> synth.Tensor:
+    return synth.Tensor(t.f32[:T], None if t.bf16 is None else t.bf16[:T])
+
+
+@pytest.mark.parametrize("T,same_kernels", [(16, True), (64, False), (256, True)])
+def test_dense_mask_26b_matches_oracle_and_sparse_path(T, same_kernels):
+    c = synth.moe_case(T, seed=5)
+    x = _sub(c.x, T)
+    idx, w = oracle.router(x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note(f"dense-mask experts 26B T={T}")
+    yd, outd = _run(c, T, x, idx, w, dense=True, bf16=True)
+    ref = oracle.experts(x.f32, c.gate_up.f32, c.down.f32, idx, w)
+    assert rel_max_err(outd, ref) <= BF16_TOL
+    note(f"sparse experts 26B T={T}")
+    ys, outs = _run(c, T, x, idx, w, dense=False, bf16=True)
+    assert rel_max_err(outs, ref) <= BF16_TOL
+    sel = np.zeros((T, c.E), bool)
+    for k in range(c.K):
+        sel[np.arange(T), idx[:, k]] = True
+        got = yd[np.arange(T), idx[:, k]]
+        if same_kernels:
+            assert np.array_equal(got.view(np.uint32), ys[:, k].view(np.uint32)), k
+        else:
+            assert rel_max_err(got, ys[:, k]) <= BF16_TOL, k
+    assert np.all(yd[~sel] == 0.0)
+
+
+def test_dense_mask_f32_tiny():
+    c = synth.tiny_case(seed=4, T=24)
+    idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note("dense-mask experts fp32 tiny")
+    _, out = _run(c, c.T, c.x, idx, w, dense=True, bf16=False)
+    ref = oracle.experts(c.x.f32, c.gate_up.f32, c.down.f32, idx, w)
+    assert rel_max_err(out, ref) <= F32_TOL
