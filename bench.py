@@ -188,11 +188,10 @@ def decode_measure(torch, wl, T, steps, warmup, xbatches, seed):
     }, runner, xs
 
 
-def prefill_measure(torch, wl, T, steps, warmup, seed):
-    """The prefill batch with imbalanced expert load: a per-expert logit bias
-    b_e ~ N(0, 1), realised through the data as channel 0 of every token set
-    to 1 and router weight column 0 set to b."""
-    runner = Runner(wl, T)
+def skewed_inputs(torch, wl, T, seed):
+    """Two input batches and the weight copies with the per-expert logit bias
+    b_e ~ N(0, 1) realised through the data (channel 0 of every token = 1,
+    router weight column 0 = b)."""
     xs = wl.batches(T, 2, seed + 1)
     g = torch.Generator(device="cuda")
     g.manual_seed(1_000_099 * seed + 3)
@@ -204,6 +203,15 @@ def prefill_measure(torch, wl, T, steps, warmup, seed):
         rwb = rw.clone()
         rwb[:, 0] = bias
         copies.append((rwb, rs, pes, gu, dn))
+    return xs, copies
+
+
+def prefill_measure(torch, wl, T, steps, warmup, seed):
+    """The prefill batch with imbalanced expert load: a per-expert logit bias
+    b_e ~ N(0, 1), realised through the data as channel 0 of every token set
+    to 1 and router weight column 0 set to b."""
+    runner = Runner(wl, T)
+    xs, copies = skewed_inputs(torch, wl, T, seed)
     ms, seg, _ = time_steps(torch, runner, xs, copies, steps, warmup)
     runner.step(xs[0], copies[0])
     torch.cuda.synchronize()
@@ -495,6 +503,96 @@ def tiny_measure(torch, lib, steps, warmup):
             "dtype": "f32", "timing": "host clock around the launches (launch-bound)"}
 
 
+def achievable(torch):
+    """Measured ceilings of this GPU (libmoe_probe): a 4 GiB streaming read and
+    a register-only bf16 MFMA loop (32x32x16, 8 independent accumulators per
+    wave, 1024 blocks of 4 waves)."""
+    from sparse_moe_transformer_router_amd import probe
+
+    buf = torch.ones(1 << 30, dtype=torch.int32, device="cuda")
+    bx = torch.empty(probe.read_blocks(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        probe.stream_read(buf, bx)
+    n = 10
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        probe.stream_read(buf, bx)
+    b.record()
+    torch.cuda.synchronize()
+    read_gbs = n * buf.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        probe.mfma(blocks, iters, out)
+    a.record()
+    for _ in range(5):
+        probe.mfma(blocks, iters, out)
+    b.record()
+    torch.cuda.synchronize()
+    mfma_tflops = 5 * probe.mfma_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12
+    assert bool((out == 16.0 * iters).all()), "MFMA probe result wrong"
+    return {"hbm_read_gbs": read_gbs, "mfma_bf16_tflops": mfma_tflops,
+            "probe": "libmoe_probe: 4 GiB streaming read (16-B loads); register-only "
+                     "v_mfma_f32_32x32x16_bf16 loop"}
+
+
+class SmiSampler:
+    """GPU clock and socket power sampled with amd-smi (a child process) in a
+    background thread while the GPU legs run."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _once(self):
+        import subprocess
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        gfx = [v["clk"]["value"] for k, v in d["clock"].items()
+               if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        return sum(gfx) / len(gfx), d["power"]["socket_power"]["value"]
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._once())
+            except Exception as e:  # amd-smi missing or its output changed
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(0.2)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=30)
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        clk = [c for c, _ in self.samples]
+        pw = [p for _, p in self.samples]
+        return {"samples": len(self.samples), "tool": "amd-smi metric -p -c",
+                "raw_mhz_w": [[round(c, 1), p] for c, p in self.samples],
+                "gfx_clk_mhz": {"mean": sum(clk) / len(clk), "min": min(clk), "max": max(clk)},
+                "socket_power_w": {"mean": sum(pw) / len(pw), "min": min(pw), "max": max(pw)}}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, wl, xs, T, seconds):
     """The oracle as it stands, on the host cores: router + sparse experts for
     the first decode batch, repeated for about `seconds`."""
@@ -520,13 +618,50 @@ def cpu_baseline(torch, wl, xs, T, seconds):
                       f"weight copy 0, repeated {n // T}x over {el:.1f} s"}
 
 
-def cpu_oracle_configs(torch, layer, seconds):
-    """Oracle rates on the other configurations (bounded samples): the tiny fp32
-    experts-only case and the whole block on 16 tokens of the 2048-token input."""
+def _oracle_experts_rate(x, args, gu32, dn32, seconds):
+    import oracle
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        idx, w = oracle.router(x, *args, K)
+        oracle.experts(x, gu32, dn32, idx, w)
+        n += x.shape[0]
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n / el, n // x.shape[0], el
+
+
+def cpu_oracle_configs(torch, wl, xs, T, layer, prefill_T, seed, seconds):
+    """Oracle rates on the other configurations (bounded samples): the decode
+    batch on one thread, 64 tokens of the skewed prefill batch, the tiny fp32
+    experts-only case and the whole block on 16 tokens."""
     import oracle
     from sparse_moe_transformer_router_amd import synth
 
-    res = {"cores": oracle.num_threads(), "kind": "oracle"}
+    res = {"cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model()}
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    rw, rs, pes, gu, dn = wl.copies[0]
+    gu32, dn32 = f(gu), f(dn)
+    cores = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        v, calls, el = _oracle_experts_rate(f(xs[0]), (f(rw), f(rs), f(pes)), gu32, dn32,
+                                            seconds / 4)
+    finally:
+        oracle.set_num_threads(cores)
+    res["decode_single_thread"] = {"tokens_per_s": v, "threads": 1,
+                                   "sample": f"router + sparse experts on the {T}-token decode "
+                                             f"batch, {calls} calls over {el:.1f} s"}
+    if prefill_T:
+        pxs, pcopies = skewed_inputs(torch, wl, prefill_T, seed)
+        prw, prs, ppes, _, _ = pcopies[0]
+        v, calls, el = _oracle_experts_rate(f(pxs[0][:64]), (f(prw), f(prs), f(ppes)), gu32,
+                                            dn32, seconds / 4)
+        res["prefill_sample"] = {"tokens_per_s": v,
+                                 "sample": f"router + sparse experts on the first 64 tokens of "
+                                           f"the skewed {prefill_T}-token batch, {calls} calls "
+                                           f"over {el:.1f} s"}
+    del gu32, dn32
     c = synth.tiny_case(seed=0)
     n, t0 = 0, time.perf_counter()
     while True:
@@ -549,7 +684,7 @@ def cpu_oracle_configs(torch, layer, seconds):
             oracle.block(x, *args, 0.06, K)
             n += x.shape[0]
             el = time.perf_counter() - t0
-            if el >= seconds * 3 / 4:
+            if el >= seconds / 4:
                 break
         res["block"] = {"tokens_per_s": n / el,
                         "sample": f"whole block on 16 tokens, {n // 16} calls over {el:.1f} s"}
@@ -592,6 +727,10 @@ def main():
 
     def done(leg):
         print(f"bench: {leg} done", file=sys.stderr, flush=True)
+
+    smi = SmiSampler().start()
+    ach = achievable(torch)
+    done("achievable read / MFMA rates")
 
     head, runner, xs = decode_measure(torch, wl, args.batch, args.steps, args.warmup,
                                       args.xbatches, args.seed)
@@ -641,12 +780,21 @@ def main():
                               args.stack_prefill, args.seed)
         done(f"stack of {args.stack} layers")
 
+    clocks = smi.stop()
+    for r in [head, *sweep.values()]:
+        r["gate_up_frac_of_achievable_read"] = r["gate_up_gbs"] / ach["hbm_read_gbs"]
+    if prefill is not None:
+        prefill["grouped_gemm_frac_of_achievable_mfma"] = (prefill["grouped_gemm_tflops"] /
+                                                           ach["mfma_bf16_tflops"])
+    int8["experts_frac_of_achievable_read"] = int8["experts_gbs"] / ach["hbm_read_gbs"]
+
     cpu = None
     cpu_configs = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, wl, xs, args.batch, args.cpu_seconds)
-        cpu_configs = cpu_oracle_configs(torch, layers[0] if layers else None,
-                                         args.cpu_seconds / 2)
+        cpu_configs = cpu_oracle_configs(torch, wl, xs, args.batch,
+                                         layers[0] if layers else None, args.prefill, args.seed,
+                                         args.cpu_seconds)
         done("cpu baselines")
 
     achieved = head["gate_up_gbs"]
@@ -670,9 +818,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gate_up_stream_kernel (expert gate_up + GELU, decode)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(),
+                     "frac_of_achievable": achieved / ach["hbm_read_gbs"],
                      "algorithmic_bytes_per_launch": head["gate_up_bytes"],
                      "avg_launch_ms": head["kernel_ms"]["gate_up"]},
         "cpu_baseline": cpu,
+        "achievable": ach,
+        "gpu_clock_power": clocks,
         "decode": {str(args.batch): head, **sweep},
         "prefill": prefill,
         "dense_masked_ablation": dense_mask or None,

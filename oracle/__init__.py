@@ -67,6 +67,8 @@ def lib():
         L.oracle_dequantize_rows.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _I
+        L.oracle_set_num_threads.argtypes = [_I]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -89,6 +91,11 @@ def _p(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only: results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def router(x, router_w, router_scale, per_expert_scale, K, eps=1e-6, pre_gain=None,

@@ -351,3 +351,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later calls use (timing only; results
+ * do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

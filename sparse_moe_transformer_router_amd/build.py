@@ -14,8 +14,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_stream.hip", "combine.hip", "quant.hip",
            "moe_api.cpp"]
+# Measurement probes (achievable read and MFMA rates), a library of their own.
+PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 vector instructions are disabled: plain fp32 code is compiled
@@ -40,16 +43,23 @@ def _compile(src: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libmoe.so and libmoe_probe.so; returns the path of libmoe.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -175,3 +175,28 @@ def test_dense_mask_entry_point_and_any_top_k_on_slot_calls():
                             None) == lib_mod.MOE_ERR_WORKSPACE
     assert router(dall, 4) == lib_mod.MOE_ERR_UNSUPPORTED
     assert L.moe_workspace_size(ctypes.byref(D(top_k=129)), 64) == 0
+
+
+def test_probe_library_exports_and_validates():
+    """The measurement probes: every symbol include/moe_probe.h declares is
+    exported, and bad arguments are refused before any launch."""
+    probe = pytest.importorskip("sparse_moe_transformer_router_amd.probe",
+                                reason="libmoe_probe.so not built")
+    header = os.path.join(ROOT, "include", "moe_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = set(re.findall(r"^\s*(?:long long|int)\s+(\w+)\s*\(", text, flags=re.M))
+    assert {"moe_probe_stream_read", "moe_probe_mfma", "moe_probe_read_blocks",
+            "moe_probe_mfma_flops"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert names <= exported
+    P = probe.raw()
+    assert P.moe_probe_read_blocks() > 0
+    assert P.moe_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 8 * 2 * 32 * 32 * 16
+    assert P.moe_probe_stream_read(None, 1024, FAKE, None) == -1
+    assert P.moe_probe_stream_read(FAKE, 1000, FAKE, None) == -1
+    assert P.moe_probe_stream_read(MISALIGNED, 1024, FAKE, None) == -1
+    assert P.moe_probe_mfma(0, 10, FAKE, None) == -1
+    assert P.moe_probe_mfma(4, 0, FAKE, None) == -1
+    assert P.moe_probe_mfma(4, 10, None, None) == -1
