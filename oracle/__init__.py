@@ -65,6 +65,14 @@ def lib():
         L.oracle_quantize_rows.restype = None
         L.oracle_dequantize_rows.argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
         L.oracle_dequantize_rows.restype = None
+        for name in ("oracle_quantize_fp8_rows", "oracle_dequantize_fp8_rows",
+                     "oracle_quantize_mxfp4_rows", "oracle_dequantize_mxfp4_rows"):
+            getattr(L, name).argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
+            getattr(L, name).restype = None
+        L.oracle_e4m3_value.argtypes = [_I]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [_I]
+        L.oracle_e2m1_value.restype = ctypes.c_double
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _I
         L.oracle_set_num_threads.argtypes = [_I]
@@ -211,3 +219,69 @@ def experts_int8(xin, gate_up_q, gate_up_s, down_q, down_s, idx, w):
     """The sparse expert loop (fp64) on the dequantized int8 weights."""
     return experts(xin, dequantize_int8(gate_up_q, gate_up_s), dequantize_int8(down_q, down_s),
                    idx, w)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an E4M3 code (OCP 8-bit floating point; NaN for S.1111.111)."""
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code."""
+    return lib().oracle_e2m1_value(int(code))
+
+
+def quantize_fp8(w):
+    """Per-row symmetric E4M3: returns (codes uint8 same shape, s fp32 [rows...])."""
+    w = _f32(w)
+    shape = w.shape
+    q = np.zeros(shape, np.uint8)
+    s = np.zeros(shape[:-1], np.float32)
+    lib().oracle_quantize_fp8_rows(int(np.prod(shape[:-1])), shape[-1], _p(w), _p(q), _p(s))
+    return q, s
+
+
+def dequantize_fp8(q, s):
+    """value(code) * s rounded once to fp32, shape of q."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = _f32(s)
+    out = np.zeros(q.shape, np.float32)
+    lib().oracle_dequantize_fp8_rows(int(np.prod(q.shape[:-1])), q.shape[-1], _p(q), _p(s),
+                                     _p(out))
+    return out
+
+
+def quantize_mxfp4(w):
+    """MXFP4 along the last axis (a multiple of 32): returns (codes uint8 [..., n/2],
+    two E2M1 codes per byte, the even column in the low nibble; E8M0 scale codes
+    uint8 [..., n/32])."""
+    w = _f32(w)
+    shape = w.shape
+    n = shape[-1]
+    assert n % 32 == 0
+    q = np.zeros(shape[:-1] + (n // 2,), np.uint8)
+    e8 = np.zeros(shape[:-1] + (n // 32,), np.uint8)
+    lib().oracle_quantize_mxfp4_rows(int(np.prod(shape[:-1])), n, _p(w), _p(q), _p(e8))
+    return q, e8
+
+
+def dequantize_mxfp4(q, e8):
+    """value(code) * 2^(e8 - 127), exact; shape [..., 2 * q.shape[-1]]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    e8 = np.ascontiguousarray(e8, dtype=np.uint8)
+    n = 2 * q.shape[-1]
+    out = np.zeros(q.shape[:-1] + (n,), np.float32)
+    lib().oracle_dequantize_mxfp4_rows(int(np.prod(q.shape[:-1])), n, _p(q), _p(e8), _p(out))
+    return out
+
+
+def experts_fp8(xin, gate_up_q, gate_up_s, down_q, down_s, idx, w):
+    """The sparse expert loop (fp64) on the dequantized E4M3 weights."""
+    return experts(xin, dequantize_fp8(gate_up_q, gate_up_s), dequantize_fp8(down_q, down_s),
+                   idx, w)
+
+
+def experts_mxfp4(xin, gate_up_q, gate_up_e8, down_q, down_e8, idx, w):
+    """The sparse expert loop (fp64) on the dequantized MXFP4 weights."""
+    return experts(xin, dequantize_mxfp4(gate_up_q, gate_up_e8),
+                   dequantize_mxfp4(down_q, down_e8), idx, w)

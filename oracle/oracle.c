@@ -343,6 +343,153 @@ void oracle_dequantize_rows(long long rows, int cols, const int8_t* q, const flo
       out[r * cols + c] = (float)((double)q[r * cols + c] * (double)s[r]);
 }
 
+/* -------------------------------------------------------------------------
+ * 8-bit and 4-bit floating-point expert weights, the low-precision options
+ * the page "Porting a 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2"
+ * weighs for the experts (section "The fp4 rabbit hole (two of them, both
+ * dead ends)": FP8, and the microscaling fp4 format of 32 E2M1 values per
+ * block).  The formats themselves are those of the published OCP standards:
+ *
+ * E4M3 (OCP 8-bit floating point): sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; there are
+ * no infinities, S.1111.111 is NaN, and the largest finite magnitude is
+ * 1.75 * 2^8 = 448.
+ *
+ * MXFP4 (OCP Microscaling, MX): blocks of 32 consecutive values share one
+ * E8M0 scale 2^(e - 127); the elements are E2M1 (sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The
+ * shared exponent is floor(log2(max |v|)) minus 2 (the largest E2M1
+ * exponent), and each element is v / 2^shared rounded to the nearest E2M1
+ * value, saturating at 6.
+ *
+ * Rounding here is done by enumeration: the nearest representable value
+ * wins, and a value exactly halfway between two takes the code whose lowest
+ * mantissa bit is 0 (round half to even).
+ * ------------------------------------------------------------------------- */
+
+/* Value of an E4M3 code (NaN for S.1111.111). */
+double oracle_e4m3_value(int code) {
+  const int sign = (code >> 7) & 1, ex = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (ex == 15 && m == 7) return NAN;
+  if (ex == 0) v = (double)m / 8.0 * ldexp(1.0, -6);
+  else v = (1.0 + (double)m / 8.0) * ldexp(1.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* Value of an E2M1 code (4 bits). */
+double oracle_e2m1_value(int code) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double v = mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* Nearest code among the non-negative codes 0..n-1 (values ascending, value
+ * of code c given by f), ties to the code with even lowest bit. */
+static int nearest_code(double a, int n, double (*f)(int)) {
+  int best = 0;
+  double bd = fabs(a - f(0));
+  for (int c = 1; c < n; ++c) {
+    const double d = fabs(a - f(c));
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+/* Per-row symmetric E4M3: s = max |w| / 448 (fp32 division), code = nearest
+ * E4M3 to w / s (fp32 division; 126 finite non-negative codes 0x00..0x7E,
+ * magnitudes past 448 take 448), sign bit = w < 0.  A row of zeros gets
+ * s = 0 and codes 0.  The dequantized weight is value(code) * s. */
+void oracle_quantize_fp8_rows(long long rows, int cols, const float* w, uint8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    const float* wr = w + r * cols;
+    float amax = 0.0f;
+    for (int c = 0; c < cols; ++c) {
+      const float a = fabsf(wr[c]);
+      if (a > amax) amax = a;
+    }
+    const float sc = amax / 448.0f;
+    s[r] = sc;
+    for (int c = 0; c < cols; ++c) {
+      int code = 0;
+      if (sc > 0.0f) {
+        const float v = wr[c] / sc;
+        code = nearest_code(fabs((double)v), 0x7F, oracle_e4m3_value);
+        if (wr[c] < 0.0f) code |= 0x80;
+      }
+      q[r * cols + c] = (uint8_t)code;
+    }
+  }
+}
+
+/* value(code) * s, rounded once to fp32. */
+void oracle_dequantize_fp8_rows(long long rows, int cols, const uint8_t* q, const float* s,
+                                float* out) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c)
+      out[r * cols + c] = (float)(oracle_e4m3_value(q[r * cols + c]) * (double)s[r]);
+}
+
+/* MXFP4 along each row (cols % 32 == 0): block b of row r holds columns
+ * 32b .. 32b + 31; e8[r * cols / 32 + b] is its E8M0 scale code, and column
+ * c's E2M1 code sits in byte r * cols / 2 + c / 2, low nibble for even c.
+ * shared = floor(log2(max |v|)) - 2, clamped to [-127, 127], e8 = shared +
+ * 127; a block of zeros gets e8 = 0 and codes 0.  Element code = nearest
+ * E2M1 to |v| / 2^shared (magnitudes past 6 take 6), sign bit = v < 0. */
+void oracle_quantize_mxfp4_rows(long long rows, int cols, const float* w, uint8_t* q,
+                                uint8_t* e8) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      const float* v = w + r * cols + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+      int shared = -127;
+      if (amax > 0.0) {
+        shared = (int)floor(log2(amax)) - 2;
+        /* log2 of an exact power of two must not be taken from a rounded log */
+        while (ldexp(1.0, shared + 2) > amax) --shared;
+        while (ldexp(1.0, shared + 3) <= amax) ++shared;
+        if (shared < -127) shared = -127;
+        if (shared > 127) shared = 127;
+      }
+      e8[r * nb + b] = (uint8_t)(amax > 0.0 ? shared + 127 : 0);
+      for (int i = 0; i < 32; ++i) {
+        int code = 0;
+        if (amax > 0.0) {
+          code = nearest_code(fabs((double)v[i]) / ldexp(1.0, shared), 8, oracle_e2m1_value);
+          if (v[i] < 0.0f) code |= 8;
+        }
+        const long long c = 32LL * b + i;
+        uint8_t* byte = q + r * (cols / 2) + c / 2;
+        if (c % 2 == 0) *byte = (uint8_t)code;
+        else *byte = (uint8_t)(*byte | (code << 4));
+      }
+    }
+  }
+}
+
+/* value(code) * 2^(e8 - 127), exact in fp32. */
+void oracle_dequantize_mxfp4_rows(long long rows, int cols, const uint8_t* q, const uint8_t* e8,
+                                  float* out) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) {
+      const uint8_t byte = q[r * (cols / 2) + c / 2];
+      const int code = (c % 2 == 0) ? (byte & 15) : (byte >> 4);
+      out[r * cols + c] =
+          (float)(oracle_e2m1_value(code) * ldexp(1.0, (int)e8[r * nb + c / 32] - 127));
+    }
+}
+
 /* Number of OpenMP threads the parallel loops use. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
