@@ -76,6 +76,20 @@ typedef enum moe_status {
   MOE_ERR_HIP = -4           /* a HIP launch reported an error */
 } moe_status;
 
+/* Storage formats of expert weights below bf16 (decode batches):
+ *   MOE_W_INT8   int8 codes, one fp32 scale per output channel;
+ *   MOE_W_FP8    E4M3 codes (OCP 8-bit floating point: bias 7, no
+ *                infinities, largest finite 448), one fp32 scale per output
+ *                channel;
+ *   MOE_W_MXFP4  E2M1 codes, two per byte with the even element in the low
+ *                nibble, and one E8M0 scale code per 32 consecutive weights of
+ *                a row (OCP Microscaling), value = code * 2^(scale - 127). */
+typedef enum moe_wformat {
+  MOE_W_INT8 = 1,
+  MOE_W_FP8 = 2,
+  MOE_W_MXFP4 = 3
+} moe_wformat;
+
 typedef enum moe_dtype {
   MOE_F32 = 0,   /* fp32 storage and fp32 arithmetic (debug path) */
   MOE_BF16 = 1   /* bf16 storage, fp32 accumulation (fast path) */
@@ -218,6 +232,51 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
                         const int8_t* w_down_q, const float* w_down_scale, const float* topk_w,
                         const int32_t* expert_offsets, const int32_t* sorted_slots,
                         void* y_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert weights below bf16: the int8 variant above and the 8-bit and 4-bit
+ * floating-point options of the same page (section "The fp4 rabbit hole (two
+ * of them, both dead ends)": FP8, and fp4 in a 32-element microscaling
+ * block), in the formats of moe_wformat.
+ *
+ * moe_quantize: w is rows x cols bf16, a row one output channel (for the
+ * experts: gate_up as E*2I rows of H, down as E*H rows of I).
+ *   MOE_W_INT8   q int8 [rows, cols], scale fp32 [rows]: as moe_quantize_int8.
+ *   MOE_W_FP8    q uint8 [rows, cols], scale fp32 [rows]: scale = max |w| /
+ *                448, code = E4M3 nearest to w / scale (fp32 divisions; ties
+ *                to the even mantissa; 448 at most), sign bit = w < 0; a zero
+ *                row gives scale 0 and codes 0.  cols % 8 == 0.
+ *   MOE_W_MXFP4  q uint8 [rows, cols / 2], scale uint8 [rows, cols / 32]: per
+ *                32-weight block, shared = floor(log2 max |w|) - 2 clamped to
+ *                [-127, 127], scale code = shared + 127, element = E2M1
+ *                nearest to |w| / 2^shared (ties to the even mantissa, 6 at
+ *                most) with sign bit w < 0; a zero block gives scale code 0
+ *                and codes 0.  cols % 32 == 0.
+ * Deterministic and exact (the same codes on any IEEE machine).
+ *
+ * moe_dequantize: codes (and scales) back to fp32 values, out [rows, cols];
+ * int8 / E4M3: value * scale rounded once; MXFP4: value * 2^(scale - 127),
+ * exact.  It widens codes exactly as moe_expert_ffn_q does.  cols % 16 == 0
+ * (MXFP4: % 32).
+ *
+ * moe_expert_ffn_q: moe_expert_ffn with the experts' weights in format fmt
+ * (gate_up codes of [E, 2I, H] weights and down codes of [E, H, I], scales
+ * as moe_quantize lays them out).  Codes widen to bf16 exactly in registers
+ * (MXFP4 with its block scale; block scales must exceed 2^-125 to stay in
+ * bf16's normal range), enter bf16 MFMAs, and int8 / E4M3 output channels
+ * are multiplied by their scale after the k-sum.  Decode batches only (T <=
+ * 64, act dtype bf16), else MOE_ERR_UNSUPPORTED.
+ *
+ * All three: device pointers, 16-byte aligned; MOE_ERR_ARG for an unknown
+ * format, bad sizes or pointers. */
+int moe_quantize(int32_t fmt, int64_t rows, int32_t cols, const void* w, void* q, void* scale,
+                 void* stream);
+int moe_dequantize(int32_t fmt, int64_t rows, int32_t cols, const void* q, const void* scale,
+                   float* out, void* stream);
+int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x,
+                     const void* w_gate_up_q, const void* w_gate_up_scale, const void* w_down_q,
+                     const void* w_down_scale, const float* topk_w,
+                     const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* The experts' scatter-add: out[t] = sum_{k=0..K-1} y_slots[t,k] (fp32, k
  * ascending, no atomics) + addend[t] (if addend is not NULL).

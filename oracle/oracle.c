@@ -362,9 +362,9 @@ void oracle_dequantize_rows(long long rows, int cols, const int8_t* q, const flo
  * exponent), and each element is v / 2^shared rounded to the nearest E2M1
  * value, saturating at 6.
  *
- * Rounding here is done by enumeration: the nearest representable value
- * wins, and a value exactly halfway between two takes the code whose lowest
- * mantissa bit is 0 (round half to even).
+ * Rounding here works on the table of representable values: the nearer of
+ * the two values around v wins, and a value exactly halfway between them
+ * takes the code whose lowest mantissa bit is 0 (round half to even).
  * ------------------------------------------------------------------------- */
 
 /* Value of an E4M3 code (NaN for S.1111.111). */
@@ -384,19 +384,22 @@ double oracle_e2m1_value(int code) {
   return (code & 8) ? -v : v;
 }
 
-/* Nearest code among the non-negative codes 0..n-1 (values ascending, value
- * of code c given by f), ties to the code with even lowest bit. */
+/* Nearest code among the non-negative codes 0..n-1, whose values f(c)
+ * ascend with c: the two codes around a (found by bisection) are compared,
+ * and a value exactly half-way takes the code with even lowest bit. */
 static int nearest_code(double a, int n, double (*f)(int)) {
-  int best = 0;
-  double bd = fabs(a - f(0));
-  for (int c = 1; c < n; ++c) {
-    const double d = fabs(a - f(c));
-    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
-      best = c;
-      bd = d;
-    }
+  if (a <= f(0)) return 0;
+  if (a >= f(n - 1)) return n - 1;
+  int lo = 0, hi = n - 1;  /* f(lo) < a < f(hi) or on one of them */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (f(mid) <= a) lo = mid;
+    else hi = mid;
   }
-  return best;
+  const double dl = a - f(lo), dh = f(hi) - a;
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (lo & 1) == 0 ? lo : hi;
 }
 
 /* Per-row symmetric E4M3: s = max |w| / 448 (fp32 division), code = nearest

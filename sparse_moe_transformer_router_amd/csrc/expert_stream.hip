@@ -27,16 +27,14 @@
 // register rings and non-temporal loads measured no better or worse.
 #include "common.h"
 #include "launch.h"
+#include "wformat.h"
 
 namespace moe {
 namespace {
 
 constexpr int kKB = 64;  // k per block
 
-union Frag {
-  uint4 u[2];
-  bf16x8 v[2];
-};
+typedef W16 Frag;  // 16 bf16 activations of one row
 
 __device__ __forceinline__ void ld_frag(Frag& f, const bf16* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -48,38 +46,6 @@ __device__ __forceinline__ void zero_frag(Frag& f) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) f.u[i] = make_uint4(0, 0, 0, 0);
 }
-
-// One lane's weights for one k-block, held raw in the register ring until
-// its MFMAs: 16 bf16 (32 B), or 16 int8 codes (16 B) that become bf16 at use
-// (exact: |q| <= 127 needs 7 significant bits).
-template <typename WQ> struct WRaw;
-template <> struct WRaw<bf16> {
-  Frag f;
-  __device__ __forceinline__ void load(const bf16* p) { ld_frag(f, p); }
-  __device__ __forceinline__ void zero() { zero_frag(f); }
-  __device__ __forceinline__ Frag frag() const { return f; }
-};
-template <> struct WRaw<int8_t> {
-  uint4 u;
-  __device__ __forceinline__ void load(const int8_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ Frag frag() const {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t word = w[m / 2];
-      const int b0 = 2 * (m % 2);  // bytes b0, b0 + 1 of word: elements 2m, 2m + 1
-      const float lo = (float)((int32_t)(word << (24 - 8 * b0)) >> 24);
-      const float hi = (float)((int32_t)(word << (16 - 8 * b0)) >> 24);
-      o[m] = (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
-    }
-    Frag f;
-    f.u[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    f.u[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    return f;
-  }
-};
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -102,9 +68,10 @@ template <typename WQ, int WK, int MB, int NS>
 __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     int H, int N, int E, int K, int rows, int ident, const bf16* __restrict__ x,
     const WQ* __restrict__ wg, const WQ* __restrict__ wu, long long w_stride,
-    const float* __restrict__ sg, const float* __restrict__ su, long long s_stride,
+    const void* __restrict__ sg, const void* __restrict__ su, long long s_stride,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     bf16* __restrict__ h) {
+  typedef WFmt<WQ> F;
   __shared__ f32x4 red[WK][MB][2][kWave];
   int e, row0, row1;
   if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
@@ -112,9 +79,16 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
   const int fr = lane % 16, fg = lane / 16;
   const int n = blockIdx.y * 16 + fr;
   const bool nvalid = n < N;
-  const size_t woff = (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * H + 16 * fg;
-  const WQ* gp = wg + woff;
-  const WQ* up = wu + woff;
+  const long long wel = (long long)e * w_stride + (long long)(nvalid ? n : 0) * H;
+  const WQ* gp = wrow(wg, wel);
+  const WQ* up = wrow(wu, wel);
+  const uint8_t* gsr = nullptr;
+  const uint8_t* usr = nullptr;
+  if constexpr (F::kBlockScale) {
+    const long long sel = (long long)e * s_stride + (long long)(nvalid ? n : 0) * (H / 32);
+    gsr = static_cast<const uint8_t*>(sg) + sel;
+    usr = static_cast<const uint8_t*>(su) + sel;
+  }
   const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
   const bf16* ap[MB];
   bool av[MB];
@@ -140,8 +114,8 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < H;
     if (nvalid && kv) {
-      g.load(gp + k);
-      u.load(up + k);
+      g.load(gp, k + 16 * fg, gsr);
+      u.load(up, k + 16 * fg, usr);
     } else {
       g.zero();
       u.zero();
@@ -161,7 +135,7 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
       if (kl < kb1) load(kl, bg[(s + NS - 1) % NS], bu[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
-      const Frag fgt = bg[s].frag(), fup = bu[s].frag();
+      const Frag fgt = bg[s].widen(), fup = bu[s].widen();
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -188,9 +162,11 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
       g += red[w][mb][0][lane];
       u += red[w][mb][1][lane];
     }
-    if (sg != nullptr && nvalid) {  // int8 codes: the channel scales
-      g *= sg[(size_t)e * s_stride + n];
-      u *= su[(size_t)e * s_stride + n];
+    if constexpr (F::kChannelScale) {
+      if (nvalid) {
+        g *= static_cast<const float*>(sg)[(size_t)e * s_stride + n];
+        u *= static_cast<const float*>(su)[(size_t)e * s_stride + n];
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -205,10 +181,11 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
 template <typename WQ, int WN, int WK, int MB, int NS, typename YT>
 __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
-    const WQ* __restrict__ wd, long long w_stride, const float* __restrict__ sd,
+    const WQ* __restrict__ wd, long long w_stride, const void* __restrict__ sd,
     long long s_stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
     YT* __restrict__ y) {
+  typedef WFmt<WQ> F;
   __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][kWave];
   int e, row0, row1;
   if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
@@ -217,7 +194,11 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   const int fr = lane % 16, fg = lane / 16;
   const int n = blockIdx.y * 16 * WN + 16 * wn + fr;
   const bool nvalid = n < H;
-  const WQ* bp = wd + (size_t)e * w_stride + (size_t)(nvalid ? n : 0) * N + 16 * fg;
+  const WQ* bp = wrow(wd, (long long)e * w_stride + (long long)(nvalid ? n : 0) * N);
+  const uint8_t* bsr = nullptr;
+  if constexpr (F::kBlockScale)
+    bsr = static_cast<const uint8_t*>(sd) + (long long)e * s_stride +
+          (long long)(nvalid ? n : 0) * (N / 32);
   const int nmb = (row1 - row0 + 15) / 16;
   const bf16* ap[MB];
   bool av[MB];
@@ -238,7 +219,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   auto load = [&](int kb, WRaw<WQ>& b, Frag (&a)[MB]) {
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < N;
-    if (nvalid && kv) b.load(bp + k);
+    if (nvalid && kv) b.load(bp, k + 16 * fg, bsr);
     else b.zero();
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -255,7 +236,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
       if (kl < kb1) load(kl, bb[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
-      const Frag fb = bb[s].frag();
+      const Frag fb = bb[s].widen();
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -275,11 +256,13 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       for (int w = 1; w < WK; ++w) acc[mb] += red[wn + w * WN][mb][lane];
     }
   }
-  const float chs = (sd != nullptr && nvalid) ? sd[(size_t)e * s_stride + n] : 1.0f;
+  float chs = 1.0f;
+  if constexpr (F::kChannelScale)
+    if (nvalid) chs = static_cast<const float*>(sd)[(size_t)e * s_stride + n];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (mb >= nmb) break;
-    if (sd != nullptr) acc[mb] *= chs;  // int8 codes: the channel scale
+    if constexpr (F::kChannelScale) acc[mb] *= chs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 16 * mb + 4 * fg + r;
@@ -304,7 +287,7 @@ void launch_gu(const GateUpArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gate_up_stream_kernel<WQ, WK, MB, NS>), grid, dim3(64 * WK), 0, s, a.H, a.N,
                      a.E, a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
                      static_cast<const WQ*>(a.w_gate), static_cast<const WQ*>(a.w_up), a.w_stride,
-                     a.w_int8 ? a.s_gate : nullptr, a.w_int8 ? a.s_up : nullptr, a.s_stride,
+                     a.s_gate, a.s_up, a.s_stride,
                      a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
 }
 
@@ -314,14 +297,19 @@ void launch_dn(const DownArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, YT>), grid, dim3(64 * WN * WK), 0, s,
                      a.H, a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
                      static_cast<const WQ*>(a.w_down), a.w_stride,
-                     a.w_int8 ? a.s_down : nullptr, a.s_stride, a.offsets, a.sorted_slots,
+                     a.s_down, a.s_stride, a.offsets, a.sorted_slots,
                      a.topk_w, static_cast<YT*>(a.y));
 }
 
 template <typename YT>
 void launch_dn_t(const DownArgs& a, hipStream_t s) {
-  if (a.w_int8) launch_dn<int8_t, 2, 2, 1, 2, YT>(a, s);
-  else if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, YT>(a, s);
+  switch (a.w_fmt) {
+    case WFormat::kInt8: launch_dn<int8_t, 2, 2, 1, 2, YT>(a, s); return;
+    case WFormat::kFP8: launch_dn<fp8e4m3, 2, 2, 1, 2, YT>(a, s); return;
+    case WFormat::kMXFP4: launch_dn<fp4x2, 2, 2, 1, 2, YT>(a, s); return;
+    case WFormat::kBF16: break;
+  }
+  if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, YT>(a, s);
   else launch_dn<bf16, 4, 1, 1, 2, YT>(a, s);
 }
 
@@ -340,14 +328,20 @@ bool use_stream_kernels(int T, int rows, int E, bool ident) {
 // projection splits the contraction over 4 waves to keep enough loads in
 // flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
-  if (a.w_int8) launch_gu<int8_t, 4, 1, 2>(a, s);
-  else if (a.ident) launch_gu<bf16, 8, 2, 2>(a, s);
-  else launch_gu<bf16, 8, 1, 3>(a, s);
+  switch (a.w_fmt) {
+    case WFormat::kInt8: launch_gu<int8_t, 4, 1, 2>(a, s); break;
+    case WFormat::kFP8: launch_gu<fp8e4m3, 4, 1, 2>(a, s); break;
+    case WFormat::kMXFP4: launch_gu<fp4x2, 4, 1, 2>(a, s); break;
+    case WFormat::kBF16:
+      if (a.ident) launch_gu<bf16, 8, 2, 2>(a, s);
+      else launch_gu<bf16, 8, 1, 3>(a, s);
+      break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s) {
-  if (a.ident && !a.w_int8) {
+  if (a.ident && a.w_fmt == WFormat::kBF16) {
     if (a.y_bf16) launch_dn<bf16, 2, 4, 2, 2, bf16>(a, s);
     else launch_dn<bf16, 2, 4, 2, 2, float>(a, s);
   } else if (a.y_bf16) {

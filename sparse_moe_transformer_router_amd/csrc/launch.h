@@ -51,6 +51,10 @@ hipError_t launch_dense_mask(int T, int E, int K, const int32_t* topk_idx, const
                              int32_t* offsets, int32_t* sorted_slots, float* w_dense,
                              hipStream_t s);
 
+// Storage format of the expert weights (decode sizes only below bf16): see
+// wformat.h.  The values equal the moe_wformat codes of include/moe.h.
+enum class WFormat : int { kBF16 = 0, kInt8 = 1, kFP8 = 2, kMXFP4 = 3 };
+
 // Grouped gated-MLP over row groups.  Group e owns rows [offsets[e],
 // offsets[e+1]) of the sorted order; row r reads input row
 // sorted_slots[r] / K (or r itself when ident).  w_gate / w_up point at the
@@ -67,11 +71,13 @@ struct GateUpArgs {
   const int32_t* offsets;      // [E+1] (unused when ident)
   const int32_t* sorted_slots; // [rows] (unused when ident)
   void* h;                     // [rows, N] act dtype, sorted order
-  // int8 weights (decode sizes only): w_gate / w_up hold int8 codes and each
-  // weight row n of group e is scaled by s_gate / s_up[e * s_stride + n].
-  bool w_int8;
-  const float* s_gate;
-  const float* s_up;
+  // Weights below bf16 (decode sizes only): w_gate / w_up hold codes; int8
+  // and E4M3 rows n of group e are scaled by the fp32 s_gate / s_up[e *
+  // s_stride + n]; MXFP4 rows carry E8M0 block scales at s_gate / s_up + e *
+  // s_stride + n * (H / 32).  w_stride counts weights (not stored units).
+  WFormat w_fmt;
+  const void* s_gate;
+  const void* s_up;
   long long s_stride;
 };
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s);
@@ -92,8 +98,8 @@ struct DownArgs {
   const int32_t* sorted_slots;
   const float* topk_w;         // [T*K] (unused when ident)
   void* y;                     // [T*K, H] slot-major (or [T,H] when ident)
-  bool w_int8;                 // int8 codes, row n of group e scaled by s_down[e * s_stride + n]
-  const float* s_down;
+  WFormat w_fmt;               // as GateUpArgs (block scales per N / 32 of a row)
+  const void* s_down;
   long long s_stride;
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
@@ -107,6 +113,15 @@ hipError_t launch_down_stream(const DownArgs& a, hipStream_t s);
 // (cols % 8 == 0): codes q [rows, cols], scales [rows].
 hipError_t launch_quantize_rows(long long rows, int cols, const void* w, int8_t* q, float* scale,
                                 hipStream_t s);
+// E4M3 per row: codes [rows, cols], fp32 scales [rows].
+hipError_t launch_quantize_fp8(long long rows, int cols, const void* w, uint8_t* q, float* scale,
+                               hipStream_t s);
+// MXFP4 along each row (cols % 32 == 0): codes [rows, cols / 2], E8M0 [rows, cols / 32].
+hipError_t launch_quantize_mxfp4(long long rows, int cols, const void* w, uint8_t* q,
+                                 uint8_t* scale, hipStream_t s);
+// Codes back to fp32 values (times their scales), with the experts' widening.
+hipError_t launch_dequantize(WFormat f, long long rows, int cols, const void* q,
+                             const void* scale, float* out, hipStream_t s);
 
 struct CombineArgs {
   int T, H, K;

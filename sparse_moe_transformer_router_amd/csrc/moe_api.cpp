@@ -243,29 +243,55 @@ int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_ga
   return run_down(d, T, h, w_down, topk_w, offsets, sorted, y, s);
 }
 
-int run_expert_ffn_int8(const moe_dims* d, int32_t T, const void* x, const int8_t* guq,
-                        const float* gus, const int8_t* dnq, const float* dns,
-                        const float* topk_w, const int32_t* offsets, const int32_t* sorted,
-                        void* y, void* ws, hipStream_t s) {
+// Experts on weights stored below bf16 (fmt: int8, E4M3 or MXFP4).  Codes
+// of gate_up are [E, 2I, H] and of down [E, H, I] (MXFP4: two per byte);
+// scales are fp32 [E, 2I] / [E, H] (int8, E4M3) or E8M0 [E, 2I, H/32] /
+// [E, H, I/32] (MXFP4).
+int run_expert_ffn_q(const moe_dims* d, moe::WFormat fmt, int32_t T, const void* x,
+                     const void* guq, const void* gus, const void* dnq, const void* dns,
+                     const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                     void* y, void* ws, hipStream_t s) {
   void* h = at<void>(ws, layout(d, T).h);
   const long long H = d->hidden, I = d->expert_inter;
+  const bool mx = fmt == moe::WFormat::kMXFP4;
+  const long long unit = mx ? 2 : 1;  // weights per stored byte
+  const unsigned char* gq = static_cast<const unsigned char*>(guq);
   moe::GateUpArgs g{};
   g.T = T; g.H = d->hidden; g.N = d->expert_inter; g.E = d->num_experts; g.K = d->top_k;
   g.rows = T * d->top_k; g.ident = false; g.bf16 = true;
-  g.x = x; g.w_gate = guq; g.w_up = guq + I * H; g.w_stride = 2 * I * H;
+  g.x = x; g.w_gate = gq; g.w_up = gq + I * H / unit; g.w_stride = 2 * I * H;
   g.offsets = offsets; g.sorted_slots = sorted; g.h = h;
-  g.w_int8 = true; g.s_gate = gus; g.s_up = gus + I; g.s_stride = 2 * I;
+  g.w_fmt = fmt;
+  if (mx) {
+    g.s_gate = gus;
+    g.s_up = static_cast<const unsigned char*>(gus) + I * (H / 32);
+    g.s_stride = 2 * I * (H / 32);
+  } else {
+    g.s_gate = gus;
+    g.s_up = static_cast<const float*>(gus) + I;
+    g.s_stride = 2 * I;
+  }
   hipError_t e = moe::launch_gate_up_stream(g, s);
-  if (e != hipSuccess) return hip_fail(e, "expert gate_up (int8)");
+  if (e != hipSuccess) return hip_fail(e, "expert gate_up (quantized weights)");
   moe::DownArgs dn{};
   dn.T = T; dn.H = d->hidden; dn.N = d->expert_inter; dn.E = d->num_experts; dn.K = d->top_k;
   dn.rows = T * d->top_k; dn.ident = false; dn.bf16 = true;
   dn.y_bf16 = d->slot_dtype == MOE_BF16;
   dn.h = h; dn.w_down = dnq; dn.w_stride = H * I;
   dn.offsets = offsets; dn.sorted_slots = sorted; dn.topk_w = topk_w; dn.y = y;
-  dn.w_int8 = true; dn.s_down = dns; dn.s_stride = H;
+  dn.w_fmt = fmt; dn.s_down = dns; dn.s_stride = mx ? H * (I / 32) : H;
   e = moe::launch_down_stream(dn, s);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down (int8)");
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down (quantized weights)");
+}
+
+// Format code of the ABI -> the kernels' format, or -1 if unknown.
+int wformat_of(int32_t fmt, moe::WFormat& f) {
+  switch (fmt) {
+    case MOE_W_INT8: f = moe::WFormat::kInt8; return 0;
+    case MOE_W_FP8: f = moe::WFormat::kFP8; return 0;
+    case MOE_W_MXFP4: f = moe::WFormat::kMXFP4; return 0;
+    default: return fail(MOE_ERR_ARG, "weight format %d unknown", fmt);
+  }
 }
 
 int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend, void* out,
@@ -373,16 +399,78 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const void* x, const void* w
                         y_slots, ws, static_cast<hipStream_t>(stream));
 }
 
-int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
-                      void* stream) {
+int moe_quantize(int32_t fmt, int64_t rows, int32_t cols, const void* w, void* q, void* scale,
+                 void* stream) {
   g_err.clear();
+  moe::WFormat f;
+  if (wformat_of(fmt, f)) return MOE_ERR_ARG;
   if (rows < 0 || rows > (int64_t)1 << 36) return fail(MOE_ERR_ARG, "rows out of range");
-  if (cols <= 0 || cols % 8 != 0) return fail(MOE_ERR_ARG, "cols must be a positive multiple of 8");
+  const int align = f == moe::WFormat::kMXFP4 ? 32 : 8;
+  if (cols <= 0 || cols % align != 0)
+    return fail(MOE_ERR_ARG, "cols must be a positive multiple of %d", align);
   if (rows == 0) return MOE_OK;
   REQUIRE_PTR(w); REQUIRE_PTR(q); REQUIRE_PTR(scale);
-  hipError_t e = moe::launch_quantize_rows(rows, cols, w, q, scale,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_int8");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (f) {
+    case moe::WFormat::kInt8:
+      e = moe::launch_quantize_rows(rows, cols, w, static_cast<int8_t*>(q),
+                                    static_cast<float*>(scale), s);
+      break;
+    case moe::WFormat::kFP8:
+      e = moe::launch_quantize_fp8(rows, cols, w, static_cast<uint8_t*>(q),
+                                   static_cast<float*>(scale), s);
+      break;
+    default:
+      e = moe::launch_quantize_mxfp4(rows, cols, w, static_cast<uint8_t*>(q),
+                                     static_cast<uint8_t*>(scale), s);
+      break;
+  }
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize");
+}
+
+int moe_dequantize(int32_t fmt, int64_t rows, int32_t cols, const void* q, const void* scale,
+                   float* out, void* stream) {
+  g_err.clear();
+  moe::WFormat f;
+  if (wformat_of(fmt, f)) return MOE_ERR_ARG;
+  if (rows < 0 || rows > (int64_t)1 << 36) return fail(MOE_ERR_ARG, "rows out of range");
+  const int align = f == moe::WFormat::kMXFP4 ? 32 : 16;
+  if (cols <= 0 || cols % align != 0)
+    return fail(MOE_ERR_ARG, "cols must be a positive multiple of %d", align);
+  if (rows == 0) return MOE_OK;
+  REQUIRE_PTR(q); REQUIRE_PTR(scale); REQUIRE_PTR(out);
+  hipError_t e = moe::launch_dequantize(f, rows, cols, q, scale, out,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dequantize");
+}
+
+int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x,
+                     const void* w_gate_up_q, const void* w_gate_up_scale, const void* w_down_q,
+                     const void* w_down_scale, const float* topk_w,
+                     const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  moe::WFormat f;
+  if (wformat_of(fmt, f)) return MOE_ERR_ARG;
+  if (dims->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "quantized experts take bf16 activations");
+  if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "quantized experts: decode batches (T <= 64) only");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
+  REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  return run_expert_ffn_q(dims, f, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
+                          topk_w, expert_offsets, sorted_slots, y_slots, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
+                      void* stream) {
+  return moe_quantize(MOE_W_INT8, rows, cols, w, q, scale, stream);
 }
 
 int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x, const int8_t* w_gate_up_q,
@@ -390,20 +478,9 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x, const in
                         const float* w_down_scale, const float* topk_w,
                         const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
                         void* ws, size_t ws_bytes, void* stream) {
-  int rc;
-  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
-  g_err.clear();
-  if (dims->act_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "int8 experts take bf16 activations");
-  if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "int8 experts: decode batches (T <= 64) only");
-  if (T == 0) return MOE_OK;
-  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
-  REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
-  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
-  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
-  return run_expert_ffn_int8(dims, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
-                             topk_w, expert_offsets, sorted_slots, y_slots, ws,
-                             static_cast<hipStream_t>(stream));
+  return moe_expert_ffn_q(dims, MOE_W_INT8, T, x, w_gate_up_q, w_gate_up_scale, w_down_q,
+                          w_down_scale, topk_w, expert_offsets, sorted_slots, y_slots, ws,
+                          ws_bytes, stream);
 }
 
 int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const void* w_gate_up,

@@ -1,0 +1,172 @@
+// Storage formats of expert weights below bf16, and their exact widening to
+// bf16 for the matrix cores.  The page "Porting a 128-expert MoE (Gemma-4
+// 26B-A4B) to AWS Inferentia2" weighs int8 per-channel experts (section "Can
+// it run on a smaller box? Yes, no, and "deeper than it looks"") and the
+// 8-bit and 4-bit floating-point options (section "The fp4 rabbit hole (two
+// of them, both dead ends)").  The floating-point formats are those of the
+// OCP standards:
+//
+//   fp8e4m3  one E4M3 code per weight (sign, 4 exponent bits with bias 7, 3
+//            mantissa bits, no infinities, largest finite 448), with one fp32
+//            scale per output channel applied after the dot product;
+//   fp4x2    two E2M1 codes per byte (the even element in the low nibble), 32
+//            consecutive weights along the contraction sharing one E8M0
+//            scale 2^(e - 127) (MXFP4).
+//
+// Every code widens to bf16 exactly: int8 codes need 7 significant bits,
+// E4M3 values 4, and E2M1 values times a power of two 2 (while the product
+// stays in bf16's normal range, i.e. block scales above 2^-125).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct fp8e4m3 {
+  uint8_t b;
+};
+struct fp4x2 {
+  uint8_t b;
+};
+
+// Per-format layout facts.  kPerUnit: weights per stored unit; kChannelScale:
+// one fp32 scale per output channel (after the k-sum); kBlockScale: one E8M0
+// scale per 32 weights along the contraction (folded into the widening).
+template <typename WQ> struct WFmt {
+  static constexpr int kPerUnit = 1;
+  static constexpr bool kChannelScale = false, kBlockScale = false;
+};
+template <> struct WFmt<int8_t> {
+  static constexpr int kPerUnit = 1;
+  static constexpr bool kChannelScale = true, kBlockScale = false;
+};
+template <> struct WFmt<fp8e4m3> {
+  static constexpr int kPerUnit = 1;
+  static constexpr bool kChannelScale = true, kBlockScale = false;
+};
+template <> struct WFmt<fp4x2> {
+  static constexpr int kPerUnit = 2;
+  static constexpr bool kChannelScale = false, kBlockScale = true;
+};
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16x2_bits(bf16x2_v v) {
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// E8M0 scale code -> 2^(e - 127) in fp32 (code 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e != 0 ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+// Four int8 codes (one word, element 0 in the low byte) -> four bf16 in two
+// words (element 0 in the low half).
+__device__ __forceinline__ void int8x4_to_bf16(uint32_t word, uint32_t& lo, uint32_t& hi) {
+  uint32_t o[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int b0 = 2 * m;
+    const float a = (float)((int32_t)(word << (24 - 8 * b0)) >> 24);
+    const float b = (float)((int32_t)(word << (16 - 8 * b0)) >> 24);
+    o[m] = (__float_as_uint(b) & 0xffff0000u) | (__float_as_uint(a) >> 16);
+  }
+  lo = o[0];
+  hi = o[1];
+}
+
+// Four E4M3 codes (one word, element 0 in the low byte) -> four bf16.
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t word, uint32_t& lo, uint32_t& hi) {
+  lo = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+  hi = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+}
+
+// Eight E2M1 codes (one word, element 0 in the low nibble) times `scale` (a
+// power of two) -> eight bf16 in four words.
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t word, float scale, uint32_t (&o)[4]) {
+  o[0] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));
+  o[1] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1));
+  o[2] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2));
+  o[3] = bf16x2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3));
+}
+
+// 16 consecutive weights of one row as bf16 (two uint4: elements 0..7, 8..15).
+union W16 {
+  uint4 u[2];
+  bf16x8 v[2];
+};
+
+// One lane's 16 weights of one row, held raw (as stored) from their load to
+// their use.  load(row, k, srow): row points at the weight row's first unit,
+// k is the element index of the first of the 16 (a multiple of 16), srow the
+// row's block scales (fp4x2 only).
+template <typename WQ> struct WRaw;
+template <> struct WRaw<bf16> {
+  W16 f;
+  __device__ __forceinline__ void load(const bf16* row, int k, const uint8_t*) {
+    const uint4* q = reinterpret_cast<const uint4*>(row + k);
+    f.u[0] = q[0];
+    f.u[1] = q[1];
+  }
+  __device__ __forceinline__ void zero() { f.u[0] = f.u[1] = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ W16 widen() const { return f; }
+};
+template <> struct WRaw<int8_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const int8_t* row, int k, const uint8_t*) {
+    u = *reinterpret_cast<const uint4*>(row + k);
+  }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ W16 widen() const {
+    W16 f;
+    int8x4_to_bf16(u.x, f.u[0].x, f.u[0].y);
+    int8x4_to_bf16(u.y, f.u[0].z, f.u[0].w);
+    int8x4_to_bf16(u.z, f.u[1].x, f.u[1].y);
+    int8x4_to_bf16(u.w, f.u[1].z, f.u[1].w);
+    return f;
+  }
+};
+template <> struct WRaw<fp8e4m3> {
+  uint4 u;
+  __device__ __forceinline__ void load(const fp8e4m3* row, int k, const uint8_t*) {
+    u = *reinterpret_cast<const uint4*>(row + k);
+  }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ W16 widen() const {
+    W16 f;
+    fp8x4_to_bf16(u.x, f.u[0].x, f.u[0].y);
+    fp8x4_to_bf16(u.y, f.u[0].z, f.u[0].w);
+    fp8x4_to_bf16(u.z, f.u[1].x, f.u[1].y);
+    fp8x4_to_bf16(u.w, f.u[1].z, f.u[1].w);
+    return f;
+  }
+};
+template <> struct WRaw<fp4x2> {
+  uint2 u;
+  float scale;
+  __device__ __forceinline__ void load(const fp4x2* row, int k, const uint8_t* srow) {
+    u = *reinterpret_cast<const uint2*>(row + k / 2);
+    scale = e8m0_to_f32(srow[k / 32]);
+  }
+  __device__ __forceinline__ void zero() {
+    u = make_uint2(0, 0);
+    scale = 1.0f;
+  }
+  __device__ __forceinline__ W16 widen() const {
+    W16 f;
+    uint32_t o[4];
+    fp4x8_to_bf16(u.x, scale, o);
+    f.u[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    fp4x8_to_bf16(u.y, scale, o);
+    f.u[1] = make_uint4(o[0], o[1], o[2], o[3]);
+    return f;
+  }
+};
+
+// First stored unit of the weight row that starts at element `elem`.
+template <typename WQ>
+__device__ __forceinline__ const WQ* wrow(const WQ* base, long long elem) {
+  return base + elem / WFmt<WQ>::kPerUnit;
+}
+
+}  // namespace moe

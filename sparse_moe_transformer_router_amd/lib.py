@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_W_INT8, MOE_W_FP8, MOE_W_MXFP4 = 1, 2, 3
 
 
 class MoeDims(ctypes.Structure):
@@ -63,11 +64,15 @@ def _load():
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.moe_quantize_int8.argtypes = [ctypes.c_int64, I32, P, P, P, P]
     L.moe_expert_ffn_int8.argtypes = [D, I32] + [P] * 10 + [SZ, P]
+    L.moe_quantize.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P]
+    L.moe_dequantize.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P]
+    L.moe_expert_ffn_q.argtypes = [D, I32, I32] + [P] * 10 + [SZ, P]
     L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
         [SZ, P]
     for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
-              "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch"):
+              "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch",
+              "moe_quantize", "moe_dequantize", "moe_expert_ffn_q"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -172,6 +177,28 @@ def moe_expert_ffn_int8(d, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_
                                     _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots),
                                     _ptr(y_slots), _ptr(ws), ws.numel() if ws is not None else 0,
                                     _stream(stream)))
+
+
+def moe_quantize(fmt, w, q, scale, stream=None):
+    """Codes and scales of a bf16 weight whose last axis is the row (input)
+    dimension, in format fmt (MOE_W_INT8, MOE_W_FP8 or MOE_W_MXFP4)."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    _check(_lib.moe_quantize(fmt, rows, cols, _ptr(w), _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def moe_dequantize(fmt, rows, cols, q, scale, out, stream=None):
+    _check(_lib.moe_dequantize(fmt, rows, cols, _ptr(q), _ptr(scale), _ptr(out),
+                               _stream(stream)))
+
+
+def moe_expert_ffn_q(d, fmt, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale, topk_w,
+                     offsets, sorted_slots, y_slots, ws, stream=None):
+    _check(_lib.moe_expert_ffn_q(ctypes.byref(d), fmt, T, _ptr(x), _ptr(w_gate_up_q),
+                                 _ptr(w_gate_up_scale), _ptr(w_down_q), _ptr(w_down_scale),
+                                 _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots),
+                                 _ptr(y_slots), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)))
 
 
 def moe_expert_gate_up(d, T, x, w_gate_up, offsets, sorted_slots, h, stream=None):

@@ -200,3 +200,29 @@ def test_probe_library_exports_and_validates():
     assert P.moe_probe_mfma(0, 10, FAKE, None) == -1
     assert P.moe_probe_mfma(4, 0, FAKE, None) == -1
     assert P.moe_probe_mfma(4, 10, None, None) == -1
+
+
+def test_quantized_format_entry_points_validate_on_the_host():
+    """moe_quantize / moe_dequantize / moe_expert_ffn_q refuse unknown formats,
+    bad sizes and pointers before any launch."""
+    qz, dq, ffn = L.moe_quantize, L.moe_dequantize, L.moe_expert_ffn_q
+    W8, F8, MX = lib_mod.MOE_W_INT8, lib_mod.MOE_W_FP8, lib_mod.MOE_W_MXFP4
+    for f in (W8, F8, MX):
+        assert qz(f, 0, 64, None, None, None, None) == lib_mod.MOE_OK
+        assert dq(f, 0, 64, None, None, None, None) == lib_mod.MOE_OK
+    assert qz(7, 4, 64, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert "format" in lib_mod.last_error()
+    assert qz(F8, 4, 60, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert qz(MX, 4, 48, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert "32" in lib_mod.last_error()
+    assert qz(MX, 4, 64, FAKE, MISALIGNED, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert dq(F8, 4, 24, FAKE, FAKE, FAKE, None) == lib_mod.MOE_ERR_ARG
+    assert dq(MX, 4, 64, FAKE, None, FAKE, None) == lib_mod.MOE_ERR_ARG
+    d = D()
+    args = [FAKE] * 10
+    assert ffn(ctypes.byref(d), F8, 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
+    assert ffn(ctypes.byref(d), 0, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_ARG
+    assert ffn(ctypes.byref(d), MX, 65, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    d32 = D(act=lib_mod.MOE_F32)
+    assert ffn(ctypes.byref(d32), F8, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert ffn(ctypes.byref(d), MX, 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE

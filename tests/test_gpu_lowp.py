@@ -1,0 +1,190 @@
+"""GPU parity of the expert weights below bf16 (the 8-bit and 4-bit
+floating-point options of "Porting a 128-expert MoE (Gemma-4 26B-A4B) to AWS
+Inferentia2", section "The fp4 rabbit hole (two of them, both dead ends)", in
+the OCP E4M3 and MXFP4 formats), through the C ABI:
+
+- moe_dequantize, which widens codes with the same code as the expert
+  kernels, is bit-exact against the oracle on every code of each format (and
+  every int8 code), with several scales: this pins the hardware conversions
+  the kernels use to the formats' definitions;
+- moe_quantize gives the oracle's codes and scales bit for bit, on rows with
+  exact ties and saturation and on the 26B weights;
+- the experts on E4M3 and MXFP4 weights are within 2e-2 x RMS of the
+  oracle's sparse loop on the oracle's own dequantized weights, at 26B decode
+  shapes, and a small ragged layer within the bf16 path's rounding bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_moe_transformer_router_amd import synth
+from tests.gpu_util import BF16_TOL, bf16_path_bound, dev_f32, dev_tensor, host, note, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_moe_transformer_router_amd import lib
+else:
+    lib = None
+
+FMTS = {"fp8": 2, "mxfp4": 3}
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _gpu_dequant(fmt, q, s, rows, cols):
+    out = torch.empty(rows, cols, dtype=torch.float32, device="cuda")
+    lib.moe_dequantize(fmt, rows, cols, q, s, out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def _same_bits(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return np.array_equal(a.view(np.uint32)[~both_nan], b.view(np.uint32)[~both_nan]) and \
+        np.array_equal(np.isnan(a), np.isnan(b))
+
+
+def test_dequantize_every_fp8_code():
+    codes = np.tile(np.arange(256, dtype=np.uint8), (6, 1))
+    scales = np.array([1.0, 2.0 ** -3, 3.0, 0.1, 2.0 ** -20, 1e3], np.float32)
+    note("dequantize every E4M3 code")
+    got = _gpu_dequant(lib.MOE_W_FP8, _u8(codes), dev_f32(scales), 6, 256)
+    assert _same_bits(got, oracle.dequantize_fp8(codes, scales))
+
+
+def test_dequantize_every_int8_code():
+    codes = np.tile(np.arange(-128, 128, dtype=np.int8), (3, 1))
+    scales = np.array([1.0, 0.37, 2.0 ** -9], np.float32)
+    note("dequantize every int8 code")
+    got = _gpu_dequant(lib.MOE_W_INT8, torch.from_numpy(codes).cuda(), dev_f32(scales), 3, 256)
+    assert _same_bits(got, oracle.dequantize_int8(codes, scales))
+
+
+def test_dequantize_every_mxfp4_byte():
+    q = np.tile(np.arange(256, dtype=np.uint8), (4, 1))           # 512 weights per row
+    e8 = np.array([[127, 120, 130, 3, 200, 64, 127, 100, 140, 90, 127, 126, 128, 5, 250, 60]] * 4,
+                  np.uint8)
+    e8[1] = e8[1][::-1]
+    note("dequantize every MXFP4 byte")
+    got = _gpu_dequant(lib.MOE_W_MXFP4, _u8(q), _u8(e8), 4, 512)
+    assert _same_bits(got, oracle.dequantize_mxfp4(q, e8))
+
+
+def _bf16_tensor(a):
+    bits = synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+    return synth.Tensor(synth.bf16_bits_to_f32(bits), bits)
+
+
+def _gpu_quant(fmt, t: synth.Tensor):
+    rows, cols = int(np.prod(t.f32.shape[:-1])), t.f32.shape[-1]
+    q = torch.empty(rows * cols // (2 if fmt == lib.MOE_W_MXFP4 else 1), dtype=torch.uint8,
+                    device="cuda")
+    if fmt == lib.MOE_W_MXFP4:
+        s = torch.empty(rows * cols // 32, dtype=torch.uint8, device="cuda")
+    else:
+        s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    lib.moe_quantize(fmt, dev_tensor(t, True), q, s)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def test_quantize_hand_rows_bit_exact():
+    fp8_row = [448, 1.0625, 1.1875, 232, 240, 2.0 ** -10, 3 * 2.0 ** -10, 15 * 2.0 ** -10,
+               -0.5, 0, -448, 100] + [0] * 4
+    rows = np.array([fp8_row, [-x * 2.0 ** -7 for x in fp8_row], [0.0] * 16], np.float32)
+    t = _bf16_tensor(rows)
+    note("quantize E4M3 hand rows")
+    q, s = _gpu_quant(lib.MOE_W_FP8, t)
+    oq, os_ = oracle.quantize_fp8(t.f32)
+    assert np.array_equal(q.reshape(oq.shape), oq)
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    blk = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -7, 0.5, 1, 1.5, 2, 3, 4, -6] + [0] * 16
+    rows = np.array([blk + [0] * 32, [x * 2.0 ** -9 for x in blk] + [-1.0] + [0] * 31],
+                    np.float32)
+    t = _bf16_tensor(rows)
+    note("quantize MXFP4 hand rows")
+    q, s = _gpu_quant(lib.MOE_W_MXFP4, t)
+    oq, oe = oracle.quantize_mxfp4(t.f32)
+    assert np.array_equal(q.reshape(oq.shape), oq)
+    assert np.array_equal(s.reshape(oe.shape), oe)
+
+
+@pytest.fixture(scope="module")
+def case26b():
+    return synth.moe_case(64, seed=0)
+
+
+@pytest.fixture(scope="module")
+def oracle_q(case26b):
+    c = case26b
+    return {"fp8": (*oracle.quantize_fp8(c.gate_up.f32), *oracle.quantize_fp8(c.down.f32)),
+            "mxfp4": (*oracle.quantize_mxfp4(c.gate_up.f32),
+                      *oracle.quantize_mxfp4(c.down.f32))}
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+def test_quantize_26b_experts_bit_exact(case26b, oracle_q, name):
+    c = case26b
+    guq, gus, dnq, dns = oracle_q[name]
+    note(f"quantize 26B experts {name}")
+    q, s = _gpu_quant(FMTS[name], c.gate_up)
+    assert np.array_equal(q.reshape(guq.shape), guq)
+    assert np.array_equal(s.reshape(gus.shape).view(np.uint8), gus.view(np.uint8))
+    q, s = _gpu_quant(FMTS[name], c.down)
+    assert np.array_equal(q.reshape(dnq.shape), dnq)
+    assert np.array_equal(s.reshape(dns.shape).view(np.uint8), dns.view(np.uint8))
+
+
+def _q_path(c, fmt, T, x, idx, w, q):
+    d = lib.dims(c.H, c.E, c.K, c.I, 0, c.eps, lib.MOE_BF16, lib.MOE_F32)
+    ws = lib.workspace(d, T)
+    counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(c.E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * c.K, dtype=torch.int32, device="cuda")
+    lib.moe_dispatch(d, T, torch.from_numpy(idx).cuda(), counts, offsets, ss, ws)
+    y = torch.empty(T, c.K, c.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, c.H, dtype=torch.bfloat16, device="cuda")
+    dq = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in q]
+    lib.moe_expert_ffn_q(d, fmt, T, dev_tensor(x, True), *dq, dev_f32(w), offsets, ss, y, ws)
+    lib.moe_combine(d, T, y, None, out)
+    torch.cuda.synchronize()
+    return host(y), host(out)
+
+
+def _run_oracle(name, x, q, idx, w):
+    return (oracle.experts_fp8 if name == "fp8" else oracle.experts_mxfp4)(x, *q, idx, w)
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_experts_lowp_26b_decode(case26b, oracle_q, name, T):
+    c = case26b
+    x = synth.Tensor(c.x.f32[:T], c.x.bf16[:T])
+    idx, w = oracle.router(x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K)
+    q = oracle_q[name]
+    note(f"experts {name} 26B decode T={T}")
+    y, out = _q_path(c, FMTS[name], T, x, idx, w, q)
+    assert rel_max_err(out, _run_oracle(name, x.f32, q, idx, w)) <= BF16_TOL
+    assert rel_max_err(y[:, 0], _run_oracle(name, x.f32, q, idx[:, :1], w[:, :1])) <= BF16_TOL
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+def test_experts_lowp_small_ragged(name):
+    """A small layer with ragged row groups (some experts empty) and
+    unit-variance weights, held to the per-element bf16 rounding bound of the
+    path on the oracle's dequantized weights."""
+    c = synth.tiny_case(seed=10, T=37, H=128, E=16, K=3, I=64, bf16=True)
+    quant = oracle.quantize_fp8 if name == "fp8" else oracle.quantize_mxfp4
+    deq = oracle.dequantize_fp8 if name == "fp8" else oracle.dequantize_mxfp4
+    q = (*quant(c.gate_up.f32), *quant(c.down.f32))
+    idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note(f"experts {name} small ragged")
+    _, out = _q_path(c, FMTS[name], c.T, c.x, idx, w, q)
+    ref = _run_oracle(name, c.x.f32, q, idx, w)
+    bound, exact = bf16_path_bound(c.x.f32, deq(q[0], q[1]), deq(q[2], q[3]), idx, w)
+    np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
+    assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) / bound))
