@@ -282,18 +282,32 @@ def dense_mask_measure(torch, wl, T, steps, warmup, xbatches, seed, sparse_ms):
     }
 
 
-def int8_decode_measure(torch, lib, wl, T, steps, warmup, xbatches, seed):
-    """Decode with the experts as int8 per-channel symmetric codes (quantized
-    on the GPU from the same weight copies): route, int8 experts, combine."""
+QUANT_FORMATS = {
+    # name: (format code, weights per byte, scale bytes per weight row of length n, description)
+    "int8": (1, 1, lambda n: 4, "int8 per-channel symmetric"),
+    "fp8": (2, 1, lambda n: 4, "E4M3 per-channel (OCP FP8)"),
+    "mxfp4": (3, 2, lambda n: n // 32, "MXFP4 (E2M1, E8M0 scale per 32 weights)"),
+}
+
+
+def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed):
+    """Decode with the experts' weights quantized on the GPU (from the same
+    weight copies) into one of QUANT_FORMATS: route, experts, combine."""
+    fmt, per_byte, sbytes, desc = QUANT_FORMATS[name]
+
+    def quant(wt):
+        rows, n = wt.numel() // wt.shape[-1], wt.shape[-1]
+        q = torch.empty(rows * n // per_byte, dtype=torch.uint8, device="cuda")
+        if fmt == 3:
+            sc = torch.empty(rows * n // 32, dtype=torch.uint8, device="cuda")
+        else:
+            sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+        lib.moe_quantize(fmt, wt, q, sc)
+        return q, sc
+
     qcopies = []
     for rw, rs, pes, gu, dn in wl.copies:
-        guq = torch.empty(gu.shape, dtype=torch.int8, device="cuda")
-        gus = torch.empty(gu.shape[:-1], dtype=torch.float32, device="cuda")
-        dnq = torch.empty(dn.shape, dtype=torch.int8, device="cuda")
-        dns = torch.empty(dn.shape[:-1], dtype=torch.float32, device="cuda")
-        lib.moe_quantize_int8(gu, guq, gus)
-        lib.moe_quantize_int8(dn, dnq, dns)
-        qcopies.append((rw, rs, pes, guq, gus, dnq, dns))
+        qcopies.append((rw, rs, pes, *quant(gu), *quant(dn)))
     torch.cuda.synchronize()
     r = Runner(wl, T)
     xs = wl.batches(T, xbatches, seed)
@@ -307,7 +321,8 @@ def int8_decode_measure(torch, lib, wl, T, steps, warmup, xbatches, seed):
         lib.moe_route(d, T, x, rw, rs, pes, None, r.idx, r.w, r.counts, r.offsets, r.sorted, r.ws)
         if ev is not None:
             ev[1].record()
-        lib.moe_expert_ffn_int8(d, T, x, guq, gus, dnq, dns, r.w, r.offsets, r.sorted, r.y, r.ws)
+        lib.moe_expert_ffn_q(d, fmt, T, x, guq, gus, dnq, dns, r.w, r.offsets, r.sorted, r.y,
+                             r.ws)
         if ev is not None:
             ev[2].record()
         lib.moe_combine(d, T, r.y, None, r.out)
@@ -325,19 +340,21 @@ def int8_decode_measure(torch, lib, wl, T, steps, warmup, xbatches, seed):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
-    seg = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
-           for j, name in enumerate(("route", "experts", "combine"))}
+    seg = {nm: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+           for j, nm in enumerate(("route", "experts", "combine"))}
     us = []
     for i in range(len(qcopies)):
         step(i)
         torch.cuda.synchronize()
         us.append(int((r.counts > 0).sum().item()))
     U = sum(us) / len(us)
-    per_expert = (GATE_UP_BYTES + DOWN_BYTES) // 2 + (2 * I + H) * 4  # codes + scales
+    # codes + scales of one expert's gate_up (2I rows of H) and down (H rows of I)
+    per_expert = (2 * I * H + H * I) // per_byte + 2 * I * sbytes(H) + H * sbytes(I)
     expert_bytes = U * per_expert + T * H * 2
     step_bytes = U * per_expert + ROUTER_BYTES + 2 * T * H * 2
     return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-            "distinct_experts": U, "kernel_ms": seg, "weights": "int8 per-channel symmetric",
+            "distinct_experts": U, "kernel_ms": seg, "weights": desc,
+            "expert_bytes_per_expert": per_expert,
             "experts_gbs": expert_bytes / (seg["experts"] * 1e-3) / 1e9,
             "experts_hbm_frac": expert_bytes / (seg["experts"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -759,9 +776,11 @@ def main():
                 torch, wl, args.prefill, 5, 2, 2, args.seed, prefill["ms_per_step"])
             done(f"all-experts ablation {args.prefill}")
 
-    int8 = int8_decode_measure(torch, lib, wl, args.batch, args.steps, args.warmup,
-                               args.xbatches, args.seed)
-    done("int8 decode")
+    quant = {}
+    for name in QUANT_FORMATS:
+        quant[name] = quant_decode_measure(torch, lib, wl, name, args.batch, args.steps,
+                                           args.warmup, args.xbatches, args.seed)
+        done(f"{name} experts decode")
 
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
     done("tiny fp32")
@@ -786,7 +805,8 @@ def main():
     if prefill is not None:
         prefill["grouped_gemm_frac_of_achievable_mfma"] = (prefill["grouped_gemm_tflops"] /
                                                            ach["mfma_bf16_tflops"])
-    int8["experts_frac_of_achievable_read"] = int8["experts_gbs"] / ach["hbm_read_gbs"]
+    for r in quant.values():
+        r["experts_frac_of_achievable_read"] = r["experts_gbs"] / ach["hbm_read_gbs"]
 
     cpu = None
     cpu_configs = None
@@ -827,7 +847,7 @@ def main():
         "decode": {str(args.batch): head, **sweep},
         "prefill": prefill,
         "dense_masked_ablation": dense_mask or None,
-        "int8_experts_decode": int8,
+        "quantized_experts_decode": quant,
         "tiny_f32": tiny,
         "block": block,
         "stack": stack,

@@ -103,6 +103,19 @@ __device__ __forceinline__ void row_tile_lookup(const RowTileScan& s,
   row1 = min(row0 + bm, offsets[e_out + 1]);
 }
 
+// Work items are (row tile, column tile) pairs, column tiles fastest.  Block
+// b of a 1-D grid runs on XCD b % 8 (workgroups go round-robin to the eight
+// XCDs); each XCD takes a contiguous range of the real items, so that items
+// sharing gathered rows or a weight slab run on one XCD at about the same time
+// and share its L2.  Blocks past an XCD's range get -1.  Needs gridDim.x >=
+// n_items.
+__device__ __forceinline__ int xcd_item(int b, int n_items) {
+  const int x = b % 8, l = b / 8;
+  const int q = n_items / 8, r = n_items % 8;
+  const int cnt = q + (x < r ? 1 : 0);
+  return l < cnt ? x * q + min(x, r) + l : -1;
+}
+
 // Returns false if `tile` is past the last tile.
 __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E,
                                               int bm, int tile, int& e_out, int& row0,

@@ -70,18 +70,6 @@ __device__ __forceinline__ void wait_vmem() {
 // s_waitcnt lgkmcnt(0).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Work items are (row tile, column tile) pairs, column tiles fastest.  Block
-// b runs on XCD b % 8; each XCD takes a contiguous range of the real items so
-// that items sharing gathered rows or a weight slab run on one XCD at about
-// the same time and share its L2.  Blocks past an XCD's range get -1.  Needs
-// gridDim.x >= n_items.
-__device__ __forceinline__ int xcd_item(int b, int n_items) {
-  const int x = b % 8, l = b / 8;
-  const int q = n_items / 8, r = n_items % 8;
-  const int cnt = q + (x < r ? 1 : 0);
-  return l < cnt ? x * q + min(x, r) + l : -1;
-}
-
 // GU: h[row] = GELU(A[row] . W0[n]) * (A[row] . W1[n]) for the block's 128
 // columns n, A row = token of the slot (or the row itself when ident).
 // !GU: y[slot] = w[slot] * (h[row] . W0[n]) for the block's 256 columns n.

@@ -21,10 +21,16 @@
 // sum over all of its k.  Contraction lengths are multiples of 32, so a
 // lane's 16-element group is either wholly inside or wholly past the end.
 //
-// Measured on the 26B-A4B decode shapes (64 tokens, ~125 experts touched):
-// gate_up streams at ~5.8 TB/s and down at ~4.8 TB/s, against ~6.0 TB/s for
-// a plain streaming read on the same part; wider per-lane loads, deeper
-// register rings and non-temporal loads measured no better or worse.
+// Weights below bf16 (int8, E4M3, MXFP4; wformat.h) are loaded as stored
+// and widened to bf16 in registers right before their MFMAs; those kernels
+// give each wave NC = 2 column groups that share its activation fragments.
+//
+// Measured on the 26B-A4B decode shapes (64 tokens, ~126 experts touched):
+// bf16 gate_up streams at the part's measured streaming-read rate (~5.6
+// TB/s) and down at ~4.8 TB/s; the narrower formats are bound by load
+// issue rather than bytes (int8 / E4M3 ~4 TB/s, MXFP4 ~2 TB/s).  Wider
+// per-lane loads, deeper register rings, more column groups per wave and
+// non-temporal loads measured no better or worse.
 #include "common.h"
 #include "launch.h"
 #include "wformat.h"
@@ -51,20 +57,40 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bool stream_tile(bool ident, int rows, const int32_t* offsets, int E,
-                                            int bm, int& e, int& row0, int& row1) {
+// The block's work item: row tile (of at most bm rows of one expert, or of
+// the tokens when ident) and column group cg of CG, from the XCD-aware
+// mapping of common.h over the real number of items, so that the column
+// groups of a row tile (which read the same activation rows) share one XCD's
+// L2.  1-D grid of at least (row tile bound) * CG blocks.
+__device__ __forceinline__ bool stream_item(bool ident, int rows, const int32_t* offsets, int E,
+                                            int bm, int CG, int& e, int& row0, int& row1,
+                                            int& cg) {
+  RowTileScan sc;
+  int R;
+  if (ident) {
+    R = (rows + bm - 1) / bm;
+  } else {
+    row_tile_scan(offsets, E, bm, sc);
+    R = sc.total;
+  }
+  const int item = xcd_item(blockIdx.x, R * CG);
+  if (item < 0) return false;
+  const int rt = item / CG;
+  cg = item % CG;
   if (ident) {
     e = 0;
-    row0 = blockIdx.x * bm;
+    row0 = rt * bm;
     row1 = min(row0 + bm, rows);
-    return row0 < rows;
+  } else {
+    row_tile_lookup(sc, offsets, bm, rt, e, row0, row1);
   }
-  return find_row_tile(offsets, E, bm, blockIdx.x, e, row0, row1);
+  return true;
 }
 
-// gate_up: one block = one row tile (<= 16 * MB rows) x 16 gate + 16 up
-// columns; its WK waves split H.
-template <typename WQ, int WK, int MB, int NS>
+// gate_up: one block = one row tile (<= 16 * MB rows) x NC groups of 16 gate
+// + 16 up columns; its WK waves split H.  A wave's activation fragments serve
+// all NC groups, so narrow weight formats stream more bytes per wave.
+template <typename WQ, int WK, int MB, int NS, int NC>
 __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     int H, int N, int E, int K, int rows, int ident, const bf16* __restrict__ x,
     const WQ* __restrict__ wg, const WQ* __restrict__ wu, long long w_stride,
@@ -72,23 +98,16 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     bf16* __restrict__ h) {
   typedef WFmt<WQ> F;
-  __shared__ f32x4 red[WK][MB][2][kWave];
-  int e, row0, row1;
-  if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
+  __shared__ f32x4 red[WK][MB][NC][2][kWave];
+  int e, row0, row1, cg;
+  const int CG = (N + 16 * NC - 1) / (16 * NC);
+  if (!stream_item(ident, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int fr = lane % 16, fg = lane / 16;
-  const int n = blockIdx.y * 16 + fr;
-  const bool nvalid = n < N;
-  const long long wel = (long long)e * w_stride + (long long)(nvalid ? n : 0) * H;
-  const WQ* gp = wrow(wg, wel);
-  const WQ* up = wrow(wu, wel);
-  const uint8_t* gsr = nullptr;
-  const uint8_t* usr = nullptr;
-  if constexpr (F::kBlockScale) {
-    const long long sel = (long long)e * s_stride + (long long)(nvalid ? n : 0) * (H / 32);
-    gsr = static_cast<const uint8_t*>(sg) + sel;
-    usr = static_cast<const uint8_t*>(su) + sel;
-  }
+  const int n0 = cg * 16 * NC + fr;  // column of group c: n0 + 16 c
+  // weight row n0 + 16 c of group e starts at element wel0 + 16 c H
+  const long long wel0 = (long long)e * w_stride + (long long)n0 * H;
+  const long long sel0 = (long long)e * s_stride + (long long)n0 * (H / 32);
   const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
   const bf16* ap[MB];
   bool av[MB];
@@ -102,83 +121,105 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
   const int KB = (H + kKB - 1) / kKB;
   const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
 
-  f32x4 accg[MB], accu[MB];
+  f32x4 accg[MB][NC], accu[MB][NC];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    accg[mb] = f32x4{0, 0, 0, 0};
-    accu[mb] = f32x4{0, 0, 0, 0};
-  }
-  WRaw<WQ> bg[NS], bu[NS];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      accg[mb][c] = f32x4{0, 0, 0, 0};
+      accu[mb][c] = f32x4{0, 0, 0, 0};
+    }
+  WRaw<WQ> bg[NS][NC], bu[NS][NC];
   Frag ba[NS][MB];
-  auto load = [&](int kb, WRaw<WQ>& g, WRaw<WQ>& u, Frag (&a)[MB]) {
+  auto load = [&](int kb, int slot) {
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < H;
-    if (nvalid && kv) {
-      g.load(gp, k + 16 * fg, gsr);
-      u.load(up, k + 16 * fg, usr);
-    } else {
-      g.zero();
-      u.zero();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (n0 + 16 * c < N && kv) {
+        const long long wel = wel0 + 16LL * c * H;
+        const uint8_t* gsr = nullptr;
+        const uint8_t* usr = nullptr;
+        if constexpr (F::kBlockScale) {
+          gsr = static_cast<const uint8_t*>(sg) + sel0 + 16LL * c * (H / 32);
+          usr = static_cast<const uint8_t*>(su) + sel0 + 16LL * c * (H / 32);
+        }
+        bg[slot][c].load(wrow(wg, wel), k + 16 * fg, gsr);
+        bu[slot][c].load(wrow(wu, wel), k + 16 * fg, usr);
+      } else {
+        bg[slot][c].zero();
+        bu[slot][c].zero();
+      }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      if (mb < nmb && av[mb] && kv) ld_frag(a[mb], ap[mb] + k);
-      else zero_frag(a[mb]);
+      if (mb < nmb && av[mb] && kv) ld_frag(ba[slot][mb], ap[mb] + k);
+      else zero_frag(ba[slot][mb]);
     }
   };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (kb0 + s < kb1) load(kb0 + s, bg[s], bu[s], ba[s]);
+    if (kb0 + s < kb1) load(kb0 + s, s);
   for (int kb = kb0; kb < kb1; kb += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
-      if (kl < kb1) load(kl, bg[(s + NS - 1) % NS], bu[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
-      const Frag fgt = bg[s].widen(), fup = bu[s].widen();
+      if (kl < kb1) load(kl, (s + NS - 1) % NS);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int c = 0; c < NC; ++c) {
+        const Frag fgt = bg[s][c].widen(), fup = bu[s][c].widen();
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          if (mb < nmb) {
-            accg[mb] = mfma16(ba[s][mb].v[j], fgt.v[j], accg[mb]);
-            accu[mb] = mfma16(ba[s][mb].v[j], fup.v[j], accu[mb]);
-          }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            if (mb < nmb) {
+              accg[mb][c] = mfma16(ba[s][mb].v[j], fgt.v[j], accg[mb][c]);
+              accu[mb][c] = mfma16(ba[s][mb].v[j], fup.v[j], accu[mb][c]);
+            }
+      }
     }
   }
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    red[wave][mb][0][lane] = accg[mb];
-    red[wave][mb][1][lane] = accu[mb];
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      red[wave][mb][c][0][lane] = accg[mb][c];
+      red[wave][mb][c][1][lane] = accu[mb][c];
+    }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (mb >= nmb) break;
-    f32x4 g = red[0][mb][0][lane], u = red[0][mb][1][lane];
 #pragma unroll
-    for (int w = 1; w < WK; ++w) {
-      g += red[w][mb][0][lane];
-      u += red[w][mb][1][lane];
-    }
-    if constexpr (F::kChannelScale) {
-      if (nvalid) {
-        g *= static_cast<const float*>(sg)[(size_t)e * s_stride + n];
-        u *= static_cast<const float*>(su)[(size_t)e * s_stride + n];
+    for (int c = 0; c < NC; ++c) {
+      const int n = n0 + 16 * c;
+      const bool nvalid = n < N;
+      f32x4 g = red[0][mb][c][0][lane], u = red[0][mb][c][1][lane];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) {
+        g += red[w][mb][c][0][lane];
+        u += red[w][mb][c][1][lane];
       }
-    }
+      if constexpr (F::kChannelScale) {
+        if (nvalid) {
+          g *= static_cast<const float*>(sg)[(size_t)e * s_stride + n];
+          u *= static_cast<const float*>(su)[(size_t)e * s_stride + n];
+        }
+      }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 16 * mb + 4 * fg + r;
-      if (row < row1 && nvalid) h[(size_t)row * N + n] = (bf16)(gelu_tanh(g[r]) * u[r]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * mb + 4 * fg + r;
+        if (row < row1 && nvalid) h[(size_t)row * N + n] = (bf16)(gelu_tanh(g[r]) * u[r]);
+      }
     }
   }
 }
 
-// down: one block = one row tile x 16 * WN output columns; WK waves split
-// the contraction (the intermediate width N).
-template <typename WQ, int WN, int WK, int MB, int NS, typename YT>
+// down: one block = one row tile x WN waves of NC groups of 16 output
+// columns; WK waves split the contraction (the intermediate width N).
+template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>
 __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
     const WQ* __restrict__ wd, long long w_stride, const void* __restrict__ sd,
@@ -186,19 +227,16 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
     YT* __restrict__ y) {
   typedef WFmt<WQ> F;
-  __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][kWave];
-  int e, row0, row1;
-  if (!stream_tile(ident, rows, offsets, E, 16 * MB, e, row0, row1)) return;
+  __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][NC][kWave];
+  int e, row0, row1, cg;
+  const int CG = (H + 16 * WN * NC - 1) / (16 * WN * NC);
+  if (!stream_item(ident, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wn = wave % WN, wk = wave / WN;
   const int fr = lane % 16, fg = lane / 16;
-  const int n = blockIdx.y * 16 * WN + 16 * wn + fr;
-  const bool nvalid = n < H;
-  const WQ* bp = wrow(wd, (long long)e * w_stride + (long long)(nvalid ? n : 0) * N);
-  const uint8_t* bsr = nullptr;
-  if constexpr (F::kBlockScale)
-    bsr = static_cast<const uint8_t*>(sd) + (long long)e * s_stride +
-          (long long)(nvalid ? n : 0) * (N / 32);
+  const int n0 = (cg * WN + wn) * 16 * NC + fr;  // column of group c: n0 + 16 c
+  const long long wel0 = (long long)e * w_stride + (long long)n0 * N;
+  const long long sel0 = (long long)e * s_stride + (long long)n0 * (N / 32);
   const int nmb = (row1 - row0 + 15) / 16;
   const bf16* ap[MB];
   bool av[MB];
@@ -211,65 +249,89 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   const int KB = (N + kKB - 1) / kKB;
   const int kb0 = wk * KB / WK, kb1 = (wk + 1) * KB / WK;
 
-  f32x4 acc[MB];
+  f32x4 acc[MB][NC];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0, 0, 0, 0};
-  WRaw<WQ> bb[NS];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[mb][c] = f32x4{0, 0, 0, 0};
+  WRaw<WQ> bb[NS][NC];
   Frag ba[NS][MB];
-  auto load = [&](int kb, WRaw<WQ>& b, Frag (&a)[MB]) {
+  auto load = [&](int kb, int slot) {
     const int k = kb * kKB;
     const bool kv = k + 16 * fg < N;
-    if (nvalid && kv) b.load(bp, k + 16 * fg, bsr);
-    else b.zero();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (n0 + 16 * c < H && kv) {
+        const uint8_t* bsr = nullptr;
+        if constexpr (F::kBlockScale)
+          bsr = static_cast<const uint8_t*>(sd) + sel0 + 16LL * c * (N / 32);
+        bb[slot][c].load(wrow(wd, wel0 + 16LL * c * N), k + 16 * fg, bsr);
+      } else {
+        bb[slot][c].zero();
+      }
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      if (mb < nmb && av[mb] && kv) ld_frag(a[mb], ap[mb] + k);
-      else zero_frag(a[mb]);
+      if (mb < nmb && av[mb] && kv) ld_frag(ba[slot][mb], ap[mb] + k);
+      else zero_frag(ba[slot][mb]);
     }
   };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (kb0 + s < kb1) load(kb0 + s, bb[s], ba[s]);
+    if (kb0 + s < kb1) load(kb0 + s, s);
   for (int kb = kb0; kb < kb1; kb += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (kb + s >= kb1) break;
       const int kl = kb + s + NS - 1;
-      if (kl < kb1) load(kl, bb[(s + NS - 1) % NS], ba[(s + NS - 1) % NS]);
-      const Frag fb = bb[s].widen();
+      if (kl < kb1) load(kl, (s + NS - 1) % NS);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int c = 0; c < NC; ++c) {
+        const Frag fb = bb[s][c].widen();
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          if (mb < nmb) acc[mb] = mfma16(ba[s][mb].v[j], fb.v[j], acc[mb]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            if (mb < nmb) acc[mb][c] = mfma16(ba[s][mb].v[j], fb.v[j], acc[mb][c]);
+      }
     }
   }
   if constexpr (WK > 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) red[wave][mb][c][lane] = acc[mb][c];
     __syncthreads();
     if (wk != 0) return;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc[mb] = red[wn][mb][lane];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int w = 1; w < WK; ++w) acc[mb] += red[wn + w * WN][mb][lane];
-    }
+      for (int c = 0; c < NC; ++c) {
+        acc[mb][c] = red[wn][mb][c][lane];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) acc[mb][c] += red[wn + w * WN][mb][c][lane];
+      }
   }
-  float chs = 1.0f;
-  if constexpr (F::kChannelScale)
-    if (nvalid) chs = static_cast<const float*>(sd)[(size_t)e * s_stride + n];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if (mb >= nmb) break;
-    if constexpr (F::kChannelScale) acc[mb] *= chs;
+  for (int c = 0; c < NC; ++c) {
+    const int n = n0 + 16 * c;
+    const bool nvalid = n < H;
+    float chs = 1.0f;
+    if constexpr (F::kChannelScale)
+      if (nvalid) chs = static_cast<const float*>(sd)[(size_t)e * s_stride + n];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 16 * mb + 4 * fg + r;
-      if (row >= row1 || !nvalid) continue;
-      const int slot = ident ? row : sorted_slots[row];
-      const float sc = ident ? 1.0f : topk_w[slot];
-      y[(size_t)slot * H + n] = from_f32<YT>(sc * acc[mb][r]);
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= nmb) break;
+      f32x4 v = acc[mb][c];
+      if constexpr (F::kChannelScale) v *= chs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * mb + 4 * fg + r;
+        if (row >= row1 || !nvalid) continue;
+        const int slot = ident ? row : sorted_slots[row];
+        const float sc = ident ? 1.0f : topk_w[slot];
+        y[(size_t)slot * H + n] = from_f32<YT>(sc * v[r]);
+      }
     }
   }
 }
@@ -281,36 +343,37 @@ int tile_bound(bool ident, int rows, int T, int E, int bm) {
   return (int)(a < b ? a : b);
 }
 
-template <typename WQ, int WK, int MB, int NS>
+template <typename WQ, int WK, int MB, int NS, int NC>
 void launch_gu(const GateUpArgs& a, hipStream_t s) {
-  dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.N + 15) / 16);
-  hipLaunchKernelGGL((gate_up_stream_kernel<WQ, WK, MB, NS>), grid, dim3(64 * WK), 0, s, a.H, a.N,
-                     a.E, a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
+  const long long cgs = (a.N + 16 * NC - 1) / (16 * NC);
+  dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
+  hipLaunchKernelGGL((gate_up_stream_kernel<WQ, WK, MB, NS, NC>), grid, dim3(64 * WK), 0, s, a.H,
+                     a.N, a.E, a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
                      static_cast<const WQ*>(a.w_gate), static_cast<const WQ*>(a.w_up), a.w_stride,
-                     a.s_gate, a.s_up, a.s_stride,
-                     a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
+                     a.s_gate, a.s_up, a.s_stride, a.offsets, a.sorted_slots,
+                     static_cast<bf16*>(a.h));
 }
 
-template <typename WQ, int WN, int WK, int MB, int NS, typename YT>
+template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>
 void launch_dn(const DownArgs& a, hipStream_t s) {
-  dim3 grid(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB), (a.H + 16 * WN - 1) / (16 * WN));
-  hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, YT>), grid, dim3(64 * WN * WK), 0, s,
-                     a.H, a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
-                     static_cast<const WQ*>(a.w_down), a.w_stride,
-                     a.s_down, a.s_stride, a.offsets, a.sorted_slots,
-                     a.topk_w, static_cast<YT*>(a.y));
+  const long long cgs = (a.H + 16 * WN * NC - 1) / (16 * WN * NC);
+  dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
+  hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, NC, YT>), grid, dim3(64 * WN * WK), 0,
+                     s, a.H, a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
+                     static_cast<const WQ*>(a.w_down), a.w_stride, a.s_down, a.s_stride,
+                     a.offsets, a.sorted_slots, a.topk_w, static_cast<YT*>(a.y));
 }
 
 template <typename YT>
 void launch_dn_t(const DownArgs& a, hipStream_t s) {
   switch (a.w_fmt) {
-    case WFormat::kInt8: launch_dn<int8_t, 2, 2, 1, 2, YT>(a, s); return;
-    case WFormat::kFP8: launch_dn<fp8e4m3, 2, 2, 1, 2, YT>(a, s); return;
-    case WFormat::kMXFP4: launch_dn<fp4x2, 2, 2, 1, 2, YT>(a, s); return;
+    case WFormat::kInt8: launch_dn<int8_t, 2, 2, 1, 2, 2, YT>(a, s); return;
+    case WFormat::kFP8: launch_dn<fp8e4m3, 2, 2, 1, 2, 2, YT>(a, s); return;
+    case WFormat::kMXFP4: launch_dn<fp4x2, 2, 2, 1, 2, 2, YT>(a, s); return;
     case WFormat::kBF16: break;
   }
-  if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, YT>(a, s);
-  else launch_dn<bf16, 4, 1, 1, 2, YT>(a, s);
+  if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, 1, YT>(a, s);
+  else launch_dn<bf16, 4, 1, 1, 2, 1, YT>(a, s);
 }
 
 }  // namespace
@@ -329,12 +392,12 @@ bool use_stream_kernels(int T, int rows, int E, bool ident) {
 // flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
   switch (a.w_fmt) {
-    case WFormat::kInt8: launch_gu<int8_t, 4, 1, 2>(a, s); break;
-    case WFormat::kFP8: launch_gu<fp8e4m3, 4, 1, 2>(a, s); break;
-    case WFormat::kMXFP4: launch_gu<fp4x2, 4, 1, 2>(a, s); break;
+    case WFormat::kInt8: launch_gu<int8_t, 4, 1, 2, 2>(a, s); break;
+    case WFormat::kFP8: launch_gu<fp8e4m3, 4, 1, 2, 2>(a, s); break;
+    case WFormat::kMXFP4: launch_gu<fp4x2, 4, 1, 2, 2>(a, s); break;
     case WFormat::kBF16:
-      if (a.ident) launch_gu<bf16, 8, 2, 2>(a, s);
-      else launch_gu<bf16, 8, 1, 3>(a, s);
+      if (a.ident) launch_gu<bf16, 8, 2, 2, 1>(a, s);
+      else launch_gu<bf16, 8, 1, 3, 1>(a, s);
       break;
   }
   return hipGetLastError();
@@ -342,8 +405,8 @@ hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
 
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s) {
   if (a.ident && a.w_fmt == WFormat::kBF16) {
-    if (a.y_bf16) launch_dn<bf16, 2, 4, 2, 2, bf16>(a, s);
-    else launch_dn<bf16, 2, 4, 2, 2, float>(a, s);
+    if (a.y_bf16) launch_dn<bf16, 2, 4, 2, 2, 1, bf16>(a, s);
+    else launch_dn<bf16, 2, 4, 2, 2, 1, float>(a, s);
   } else if (a.y_bf16) {
     launch_dn_t<bf16>(a, s);
   } else {
