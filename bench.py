@@ -555,47 +555,57 @@ def achievable(torch):
                      "v_mfma_f32_32x32x16_bf16 loop"}
 
 
-class SmiSampler:
-    """GPU clock and socket power sampled with amd-smi (a child process) in a
-    background thread while the GPU legs run."""
-
-    def __init__(self):
-        import threading
-        self.samples, self.error = [], None
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _once(self):
-        import subprocess
+SMI_SAMPLER = r"""
+import json, subprocess, sys, time
+while True:
+    try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
                            capture_output=True, text=True, timeout=20)
         d = json.loads(r.stdout)["gpu_data"][0]
         gfx = [v["clk"]["value"] for k, v in d["clock"].items()
                if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-        return sum(gfx) / len(gfx), d["power"]["socket_power"]["value"]
+        print(json.dumps([sum(gfx) / len(gfx), d["power"]["socket_power"]["value"]]), flush=True)
+    except Exception as e:
+        print(json.dumps({"error": (type(e).__name__ + ": " + str(e))[:200]}), flush=True)
+        break
+    time.sleep(0.2)
+"""
 
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._once())
-            except Exception as e:  # amd-smi missing or its output changed
-                self.error = f"{type(e).__name__}: {e}"[:200]
-                return
-            self._stop.wait(0.2)
 
-    def start(self):
-        self._thread.start()
-        return self
+class SmiSampler:
+    """GPU clock and socket power sampled with amd-smi over the whole run.  The
+    sampler is a child process started before this process touches the GPU,
+    so that no process that has initialised the GPU starts another program."""
+
+    def __init__(self):
+        import subprocess
+        self.proc = subprocess.Popen([sys.executable, "-c", SMI_SAMPLER],
+                                     stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
 
     def stop(self):
-        self._stop.set()
-        self._thread.join(timeout=30)
-        if not self.samples:
-            return {"error": self.error or "no samples"}
-        clk = [c for c, _ in self.samples]
-        pw = [p for _, p in self.samples]
-        return {"samples": len(self.samples), "tool": "amd-smi metric -p -c",
-                "raw_mhz_w": [[round(c, 1), p] for c, p in self.samples],
+        import subprocess
+        self.proc.terminate()
+        try:
+            out = self.proc.communicate(timeout=30)[0]
+        except subprocess.TimeoutExpired:
+            self.proc.kill()
+            out = self.proc.communicate()[0]
+        samples, error = [], None
+        for line in out.splitlines():
+            try:
+                v = json.loads(line)
+            except ValueError:
+                continue
+            if isinstance(v, dict):
+                error = v.get("error")
+            else:
+                samples.append(v)
+        if not samples:
+            return {"error": error or "no samples"}
+        clk = [c for c, _ in samples]
+        pw = [p for _, p in samples]
+        return {"samples": len(samples), "tool": "amd-smi metric -p -c",
+                "raw_mhz_w": [[round(c, 1), p] for c, p in samples],
                 "gfx_clk_mhz": {"mean": sum(clk) / len(clk), "min": min(clk), "max": max(clk)},
                 "socket_power_w": {"mean": sum(pw) / len(pw), "min": min(pw), "max": max(pw)}}
 
@@ -730,6 +740,8 @@ def main():
               "(no collectives or sharding); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    smi = SmiSampler()  # before anything loads the GPU runtime
+
     import torch
     from sparse_moe_transformer_router_amd import lib
 
@@ -745,7 +757,6 @@ def main():
     def done(leg):
         print(f"bench: {leg} done", file=sys.stderr, flush=True)
 
-    smi = SmiSampler().start()
     ach = achievable(torch)
     done("achievable read / MFMA rates")
 
