@@ -42,6 +42,22 @@ constexpr int kKB = 64;  // k per block
 
 typedef W16 Frag;  // 16 bf16 activations of one row
 
+// Block scales (MXFP4) of the weight rows a block streams, staged in LDS at
+// block start: one E8M0 byte per 32 weights of a row, contraction up to
+// 32 * kMaxScaleRow.  Read from HBM once per block instead of once per
+// k-block and row (their cache lines would not survive the weight stream).
+constexpr int kMaxScaleRow = 256;
+
+// Copies n_rows scale rows of row_bytes each, consecutive in memory from
+// src (rows past valid_rows are left unset: their weights are never loaded),
+// into dst; ends with a barrier.
+__device__ __forceinline__ void stage_scales(uint8_t* dst, const uint8_t* src, int n_rows,
+                                             int valid_rows, int row_bytes) {
+  const int n = min(n_rows, max(valid_rows, 0)) * row_bytes;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+  __syncthreads();
+}
+
 __device__ __forceinline__ void ld_frag(Frag& f, const bf16* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
@@ -99,15 +115,23 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     bf16* __restrict__ h) {
   typedef WFmt<WQ> F;
   __shared__ f32x4 red[WK][MB][NC][2][kWave];
+  // gate and up block scales of the block's 16 * NC rows (MXFP4 only)
+  __shared__ uint8_t ssc[F::kBlockScale ? 2 * 16 * NC * kMaxScaleRow : 1];
   int e, row0, row1, cg;
   const int CG = (N + 16 * NC - 1) / (16 * NC);
   if (!stream_item(ident, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
+  if constexpr (F::kBlockScale) {
+    const long long first = (long long)e * s_stride + (long long)cg * 16 * NC * (H / 32);
+    const int valid = N - cg * 16 * NC;
+    stage_scales(ssc, static_cast<const uint8_t*>(sg) + first, 16 * NC, valid, H / 32);
+    stage_scales(ssc + 16 * NC * (H / 32), static_cast<const uint8_t*>(su) + first, 16 * NC,
+                 valid, H / 32);
+  }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int fr = lane % 16, fg = lane / 16;
   const int n0 = cg * 16 * NC + fr;  // column of group c: n0 + 16 c
   // weight row n0 + 16 c of group e starts at element wel0 + 16 c H
   const long long wel0 = (long long)e * w_stride + (long long)n0 * H;
-  const long long sel0 = (long long)e * s_stride + (long long)n0 * (H / 32);
   const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
   const bf16* ap[MB];
   bool av[MB];
@@ -141,8 +165,8 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
         const uint8_t* gsr = nullptr;
         const uint8_t* usr = nullptr;
         if constexpr (F::kBlockScale) {
-          gsr = static_cast<const uint8_t*>(sg) + sel0 + 16LL * c * (H / 32);
-          usr = static_cast<const uint8_t*>(su) + sel0 + 16LL * c * (H / 32);
+          gsr = ssc + (16 * c + fr) * (H / 32);
+          usr = ssc + (16 * NC + 16 * c + fr) * (H / 32);
         }
         bg[slot][c].load(wrow(wg, wel), k + 16 * fg, gsr);
         bu[slot][c].load(wrow(wu, wel), k + 16 * fg, usr);
@@ -228,15 +252,21 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     YT* __restrict__ y) {
   typedef WFmt<WQ> F;
   __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][NC][kWave];
+  // block scales of the block's 16 * WN * NC output rows (MXFP4 only)
+  __shared__ uint8_t ssc[F::kBlockScale ? 16 * WN * NC * kMaxScaleRow : 1];
   int e, row0, row1, cg;
   const int CG = (H + 16 * WN * NC - 1) / (16 * WN * NC);
   if (!stream_item(ident, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
+  if constexpr (F::kBlockScale)
+    stage_scales(ssc,
+                 static_cast<const uint8_t*>(sd) + (long long)e * s_stride +
+                     (long long)cg * 16 * WN * NC * (N / 32),
+                 16 * WN * NC, H - cg * 16 * WN * NC, N / 32);
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wn = wave % WN, wk = wave / WN;
   const int fr = lane % 16, fg = lane / 16;
   const int n0 = (cg * WN + wn) * 16 * NC + fr;  // column of group c: n0 + 16 c
   const long long wel0 = (long long)e * w_stride + (long long)n0 * N;
-  const long long sel0 = (long long)e * s_stride + (long long)n0 * (N / 32);
   const int nmb = (row1 - row0 + 15) / 16;
   const bf16* ap[MB];
   bool av[MB];
@@ -263,8 +293,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     for (int c = 0; c < NC; ++c) {
       if (n0 + 16 * c < H && kv) {
         const uint8_t* bsr = nullptr;
-        if constexpr (F::kBlockScale)
-          bsr = static_cast<const uint8_t*>(sd) + sel0 + 16LL * c * (N / 32);
+        if constexpr (F::kBlockScale) bsr = ssc + (16 * (wn * NC + c) + fr) * (N / 32);
         bb[slot][c].load(wrow(wd, wel0 + 16LL * c * N), k + 16 * fg, bsr);
       } else {
         bb[slot][c].zero();
