@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--dense-mask", type=int, default=1,
                     help="time the all-experts ablation at the decode and prefill sizes (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--clock-warmup", type=float, default=1.0,
+                    help="seconds of untimed decode steps before the first leg, so that the "
+                         "GPU clock has left its idle level (0 = none)")
     return ap.parse_args()
 
 
@@ -127,7 +130,8 @@ class Runner:
     def step(self, x, copy, ev=None):
         lib, d, T = self.wl.lib, self.wl.dims, self.T
         rw, rs, pes, gu, dn = copy
-        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        rec = (lambda j: ev[j] is not None and ev[j].record()) if ev is not None \
+            else (lambda j: None)
         rec(0)
         lib.moe_route(d, T, x, rw, rs, pes, None, self.idx, self.w, self.counts, self.offsets,
                       self.sorted, self.ws)
@@ -140,25 +144,41 @@ class Runner:
         rec(4)
 
 
-def time_steps(torch, runner, xs, copies, steps, warmup):
-    """Warm-up, then `steps` timed steps; returns (ms per step, per-segment ms, pairs used)."""
+def time_steps(torch, runner, xs, copies, steps, warmup, leg=None):
+    """Warm-up, then `steps` timed steps, then `steps` instrumented steps.
+
+    The timed region holds HIP events only around the gate_up launch (the
+    roofline kernel); an event between every launch costs the step several
+    microseconds, so the per-segment times come from the instrumented pass
+    that follows it.  Returns (ms per step, per-segment ms with gate_up from
+    the timed region, pairs of input / weight copy used in the timed region)."""
     n_ev = len(SEGMENTS) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     for i in range(warmup):
         runner.step(xs[i % len(xs)], copies[i % len(copies)])
     torch.cuda.synchronize()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pairs = []
+    t0 = time.perf_counter()
     start.record()
     for i in range(steps):
         j = warmup + i
         pairs.append((j % len(xs), j % len(copies)))
-        runner.step(xs[j % len(xs)], copies[j % len(copies)], events[i])
+        runner.step(xs[j % len(xs)], copies[j % len(copies)], [None, gev[i][0], gev[i][1]] +
+                    [None] * (n_ev - 3))
     end.record()
     torch.cuda.synchronize()
+    if leg is not None:
+        WINDOWS[leg] = (t0, time.perf_counter())
     total = start.elapsed_time(end)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for i in range(steps):
+        j = warmup + steps + i
+        runner.step(xs[j % len(xs)], copies[j % len(copies)], events[i])
+    torch.cuda.synchronize()
     seg = {name: sum(events[i][s].elapsed_time(events[i][s + 1]) for i in range(steps)) / steps
            for s, name in enumerate(SEGMENTS)}
+    seg["gate_up"] = sum(g[0].elapsed_time(g[1]) for g in gev) / steps
     return total / steps, seg, pairs
 
 
@@ -175,7 +195,7 @@ def distinct_experts(torch, runner, xs, copies, pairs):
 def decode_measure(torch, wl, T, steps, warmup, xbatches, seed):
     runner = Runner(wl, T)
     xs = wl.batches(T, xbatches, seed)
-    ms, seg, pairs = time_steps(torch, runner, xs, wl.copies, steps, warmup)
+    ms, seg, pairs = time_steps(torch, runner, xs, wl.copies, steps, warmup, f"decode_{T}")
     U = distinct_experts(torch, runner, xs, wl.copies, pairs)
     gate_up_bytes = U * GATE_UP_BYTES + T * H * 2
     step_bytes = U * (GATE_UP_BYTES + DOWN_BYTES) + ROUTER_BYTES + 2 * T * H * 2
@@ -212,7 +232,7 @@ def prefill_measure(torch, wl, T, steps, warmup, seed):
     to 1 and router weight column 0 set to b."""
     runner = Runner(wl, T)
     xs, copies = skewed_inputs(torch, wl, T, seed)
-    ms, seg, _ = time_steps(torch, runner, xs, copies, steps, warmup)
+    ms, seg, _ = time_steps(torch, runner, xs, copies, steps, warmup, f"prefill_{T}")
     runner.step(xs[0], copies[0])
     torch.cuda.synchronize()
     counts = runner.counts.cpu()
@@ -250,7 +270,8 @@ class DenseMaskRunner:
     def step(self, x, copy, ev=None):
         lib, d, T, sp = self.wl.lib, self.wl.dims, self.T, self.sparse
         rw, rs, pes, gu, dn = copy
-        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        rec = (lambda j: ev[j] is not None and ev[j].record()) if ev is not None \
+            else (lambda j: None)
         rec(0)
         lib.moe_route(d, T, x, rw, rs, pes, None, sp.idx, sp.w, sp.counts, sp.offsets,
                       sp.sorted, sp.ws)
@@ -268,7 +289,7 @@ def dense_mask_measure(torch, wl, T, steps, warmup, xbatches, seed, sparse_ms):
     """The all-experts ablation at T tokens against the sparse path's step time."""
     runner = DenseMaskRunner(wl, T)
     xs = wl.batches(T, xbatches, seed)
-    ms, seg, _ = time_steps(torch, runner, xs, wl.copies, steps, warmup)
+    ms, seg, _ = time_steps(torch, runner, xs, wl.copies, steps, warmup, f"all_experts_{T}")
     flops = T * E * 6 * H * I
     return {
         "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
@@ -332,14 +353,20 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     a.record()
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(warmup + i)
     b.record()
     torch.cuda.synchronize()
+    WINDOWS[f"{name}_decode_{T}"] = (t0, time.perf_counter())
     ms = a.elapsed_time(b) / steps
+    # per-segment times from an instrumented pass after the timed region
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
     seg = {nm: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
            for j, nm in enumerate(("route", "experts", "combine"))}
     us = []
@@ -520,6 +547,23 @@ def tiny_measure(torch, lib, steps, warmup):
             "dtype": "f32", "timing": "host clock around the launches (launch-bound)"}
 
 
+def clock_warmup(torch, wl, T, seconds, seed):
+    """Untimed decode steps for `seconds`: the GPU clock starts from its idle
+    level and takes a while to rise under load, which the few warmup steps of
+    each leg do not cover.  Returns the number of steps run."""
+    if seconds <= 0:
+        return 0
+    runner = Runner(wl, T)
+    xs = wl.batches(T, 4, seed + 99)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(64):
+            runner.step(xs[n % len(xs)], wl.copies[n % len(wl.copies)])
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def achievable(torch):
     """Measured ceilings of this GPU (libmoe_probe): a 4 GiB streaming read and
     a register-only bf16 MFMA loop (32x32x16, 8 independent accumulators per
@@ -532,22 +576,26 @@ def achievable(torch):
         probe.stream_read(buf, bx)
     n = 10
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     a.record()
     for _ in range(n):
         probe.stream_read(buf, bx)
     b.record()
     torch.cuda.synchronize()
+    WINDOWS["probe_hbm_read"] = (t0, time.perf_counter())
     read_gbs = n * buf.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
     del buf
     blocks, iters = 1024, 2000
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
     for _ in range(2):
         probe.mfma(blocks, iters, out)
+    t0 = time.perf_counter()
     a.record()
     for _ in range(5):
         probe.mfma(blocks, iters, out)
     b.record()
     torch.cuda.synchronize()
+    WINDOWS["probe_mfma"] = (t0, time.perf_counter())
     mfma_tflops = 5 * probe.mfma_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12
     assert bool((out == 16.0 * iters).all()), "MFMA probe result wrong"
     return {"hbm_read_gbs": read_gbs, "mfma_bf16_tflops": mfma_tflops,
@@ -555,59 +603,75 @@ def achievable(torch):
                      "v_mfma_f32_32x32x16_bf16 loop"}
 
 
-SMI_SAMPLER = r"""
-import json, subprocess, sys, time
-while True:
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)["gpu_data"][0]
-        gfx = [v["clk"]["value"] for k, v in d["clock"].items()
-               if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-        print(json.dumps([sum(gfx) / len(gfx), d["power"]["socket_power"]["value"]]), flush=True)
-    except Exception as e:
-        print(json.dumps({"error": (type(e).__name__ + ": " + str(e))[:200]}), flush=True)
-        break
-    time.sleep(0.2)
-"""
+class ClockSampler:
+    """GPU clock and socket power read from sysfs every few milliseconds in a
+    background thread (no child process): the gfx clock level the driver
+    marks current in pp_dpm_sclk, and hwmon power1_input.  Each leg reports
+    the samples that fall inside its timed region."""
 
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk = cards[0] if cards else None
+        pw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.power = pw[0] if pw else None
+        self.samples = []  # (t, MHz, W)
+        self.error = None if self.sclk else "no pp_dpm_sclk in sysfs"
+        self._stop = threading.Event()
+        self._period = period_s
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        if self.sclk:
+            self._thread.start()
 
-class SmiSampler:
-    """GPU clock and socket power sampled with amd-smi over the whole run.  The
-    sampler is a child process started before this process touches the GPU,
-    so that no process that has initialised the GPU starts another program."""
+    def _read(self):
+        mhz = None
+        with open(self.sclk) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    mhz = float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        watts = None
+        if self.power:
+            with open(self.power) as f:
+                watts = int(f.read().strip()) / 1e6
+        return mhz, watts
 
-    def __init__(self):
-        import subprocess
-        self.proc = subprocess.Popen([sys.executable, "-c", SMI_SAMPLER],
-                                     stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz, watts = self._read()
+                self.samples.append((time.perf_counter(), mhz, watts))
+            except (OSError, ValueError, IndexError) as e:
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(self._period)
 
     def stop(self):
-        import subprocess
-        self.proc.terminate()
-        try:
-            out = self.proc.communicate(timeout=30)[0]
-        except subprocess.TimeoutExpired:
-            self.proc.kill()
-            out = self.proc.communicate()[0]
-        samples, error = [], None
-        for line in out.splitlines():
-            try:
-                v = json.loads(line)
-            except ValueError:
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join(timeout=5)
+
+    def summary(self, windows):
+        """Per leg: mean / min / max gfx clock and power over its timed window."""
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        out = {"source": f"{self.sclk} (current level), {self.power}",
+               "period_ms": self._period * 1e3}
+        for leg, (t0, t1) in windows.items():
+            sel = [(m, w) for t, m, w in self.samples if t0 <= t <= t1 and m is not None]
+            if not sel:
                 continue
-            if isinstance(v, dict):
-                error = v.get("error")
-            else:
-                samples.append(v)
-        if not samples:
-            return {"error": error or "no samples"}
-        clk = [c for c, _ in samples]
-        pw = [p for _, p in samples]
-        return {"samples": len(samples), "tool": "amd-smi metric -p -c",
-                "raw_mhz_w": [[round(c, 1), p] for c, p in samples],
-                "gfx_clk_mhz": {"mean": sum(clk) / len(clk), "min": min(clk), "max": max(clk)},
-                "socket_power_w": {"mean": sum(pw) / len(pw), "min": min(pw), "max": max(pw)}}
+            ms = [m for m, _ in sel]
+            ws = [w for _, w in sel if w is not None]
+            out[leg] = {"samples": len(sel),
+                        "gfx_clk_mhz": {"mean": sum(ms) / len(ms), "min": min(ms), "max": max(ms)}}
+            if ws:
+                out[leg]["socket_power_w"] = {"mean": sum(ws) / len(ws), "min": min(ws),
+                                              "max": max(ws)}
+        return out
+
+
+WINDOWS = {}  # leg -> (start, end) of its timed region, host clock
 
 
 def cpu_model():
@@ -740,12 +804,11 @@ def main():
               "(no collectives or sharding); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    smi = SmiSampler()  # before anything loads the GPU runtime
-
     import torch
     from sparse_moe_transformer_router_amd import lib
 
     torch.cuda.set_device(0)
+    clocks_sampler = ClockSampler()
     wl = Workload(torch, lib, args.copies, args.seed)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -757,6 +820,8 @@ def main():
     def done(leg):
         print(f"bench: {leg} done", file=sys.stderr, flush=True)
 
+    warm_steps = clock_warmup(torch, wl, args.batch, args.clock_warmup, args.seed)
+    done(f"clock warm-up ({warm_steps} untimed decode steps)")
     ach = achievable(torch)
     done("achievable read / MFMA rates")
 
@@ -810,7 +875,8 @@ def main():
                               args.stack_prefill, args.seed)
         done(f"stack of {args.stack} layers")
 
-    clocks = smi.stop()
+    clocks_sampler.stop()
+    clocks = clocks_sampler.summary(WINDOWS)
     for r in [head, *sweep.values()]:
         r["gate_up_frac_of_achievable_read"] = r["gate_up_gbs"] / ach["hbm_read_gbs"]
     if prefill is not None:
@@ -836,6 +902,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup": {"seconds": args.clock_warmup, "untimed_decode_steps": warm_steps},
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
