@@ -5,40 +5,43 @@
 // (gate_up [2I, H] and down [H, I] of the page "Porting a 128-expert MoE
 // (Gemma-4 26B-A4B) to AWS Inferentia2", section "The architecture: a
 // dual-path FFN nobody warned me about").  These kernels keep the weight
-// operand out of LDS: per 64-wide k-block every lane loads 32 contiguous
-// bytes of one weight row straight into registers (four lanes cover a
-// 128-byte line) and feeds them to v_mfma_f32_16x16x32_bf16 as two
-// 8-element operands; the activation rows (at most 16 * MB per tile, resident
-// in L2) are loaded the same way.  Loads run NS k-blocks ahead of the MFMAs
-// (a register ring).  A block's waves split the contraction; their partial
-// sums meet in LDS and are added in wave order (deterministic), then the
-// epilogue applies GELU-tanh(gate) * up (gate_up) or the routing weight and
-// the slot scatter (down).
+// operand out of LDS: per k-block every lane loads 32 contiguous bytes of
+// one weight row straight into registers (four lanes cover a 128-byte line,
+// which is then used whole) and feeds them to v_mfma_f32_16x16x32_bf16 in
+// 8-element operands; the activation rows (at most 16 * MB per tile,
+// resident in L2) are loaded the same way.  Loads run NS - 1 k-blocks ahead
+// of the MFMAs (a register ring).  A block's waves split the contraction;
+// their partial sums meet in LDS and are added in wave order
+// (deterministic), then the epilogue applies GELU-tanh(gate) * up (gate_up)
+// or the routing weight and the slot scatter (down).
 //
-// k mapping: in k-block kb, lane l (row or column l % 16, group g = l / 16)
-// holds k = 64 kb + 16 g + [0, 16); MFMA j of the block uses its elements
-// [8 j, 8 j + 8).  A and B use the same mapping, so the two MFMAs of a block
-// sum over all of its k.  Contraction lengths are multiples of 32, so a
-// lane's 16-element group is either wholly inside or wholly past the end.
+// k mapping: a lane's span is L = 32 bytes of weights (L = 16 bf16, 32 int8
+// or E4M3, 64 MXFP4 weights); a k-block is 4 L.  In k-block kb, lane l (row
+// or column l % 16, group g = l / 16) holds k = 4 L kb + L g + [0, L); MFMA j
+// of the block uses its elements [8 j, 8 j + 8).  A and B use the same
+// mapping, so the 2 L / 16 MFMAs of a block sum over all of its k.
+// Contraction lengths are multiples of 32, so each 16-element sub-group of a
+// span is either wholly inside or wholly past the end.
 //
 // Weights below bf16 (int8, E4M3, MXFP4; wformat.h) are loaded as stored
-// and widened to bf16 in registers right before their MFMAs; those kernels
-// give each wave NC = 2 column groups that share its activation fragments.
+// and widened to bf16 in registers right before their MFMAs.  With
+// 16-element spans for every format, a line of an int8 or MXFP4 row was
+// used by 2 or 4 successive k-blocks, microseconds apart, and the L2 dropped
+// it in between: 17% and 45% more HBM reads than the weights.
 //
-// Measured on the 26B-A4B decode shapes (64 tokens, ~126 experts touched):
-// bf16 gate_up streams at the part's measured streaming-read rate (~5.6
-// TB/s) and down at ~4.8 TB/s; the narrower formats are bound by load
-// issue rather than bytes (int8 / E4M3 ~4 TB/s, MXFP4 ~2 TB/s).  Wider
-// per-lane loads, deeper register rings, more column groups per wave and
-// non-temporal loads measured no better or worse.
+// The loads carry no conditions in the steady state of the k-loop (clamped
+// addresses instead, see the kernels).  A load under a condition leaves the
+// compiler unsure how many loads are outstanding on each path, and it then
+// waits for all of them before every MFMA: the ring was being drained at
+// every k-block.
 #include "common.h"
 #include "launch.h"
 #include "wformat.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
-
-constexpr int kKB = 64;  // k per block
 
 typedef W16 Frag;  // 16 bf16 activations of one row
 
@@ -49,8 +52,8 @@ typedef W16 Frag;  // 16 bf16 activations of one row
 constexpr int kMaxScaleRow = 256;
 
 // Copies n_rows scale rows of row_bytes each, consecutive in memory from
-// src (rows past valid_rows are left unset: their weights are never loaded),
-// into dst; ends with a barrier.
+// src (rows past valid_rows are left unset and never read: the kernels clamp
+// their row index), into dst; ends with a barrier.
 __device__ __forceinline__ void stage_scales(uint8_t* dst, const uint8_t* src, int n_rows,
                                              int valid_rows, int row_bytes) {
   const int n = min(n_rows, max(valid_rows, 0)) * row_bytes;
@@ -62,11 +65,6 @@ __device__ __forceinline__ void ld_frag(Frag& f, const bf16* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
   for (int i = 0; i < 2; ++i) f.u[i] = q[i];
-}
-
-__device__ __forceinline__ void zero_frag(Frag& f) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) f.u[i] = make_uint4(0, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -100,6 +98,11 @@ __device__ __forceinline__ bool stream_item(bool ident, int rows, const int32_t*
   } else {
     row_tile_lookup(sc, offsets, bm, rt, e, row0, row1);
   }
+  // the same for every lane: scalar registers, scalar branches
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  row1 = __builtin_amdgcn_readfirstlane(row1);
+  cg = __builtin_amdgcn_readfirstlane(cg);
   return true;
 }
 
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots,
     bf16* __restrict__ h) {
   typedef WFmt<WQ> F;
+  static_assert(NS >= 2, "the load ring needs two slots or more");
   __shared__ f32x4 red[WK][MB][NC][2][kWave];
   // gate and up block scales of the block's 16 * NC rows (MXFP4 only)
   __shared__ uint8_t ssc[F::kBlockScale ? 2 * 16 * NC * kMaxScaleRow : 1];
@@ -127,22 +131,37 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
     stage_scales(ssc + 16 * NC * (H / 32), static_cast<const uint8_t*>(su) + first, 16 * NC,
                  valid, H / 32);
   }
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  constexpr int LK = F::kLaneK, U = LK / 16, KBK = 4 * LK;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int fr = lane % 16, fg = lane / 16;
   const int n0 = cg * 16 * NC + fr;  // column of group c: n0 + 16 c
-  // weight row n0 + 16 c of group e starts at element wel0 + 16 c H
-  const long long wel0 = (long long)e * w_stride + (long long)n0 * H;
+  // Every load below is unconditional and in bounds.  A column past N (a
+  // ragged last group) reads row N - 1 and a row past row1 reads row row0:
+  // their MFMA outputs are never stored.  A span past the end of the
+  // contraction reads k = 0, and its weights are zeroed where they are used
+  // (only in a ragged last k-block).
+  long long wel[NC];  // first element of the weight row of column n0 + 16 c
+  const uint8_t* gsr[NC];
+  const uint8_t* usr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    wel[c] = (long long)e * w_stride + (long long)min(n0 + 16 * c, N - 1) * H;
+    gsr[c] = usr[c] = nullptr;
+    if constexpr (F::kBlockScale) {
+      const int sr = min(16 * c + fr, N - 1 - cg * 16 * NC);  // staged rows only
+      gsr[c] = ssc + sr * (H / 32);
+      usr[c] = ssc + (16 * NC + sr) * (H / 32);
+    }
+  }
   const int nmb = (row1 - row0 + 15) / 16;  // active 16-row blocks (uniform)
   const bf16* ap[MB];
-  bool av[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int r = row0 + 16 * mb + fr;
-    av[mb] = r < row1;
-    const int tok = av[mb] ? (ident ? r : sorted_slots[r] / K) : 0;
-    ap[mb] = x + (size_t)tok * H + 16 * fg;
+    const int r = row0 + 16 * mb + fr, rr = r < row1 ? r : row0;
+    const int tok = ident ? rr : sorted_slots[rr] / K;
+    ap[mb] = x + (size_t)tok * H;
   }
-  const int KB = (H + kKB - 1) / kKB;
+  const int KB = (H + KBK - 1) / KBK;
   const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
 
   f32x4 accg[MB][NC], accu[MB][NC];
@@ -154,56 +173,69 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
       accu[mb][c] = f32x4{0, 0, 0, 0};
     }
   WRaw<WQ> bg[NS][NC], bu[NS][NC];
-  Frag ba[NS][MB];
+  Frag ba[NS][MB][U];
   auto load = [&](int kb, int slot) {
-    const int k = kb * kKB;
-    const bool kv = k + 16 * fg < H;
+    const int ks = kb * KBK + LK * fg;  // first weight of this lane's span
+    const bool kv = ks < H;
+    const int kc = kv ? ks : 0;              // in-bounds start
+    const bool kfull = kc + LK <= H;       // else only its first half lies inside
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (n0 + 16 * c < N && kv) {
-        const long long wel = wel0 + 16LL * c * H;
-        const uint8_t* gsr = nullptr;
-        const uint8_t* usr = nullptr;
-        if constexpr (F::kBlockScale) {
-          gsr = ssc + (16 * c + fr) * (H / 32);
-          usr = ssc + (16 * NC + 16 * c + fr) * (H / 32);
-        }
-        bg[slot][c].load(wrow(wg, wel), k + 16 * fg, gsr);
-        bu[slot][c].load(wrow(wu, wel), k + 16 * fg, usr);
-      } else {
-        bg[slot][c].zero();
-        bu[slot][c].zero();
-      }
+      bg[slot][c].load(wrow(wg, wel[c]), kc, gsr[c], kfull);
+      bu[slot][c].load(wrow(wu, wel[c]), kc, usr[c], kfull);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb < nmb && av[mb] && kv) ld_frag(ba[slot][mb], ap[mb] + k);
-      else zero_frag(ba[slot][mb]);
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb == 0 || mb < nmb)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int ku = kc + 16 * u;
+          ld_frag(ba[slot][mb][u], ap[mb] + (ku < H ? ku : 0));
+        }
+  };
+  // NS steps: step s loads k-block kb + s + NS - 1 into its ring slot, then
+  // runs the MFMAs of k-block kb + s.  In the steady state (kTail false)
+  // every load is in range and unconditional, so the compiler's waits count
+  // exactly the loads still outstanding and the ring stays in flight; the
+  // tail (the last 2 NS - 2 k-blocks at most) checks the ends and masks the
+  // ragged last k-block.
+  auto steps = [&](int kb, auto tail) {
+    constexpr bool kTail = decltype(tail)::value;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (kTail && kb + s >= kb1) break;
+      const int kl = kb + s + NS - 1;
+      if (!kTail || kl < kb1) load(kl, (s + NS - 1) % NS);
+      if (kTail && (kb + s + 1) * KBK > H) {  // uniform
+        const int ks = (kb + s) * KBK + LK * fg;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          bg[s][c].mask(ks < H, ks + LK <= H);
+          bu[s][c].mask(ks < H, ks + LK <= H);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const Frag fgt = bg[s][c].widen(u), fup = bu[s][c].widen(u);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              if (mb == 0 || mb < nmb) {
+                accg[mb][c] = mfma16(ba[s][mb][u].v[j], fgt.v[j], accg[mb][c]);
+                accu[mb][c] = mfma16(ba[s][mb][u].v[j], fup.v[j], accu[mb][c]);
+              }
+        }
     }
   };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (kb0 + s < kb1) load(kb0 + s, s);
-  for (int kb = kb0; kb < kb1; kb += NS) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (kb + s >= kb1) break;
-      const int kl = kb + s + NS - 1;
-      if (kl < kb1) load(kl, (s + NS - 1) % NS);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const Frag fgt = bg[s][c].widen(), fup = bu[s][c].widen();
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            if (mb < nmb) {
-              accg[mb][c] = mfma16(ba[s][mb].v[j], fgt.v[j], accg[mb][c]);
-              accu[mb][c] = mfma16(ba[s][mb].v[j], fup.v[j], accu[mb][c]);
-            }
-      }
-    }
-  }
+  int kb = kb0;
+  for (; kb + 2 * NS - 2 < kb1; kb += NS) steps(kb, std::false_type{});
+  for (; kb < kb1; kb += NS) steps(kb, std::true_type{});
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -251,6 +283,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
     YT* __restrict__ y) {
   typedef WFmt<WQ> F;
+  static_assert(NS >= 2, "the load ring needs two slots or more");
   __shared__ f32x4 red[WK > 1 ? WN * WK : 1][MB][NC][kWave];
   // block scales of the block's 16 * WN * NC output rows (MXFP4 only)
   __shared__ uint8_t ssc[F::kBlockScale ? 16 * WN * NC * kMaxScaleRow : 1];
@@ -262,21 +295,31 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
                  static_cast<const uint8_t*>(sd) + (long long)e * s_stride +
                      (long long)cg * 16 * WN * NC * (N / 32),
                  16 * WN * NC, H - cg * 16 * WN * NC, N / 32);
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  constexpr int LK = F::kLaneK, U = LK / 16, KBK = 4 * LK;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wn = wave % WN, wk = wave / WN;
   const int fr = lane % 16, fg = lane / 16;
   const int n0 = (cg * WN + wn) * 16 * NC + fr;  // column of group c: n0 + 16 c
-  const long long wel0 = (long long)e * w_stride + (long long)n0 * N;
+  // Unconditional in-bounds loads, as in gate_up: a column past H reads row
+  // H - 1, a row past row1 reads row row0, a span past N reads k = 0 with its
+  // weights zeroed where they are used.
+  long long wel[NC];
+  const uint8_t* bsr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    wel[c] = (long long)e * w_stride + (long long)min(n0 + 16 * c, H - 1) * N;
+    bsr[c] = nullptr;
+    if constexpr (F::kBlockScale)
+      bsr[c] = ssc + min(16 * (wn * NC + c) + fr, H - 1 - cg * 16 * WN * NC) * (N / 32);
+  }
   const int nmb = (row1 - row0 + 15) / 16;
   const bf16* ap[MB];
-  bool av[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = row0 + 16 * mb + fr;
-    av[mb] = r < row1;
-    ap[mb] = hbuf + (size_t)(av[mb] ? r : 0) * N + 16 * fg;
+    ap[mb] = hbuf + (size_t)(r < row1 ? r : row0) * N;
   }
-  const int KB = (N + kKB - 1) / kKB;
+  const int KB = (N + KBK - 1) / KBK;
   const int kb0 = wk * KB / WK, kb1 = (wk + 1) * KB / WK;
 
   f32x4 acc[MB][NC];
@@ -285,46 +328,55 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[mb][c] = f32x4{0, 0, 0, 0};
   WRaw<WQ> bb[NS][NC];
-  Frag ba[NS][MB];
+  Frag ba[NS][MB][U];
   auto load = [&](int kb, int slot) {
-    const int k = kb * kKB;
-    const bool kv = k + 16 * fg < N;
+    const int ks = kb * KBK + LK * fg;  // first weight of this lane's span
+    const bool kv = ks < N;
+    const int kc = kv ? ks : 0;              // in-bounds start
+    const bool kfull = kc + LK <= N;       // else only its first half lies inside
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (n0 + 16 * c < H && kv) {
-        const uint8_t* bsr = nullptr;
-        if constexpr (F::kBlockScale) bsr = ssc + (16 * (wn * NC + c) + fr) * (N / 32);
-        bb[slot][c].load(wrow(wd, wel0 + 16LL * c * N), k + 16 * fg, bsr);
-      } else {
-        bb[slot][c].zero();
+    for (int c = 0; c < NC; ++c) bb[slot][c].load(wrow(wd, wel[c]), kc, bsr[c], kfull);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb == 0 || mb < nmb)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int ku = kc + 16 * u;
+          ld_frag(ba[slot][mb][u], ap[mb] + (ku < N ? ku : 0));
+        }
+  };
+  // The same steady state and tail as gate_up.
+  auto steps = [&](int kb, auto tail) {
+    constexpr bool kTail = decltype(tail)::value;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (kTail && kb + s >= kb1) break;
+      const int kl = kb + s + NS - 1;
+      if (!kTail || kl < kb1) load(kl, (s + NS - 1) % NS);
+      if (kTail && (kb + s + 1) * KBK > N) {  // uniform
+        const int ks = (kb + s) * KBK + LK * fg;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bb[s][c].mask(ks < N, ks + LK <= N);
       }
-    }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb < nmb && av[mb] && kv) ld_frag(ba[slot][mb], ap[mb] + k);
-      else zero_frag(ba[slot][mb]);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const Frag fb = bb[s][c].widen(u);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              if (mb == 0 || mb < nmb) acc[mb][c] = mfma16(ba[s][mb][u].v[j], fb.v[j], acc[mb][c]);
+        }
     }
   };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (kb0 + s < kb1) load(kb0 + s, s);
-  for (int kb = kb0; kb < kb1; kb += NS) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (kb + s >= kb1) break;
-      const int kl = kb + s + NS - 1;
-      if (kl < kb1) load(kl, (s + NS - 1) % NS);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const Frag fb = bb[s][c].widen();
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            if (mb < nmb) acc[mb][c] = mfma16(ba[s][mb].v[j], fb.v[j], acc[mb][c]);
-      }
-    }
-  }
+  int kb = kb0;
+  for (; kb + 2 * NS - 2 < kb1; kb += NS) steps(kb, std::false_type{});
+  for (; kb < kb1; kb += NS) steps(kb, std::true_type{});
   if constexpr (WK > 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -396,9 +448,9 @@ void launch_dn(const DownArgs& a, hipStream_t s) {
 template <typename YT>
 void launch_dn_t(const DownArgs& a, hipStream_t s) {
   switch (a.w_fmt) {
-    case WFormat::kInt8: launch_dn<int8_t, 2, 2, 1, 2, 2, YT>(a, s); return;
-    case WFormat::kFP8: launch_dn<fp8e4m3, 2, 2, 1, 2, 2, YT>(a, s); return;
-    case WFormat::kMXFP4: launch_dn<fp4x2, 2, 2, 1, 2, 2, YT>(a, s); return;
+    case WFormat::kInt8: launch_dn<int8_t, 4, 1, 1, 2, 1, YT>(a, s); return;
+    case WFormat::kFP8: launch_dn<fp8e4m3, 4, 1, 1, 2, 1, YT>(a, s); return;
+    case WFormat::kMXFP4: launch_dn<fp4x2, 4, 1, 1, 2, 2, YT>(a, s); return;
     case WFormat::kBF16: break;
   }
   if (a.T <= 8) launch_dn<bf16, 2, 2, 1, 2, 1, YT>(a, s);
@@ -421,12 +473,12 @@ bool use_stream_kernels(int T, int rows, int E, bool ident) {
 // flight.
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
   switch (a.w_fmt) {
-    case WFormat::kInt8: launch_gu<int8_t, 4, 1, 2, 2>(a, s); break;
-    case WFormat::kFP8: launch_gu<fp8e4m3, 4, 1, 2, 2>(a, s); break;
-    case WFormat::kMXFP4: launch_gu<fp4x2, 4, 1, 2, 2>(a, s); break;
+    case WFormat::kInt8: launch_gu<int8_t, 2, 1, 3, 1>(a, s); break;
+    case WFormat::kFP8: launch_gu<fp8e4m3, 2, 1, 3, 1>(a, s); break;
+    case WFormat::kMXFP4: launch_gu<fp4x2, 1, 1, 2, 1>(a, s); break;
     case WFormat::kBF16:
       if (a.ident) launch_gu<bf16, 8, 2, 2, 1>(a, s);
-      else launch_gu<bf16, 8, 1, 3, 1>(a, s);
+      else launch_gu<bf16, 4, 1, 4, 1>(a, s);
       break;
   }
   return hipGetLastError();

@@ -202,8 +202,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(long long rows, int col
   const uint8_t* srow = nullptr;
   if constexpr (F::kBlockScale) srow = static_cast<const uint8_t*>(scale) + r * (cols / 32);
   WRaw<WQ> raw;
-  raw.load(wrow(q, r * cols), k, srow);
-  const W16 f = raw.widen();
+  raw.load16(wrow(q, r * cols), k, srow);
+  const W16 f = raw.widen(0);
   float sc = 1.0f;
   if constexpr (F::kChannelScale) sc = static_cast<const float*>(scale)[r];
   float v[16];

@@ -31,25 +31,31 @@ struct fp4x2 {
 
 // Per-format layout facts.  kPerUnit: weights per stored unit; kChannelScale:
 // one fp32 scale per output channel (after the k-sum); kBlockScale: one E8M0
-// scale per 32 weights along the contraction (folded into the widening).
+// scale per 32 weights along the contraction (folded into the widening);
+// kLaneK: weights of one row a lane loads at a time, 32 bytes as stored in
+// every format, so that four lanes cover one 128-byte line of the row.
 template <typename WQ> struct WFmt {
-  static constexpr int kPerUnit = 1;
+  static constexpr int kPerUnit = 1, kLaneK = 16;
   static constexpr bool kChannelScale = false, kBlockScale = false;
 };
 template <> struct WFmt<int8_t> {
-  static constexpr int kPerUnit = 1;
+  static constexpr int kPerUnit = 1, kLaneK = 32;
   static constexpr bool kChannelScale = true, kBlockScale = false;
 };
 template <> struct WFmt<fp8e4m3> {
-  static constexpr int kPerUnit = 1;
+  static constexpr int kPerUnit = 1, kLaneK = 32;
   static constexpr bool kChannelScale = true, kBlockScale = false;
 };
 template <> struct WFmt<fp4x2> {
-  static constexpr int kPerUnit = 2;
+  static constexpr int kPerUnit = 2, kLaneK = 64;
   static constexpr bool kChannelScale = false, kBlockScale = true;
 };
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 keep4(uint4 q, bool v) {
+  return make_uint4(v ? q.x : 0u, v ? q.y : 0u, v ? q.z : 0u, v ? q.w : 0u);
+}
 
 __device__ __forceinline__ uint32_t bf16x2_bits(bf16x2_v v) {
   return __builtin_bit_cast(uint32_t, v);
@@ -96,68 +102,110 @@ union W16 {
   bf16x8 v[2];
 };
 
-// One lane's 16 weights of one row, held raw (as stored) from their load to
-// their use.  load(row, k, srow): row points at the weight row's first unit,
-// k is the element index of the first of the 16 (a multiple of 16), srow the
-// row's block scales (fp4x2 only).
+// One lane's kLaneK weights of one row (32 bytes), held raw (as stored) from
+// their load to their use.  load(row, k, srow, full): row points at the
+// weight row's first unit, k is the element index of the first weight (a
+// multiple of kLaneK), srow the row's block scales (fp4x2 only); full is
+// false when only the first half of the span lies inside the row (fp4x2
+// only: a contraction that is a multiple of 32 but not of 64), and the
+// second half is then loaded from the first half's address and must be
+// dropped with mask().  The loads are unconditional and nothing reads their
+// registers until the weights are used, so a ring of them stays in flight.
+// mask(v, full) zeroes the span unless v, and its second half unless full
+// (selects; called at the point of use).  widen(u) gives weights
+// [16 u, 16 u + 16) of the span as bf16 (u < kLaneK / 16).  load16(row, k,
+// srow) loads only weights [k, k + 16) (k a multiple of 16), as sub-group 0.
 template <typename WQ> struct WRaw;
 template <> struct WRaw<bf16> {
   W16 f;
-  __device__ __forceinline__ void load(const bf16* row, int k, const uint8_t*) {
+  __device__ __forceinline__ void load(const bf16* row, int k, const uint8_t*, bool) {
     const uint4* q = reinterpret_cast<const uint4*>(row + k);
     f.u[0] = q[0];
     f.u[1] = q[1];
   }
-  __device__ __forceinline__ void zero() { f.u[0] = f.u[1] = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ W16 widen() const { return f; }
+  __device__ __forceinline__ void load16(const bf16* row, int k, const uint8_t* srow) {
+    load(row, k, srow, true);
+  }
+  __device__ __forceinline__ void mask(bool v, bool) {
+    f.u[0] = keep4(f.u[0], v);
+    f.u[1] = keep4(f.u[1], v);
+  }
+  __device__ __forceinline__ W16 widen(int) const { return f; }
 };
 template <> struct WRaw<int8_t> {
-  uint4 u;
-  __device__ __forceinline__ void load(const int8_t* row, int k, const uint8_t*) {
-    u = *reinterpret_cast<const uint4*>(row + k);
+  uint4 q[2];
+  __device__ __forceinline__ void load(const int8_t* row, int k, const uint8_t*, bool) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + k);
+    q[0] = p[0];
+    q[1] = p[1];
   }
-  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ W16 widen() const {
+  __device__ __forceinline__ void load16(const int8_t* row, int k, const uint8_t*) {
+    q[0] = *reinterpret_cast<const uint4*>(row + k);
+  }
+  __device__ __forceinline__ void mask(bool v, bool) {
+    q[0] = keep4(q[0], v);
+    q[1] = keep4(q[1], v);
+  }
+  __device__ __forceinline__ W16 widen(int u) const {
     W16 f;
-    int8x4_to_bf16(u.x, f.u[0].x, f.u[0].y);
-    int8x4_to_bf16(u.y, f.u[0].z, f.u[0].w);
-    int8x4_to_bf16(u.z, f.u[1].x, f.u[1].y);
-    int8x4_to_bf16(u.w, f.u[1].z, f.u[1].w);
+    int8x4_to_bf16(q[u].x, f.u[0].x, f.u[0].y);
+    int8x4_to_bf16(q[u].y, f.u[0].z, f.u[0].w);
+    int8x4_to_bf16(q[u].z, f.u[1].x, f.u[1].y);
+    int8x4_to_bf16(q[u].w, f.u[1].z, f.u[1].w);
     return f;
   }
 };
 template <> struct WRaw<fp8e4m3> {
-  uint4 u;
-  __device__ __forceinline__ void load(const fp8e4m3* row, int k, const uint8_t*) {
-    u = *reinterpret_cast<const uint4*>(row + k);
+  uint4 q[2];
+  __device__ __forceinline__ void load(const fp8e4m3* row, int k, const uint8_t*, bool) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + k);
+    q[0] = p[0];
+    q[1] = p[1];
   }
-  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ W16 widen() const {
+  __device__ __forceinline__ void load16(const fp8e4m3* row, int k, const uint8_t*) {
+    q[0] = *reinterpret_cast<const uint4*>(row + k);
+  }
+  __device__ __forceinline__ void mask(bool v, bool) {
+    q[0] = keep4(q[0], v);
+    q[1] = keep4(q[1], v);
+  }
+  __device__ __forceinline__ W16 widen(int u) const {
     W16 f;
-    fp8x4_to_bf16(u.x, f.u[0].x, f.u[0].y);
-    fp8x4_to_bf16(u.y, f.u[0].z, f.u[0].w);
-    fp8x4_to_bf16(u.z, f.u[1].x, f.u[1].y);
-    fp8x4_to_bf16(u.w, f.u[1].z, f.u[1].w);
+    fp8x4_to_bf16(q[u].x, f.u[0].x, f.u[0].y);
+    fp8x4_to_bf16(q[u].y, f.u[0].z, f.u[0].w);
+    fp8x4_to_bf16(q[u].z, f.u[1].x, f.u[1].y);
+    fp8x4_to_bf16(q[u].w, f.u[1].z, f.u[1].w);
     return f;
   }
 };
 template <> struct WRaw<fp4x2> {
-  uint2 u;
-  float scale;
-  __device__ __forceinline__ void load(const fp4x2* row, int k, const uint8_t* srow) {
-    u = *reinterpret_cast<const uint2*>(row + k / 2);
-    scale = e8m0_to_f32(srow[k / 32]);
+  uint4 q[2];
+  float scale[2];  // of weights [0, 32) and [32, 64) of the span
+  __device__ __forceinline__ void load(const fp4x2* row, int k, const uint8_t* srow, bool full) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + k / 2);
+    const int h = full ? 1 : 0;  // the second half re-reads the first when past the end
+    q[0] = p[0];
+    q[1] = p[h];
+    scale[0] = e8m0_to_f32(srow[k / 32]);
+    scale[1] = e8m0_to_f32(srow[k / 32 + h]);
   }
-  __device__ __forceinline__ void zero() {
-    u = make_uint2(0, 0);
-    scale = 1.0f;
+  __device__ __forceinline__ void mask(bool v, bool full) {
+    q[0] = keep4(q[0], v);
+    q[1] = keep4(q[1], v && full);
   }
-  __device__ __forceinline__ W16 widen() const {
+  __device__ __forceinline__ void load16(const fp4x2* row, int k, const uint8_t* srow) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + k / 2);
+    q[0] = make_uint4(w.x, w.y, 0, 0);
+    scale[0] = e8m0_to_f32(srow[k / 32]);
+  }
+  __device__ __forceinline__ W16 widen(int u) const {
+    const uint4& w = q[u / 2];
+    const uint32_t lo = (u & 1) ? w.z : w.x, hi = (u & 1) ? w.w : w.y;
     W16 f;
     uint32_t o[4];
-    fp4x8_to_bf16(u.x, scale, o);
+    fp4x8_to_bf16(lo, scale[u / 2], o);
     f.u[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    fp4x8_to_bf16(u.y, scale, o);
+    fp4x8_to_bf16(hi, scale[u / 2], o);
     f.u[1] = make_uint4(o[0], o[1], o[2], o[3]);
     return f;
   }
