@@ -302,10 +302,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
   }
 }
 
-// Configurations (256-row tiles): gate_up 8 waves (4 x 2), 5 stages; down 16
-// waves (4 x 4), 4 stages.  128-row tiles measured slower on every shape
-// tried (groups of ~128 rows at 2048 tokens included): the per-barrier MFMA
-// count halves, and weights are read from HBM once per tile either way.
+// Configurations (256-row tiles): gate_up and down both 16 waves (4 x 4), 4
+// stages.  gate_up with 8 waves (4 x 2) and 5 stages was 3-6% slower (4096
+// skewed, 2048 and 8192 tokens): with 16 waves a partial row tile still keeps
+// one wave on every SIMD.  128-row tiles measured slower on every shape tried
+// (groups of ~128 rows at 2048 tokens included): the per-barrier MFMA count
+// halves, and weights are read from HBM once per tile either way.
 
 // ---------------------------------------------------------------------------
 // fp32 kernels (debug path)
@@ -458,7 +460,7 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
     const bf16* wg = static_cast<const bf16*>(a.w_gate);
     const bf16* wu = static_cast<const bf16*>(a.w_up);
     bf16* h = static_cast<bf16*>(a.h);
-    const hipError_t e = launch_grouped<true, 256, 4, 2, 5, float>(
+    const hipError_t e = launch_grouped<true, 256, 4, 4, 4, float>(
           a.H, a.N, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
           x, wg, wu, a.w_stride, a.offsets, a.sorted_slots, nullptr, h, nullptr, s);
     if (e != hipSuccess) return e;
