@@ -58,6 +58,20 @@ __device__ __forceinline__ bool get_row_tile(bool ident, int rows, const int32_t
 constexpr int GN = 256, GK = 32;
 template <int BM>
 constexpr int stage_bytes() { return (BM + GN) * GK * 2; }
+// Epilogue staging (the ring's LDS, free after the main loop): down stages
+// 128 rows x 256 fp32 per pass, gate_up all BM rows x 128 bf16 at once; rows
+// are padded by 16 B.  The down tile's row slots and weights sit past both.
+constexpr int kDnStageRows = 128, kDnStride = GN + 4;     // floats
+constexpr int kGuStride = GN / 2 + 8;                     // bf16
+template <bool GU, int BM, int NSTAGE>
+constexpr int slots_offset() {
+  return NSTAGE * stage_bytes<BM>() > kDnStageRows * kDnStride * 4 ? NSTAGE * stage_bytes<BM>()
+                                                                    : kDnStageRows * kDnStride * 4;
+}
+template <bool GU, int BM, int NSTAGE>
+constexpr int gemm_lds_bytes() {
+  return GU ? NSTAGE * stage_bytes<BM>() : slots_offset<GU, BM, NSTAGE>() + BM * 8;
+}
 
 __device__ __forceinline__ int gswz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
@@ -85,7 +99,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
   constexpr int NF = TM + TN, NMF = TM * TN;
   static_assert(LPW * NW * 16 == ROWS && NF <= NMF && LPW <= NMF, "tile shape");
   static_assert(!GU || TN % 2 == 0, "gate_up waves need gate/up column pairs");
-  static_assert(NSTAGE >= 3 && NSTAGE * SB + (GU ? 0 : BM * 8) <= 160 * 1024, "LDS");
+  static_assert(NSTAGE >= 3 && gemm_lds_bytes<GU, BM, NSTAGE>() <= 160 * 1024, "LDS");
+  static_assert(!GU || BM * kGuStride * 2 <= NSTAGE * SB, "gate_up staging fits the ring");
+  static_assert(GU || BM % kDnStageRows == 0, "down staging passes");
+  static_assert((BM * (GN / 16)) % (64 * NW) == 0 && (kDnStageRows * (GN / 4)) % (64 * NW) == 0,
+                "epilogue store loops cover the staged rows exactly");
   extern __shared__ __align__(16) unsigned char smem[];
 
   int e = 0, row0, row1, nt;
@@ -114,7 +132,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
   const int nbase = GU ? nt * (GN / 2) : nt * GN;
   // down: output slot and routing weight of each of the tile's rows, fetched
   // now (behind the main loop) into LDS past the ring, for the epilogue
-  int* row_slot = reinterpret_cast<int*>(smem + NSTAGE * SB);
+  int* row_slot = reinterpret_cast<int*>(smem + slots_offset<GU, BM, NSTAGE>());
   float* row_w = reinterpret_cast<float*>(row_slot + BM);
   if constexpr (!GU) {
     if (threadIdx.x < BM) {
@@ -267,8 +285,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
   else
     mainloop(std::false_type{});
 
+  // Epilogue through LDS: the accumulators go to a row-major staging tile
+  // in the ring's LDS, then whole rows leave in 16-B stores (the accumulator
+  // layout alone gives 2- or 4-B stores scattered over two rows each; those
+  // took ~10% of gate_up's and ~20% of down's time).
+  __syncthreads();  // every wave is done with the ring
+  const int tid = threadIdx.x;
+  constexpr int NT_ = 64 * NW;
   if constexpr (GU) {
     constexpr int half = TN / 2;
+    bf16* stg = reinterpret_cast<bf16*>(smem);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= nv) break;
@@ -276,28 +302,64 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
       for (int j = 0; j < half; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int row = row0 + wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
-          const int col = nbase + wn * (WC / 2) + j * 32 + fr;
-          if (row < row1 && col < Nout)
-            hout[(size_t)row * Nout + col] = (bf16)(gelu_tanh(acc[i][j][q]) * acc[i][j + half][q]);
+          const int r = wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
+          const int c = wn * (WC / 2) + j * 32 + fr;
+          stg[r * kGuStride + c] = (bf16)(gelu_tanh(acc[i][j][q]) * acc[i][j + half][q]);
         }
     }
+    __syncthreads();
+    // BM rows x 16 chunks of 8 bf16; Nout is a multiple of 32, so a chunk is
+    // wholly inside or past the last column.
+    constexpr int CH = (GN / 2) / 8;
+#pragma unroll
+    for (int it = 0; it < BM * CH / NT_; ++it) {
+      const int k = tid + it * NT_;
+      const int r = k / CH, ch = k % CH;
+      const int col = nbase + ch * 8;
+      if (row0 + r < row1 && col < Nout)
+        *reinterpret_cast<uint4*>(hout + (size_t)(row0 + r) * Nout + col) =
+            *reinterpret_cast<const uint4*>(stg + r * kGuStride + ch * 8);
+    }
   } else {
+    float* stg = reinterpret_cast<float*>(smem);
+    constexpr int CH = GN / 4;  // chunks of 4 fp32 per row
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i >= nv) break;
+    for (int pass = 0; pass < BM / kDnStageRows; ++pass) {
+      if (wm * WR / kDnStageRows == pass) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = wm * WR + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
-        if (row0 + r >= row1) continue;
-        const int slot = row_slot[r];
-        const float sc = row_w[r];
+        for (int i = 0; i < TM; ++i) {
+          if (i >= nv) break;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = nbase + wn * WC + j * 32 + fr;
-          if (col < Nout) yout[(size_t)slot * Nout + col] = from_f32<YT>(sc * acc[i][j][q]);
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm * WR - pass * kDnStageRows + i * 32 + 8 * (q / 4) + 4 * fq + (q % 4);
+              stg[r * kDnStride + wn * WC + j * 32 + fr] = acc[i][j][q];
+            }
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < kDnStageRows * CH / NT_; ++it) {
+        const int k = tid + it * NT_;
+        const int rl = k / CH, ch = k % CH;
+        const int r = pass * kDnStageRows + rl;
+        const int col = nbase + ch * 4;
+        if (row0 + r < row1 && col < Nout) {
+          const float sc = row_w[r];
+          const float4 v = *reinterpret_cast<const float4*>(stg + rl * kDnStride + ch * 4);
+          YT* dst = yout + (size_t)row_slot[r] * Nout + col;
+          if constexpr (std::is_same<YT, float>::value) {
+            *reinterpret_cast<float4*>(dst) = make_float4(sc * v.x, sc * v.y, sc * v.z, sc * v.w);
+          } else {
+            dst[0] = from_f32<YT>(sc * v.x);
+            dst[1] = from_f32<YT>(sc * v.y);
+            dst[2] = from_f32<YT>(sc * v.z);
+            dst[3] = from_f32<YT>(sc * v.w);
+          }
+        }
+      }
+      __syncthreads();
     }
   }
 }
@@ -428,7 +490,7 @@ hipError_t launch_grouped(int Kd, int Nout, int E, int K, int rows, bool ident, 
                           const int32_t* offsets, const int32_t* sorted_slots,
                           const float* topk_w, bf16* hout, YT* yout, hipStream_t s) {
   auto kf = grouped_gemm_kernel<GU, BM, WM, WN, NSTAGE, YT>;
-  const int lds = NSTAGE * stage_bytes<BM>() + (GU ? 0 : BM * 8);  // ring (+ row slots, weights)
+  const int lds = gemm_lds_bytes<GU, BM, NSTAGE>();  // ring or staging (+ row slots, weights)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
