@@ -52,6 +52,7 @@ ROUTER_BYTES = E * H * 4 + H * 4 + E * 4
 KERNEL_SRC = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc", "expert_stream.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_decode_b64_traffic.txt")
 SEGMENTS = ("route", "gate_up", "down", "combine")
+GATE_UP_SAMPLE = 5  # the timed region times gate_up on every 5th step
 D = 2112                          # dense MLP width of the block
 DENSE_BYTES = 3 * D * H * 2       # dense gate, up, down, bf16
 LAYERS = 30
@@ -111,7 +112,12 @@ class Workload:
 
 
 class Runner:
-    """Buffers for one batch size and the per-step call sequence."""
+    """Buffers for one batch size and the per-step call sequence.  Events 1
+    and 2 of a step (gate_up's start and end) are recorded by the gate_up
+    kernel's own dispatch (moe_expert_gate_up_timed), so they put no packets
+    between the launches."""
+
+    timed_gate_up = True
 
     def __init__(self, wl: Workload, T: int):
         torch, lib = wl.torch, wl.lib
@@ -135,9 +141,11 @@ class Runner:
         rec(0)
         lib.moe_route(d, T, x, rw, rs, pes, None, self.idx, self.w, self.counts, self.offsets,
                       self.sorted, self.ws)
-        rec(1)
-        lib.moe_expert_gate_up(d, T, x, gu, self.offsets, self.sorted, self.h)
-        rec(2)
+        if ev is not None and ev[1] is not None and ev[2] is not None:
+            lib.moe_expert_gate_up_timed(d, T, x, gu, self.offsets, self.sorted, self.h, ev[1],
+                                         ev[2])
+        else:
+            lib.moe_expert_gate_up(d, T, x, gu, self.offsets, self.sorted, self.h)
         lib.moe_expert_down(d, T, self.h, dn, self.w, self.offsets, self.sorted, self.y)
         rec(3)
         lib.moe_combine(d, T, self.y, None, self.out)
@@ -147,16 +155,27 @@ class Runner:
 def time_steps(torch, runner, xs, copies, steps, warmup, leg=None):
     """Warm-up, then `steps` timed steps, then `steps` instrumented steps.
 
-    The timed region holds HIP events only around the gate_up launch (the
-    roofline kernel); an event between every launch costs the step several
-    microseconds, so the per-segment times come from the instrumented pass
-    that follows it.  Returns (ms per step, per-segment ms with gate_up from
-    the timed region, pairs of input / weight copy used in the timed region)."""
+    The timed region's only HIP events, besides the two around the whole
+    region, are gate_up's start and end (the roofline kernel) on every
+    GATE_UP_SAMPLE-th step, recorded by the kernel's own dispatch when the
+    runner supports it.  Any event attached to a launch leaves the GPU idle
+    around it (~6.5 us before gate_up and ~4.6 us after it in the kernel
+    trace, against none between unrecorded launches), so recording every step
+    would understate the step rate by ~4%.  The other segments' times come
+    from the instrumented pass that follows.  Returns (ms per step,
+    per-segment ms with gate_up from the timed region's sampled launches when
+    the runner times it there, pairs of input / weight copy used in the timed
+    region)."""
     n_ev = len(SEGMENTS) + 1
+    timed = getattr(runner, "timed_gate_up", False)
     for i in range(warmup):
         runner.step(xs[i % len(xs)], copies[i % len(copies)])
     torch.cuda.synchronize()
     gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for e in [e for row in gev + events for e in row]:
+        e.record()  # torch creates an event at its first record
+    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pairs = []
     t0 = time.perf_counter()
@@ -164,32 +183,35 @@ def time_steps(torch, runner, xs, copies, steps, warmup, leg=None):
     for i in range(steps):
         j = warmup + i
         pairs.append((j % len(xs), j % len(copies)))
-        runner.step(xs[j % len(xs)], copies[j % len(copies)], [None, gev[i][0], gev[i][1]] +
-                    [None] * (n_ev - 3))
+        sampled = timed and i % GATE_UP_SAMPLE == 0
+        runner.step(xs[j % len(xs)], copies[j % len(copies)],
+                    [None, gev[i][0], gev[i][1]] + [None] * (n_ev - 3) if sampled else None)
     end.record()
     torch.cuda.synchronize()
     if leg is not None:
         WINDOWS[leg] = (t0, time.perf_counter())
     total = start.elapsed_time(end)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     for i in range(steps):
         j = warmup + steps + i
         runner.step(xs[j % len(xs)], copies[j % len(copies)], events[i])
     torch.cuda.synchronize()
     seg = {name: sum(events[i][s].elapsed_time(events[i][s + 1]) for i in range(steps)) / steps
            for s, name in enumerate(SEGMENTS)}
-    seg["gate_up"] = sum(g[0].elapsed_time(g[1]) for g in gev) / steps
+    if timed:
+        samp = [g[0].elapsed_time(g[1]) for i, g in enumerate(gev) if i % GATE_UP_SAMPLE == 0]
+        seg["gate_up"] = sum(samp) / len(samp)
     return total / steps, seg, pairs
 
 
 def distinct_experts(torch, runner, xs, copies, pairs):
-    """Average number of distinct experts a step touches (from its routing)."""
-    us = []
+    """Average over the given steps (pairs of input / weight copy) of the
+    number of distinct experts a step touches (from its routing)."""
+    u = {}
     for xi, ci in sorted(set(pairs)):
         runner.step(xs[xi], copies[ci])
         torch.cuda.synchronize()
-        us.append(int((runner.counts > 0).sum().item()))
-    return sum(us) / len(us)
+        u[(xi, ci)] = int((runner.counts > 0).sum().item())
+    return sum(u[p] for p in pairs) / len(pairs)
 
 
 def decode_measure(torch, wl, T, steps, warmup, xbatches, seed):
@@ -197,11 +219,13 @@ def decode_measure(torch, wl, T, steps, warmup, xbatches, seed):
     xs = wl.batches(T, xbatches, seed)
     ms, seg, pairs = time_steps(torch, runner, xs, wl.copies, steps, warmup, f"decode_{T}")
     U = distinct_experts(torch, runner, xs, wl.copies, pairs)
-    gate_up_bytes = U * GATE_UP_BYTES + T * H * 2
+    # the gate_up launches timed are those of every GATE_UP_SAMPLE-th step
+    U_timed = distinct_experts(torch, runner, xs, wl.copies, pairs[::GATE_UP_SAMPLE])
+    gate_up_bytes = U_timed * GATE_UP_BYTES + T * H * 2
     step_bytes = U * (GATE_UP_BYTES + DOWN_BYTES) + ROUTER_BYTES + 2 * T * H * 2
     return {
         "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-        "distinct_experts": U, "kernel_ms": seg,
+        "distinct_experts": U, "distinct_experts_gate_up_timed": U_timed, "kernel_ms": seg,
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "gate_up_gbs": gate_up_bytes / (seg["gate_up"] * 1e-3) / 1e9,
         "gate_up_bytes": gate_up_bytes,

@@ -209,6 +209,20 @@ int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* 
                     const float* topk_w, const int32_t* expert_offsets,
                     const int32_t* sorted_slots, void* y_slots, void* stream);
 
+/* moe_expert_gate_up with its kernel timed: start_event and stop_event
+ * (hipEvent_t, created by the caller with timing enabled, not NULL) are
+ * recorded by the gate_up kernel's own dispatch (HIP's extended launch) when
+ * it starts and ends, so hipEventElapsedTime(start, stop) is that kernel's
+ * duration and no event packets sit between the stream's launches (a
+ * hipEventRecord pair around a launch holds back the next dispatch until the
+ * previous kernel has finished, ~5 us per record on MI355X).  Same result as
+ * moe_expert_gate_up, bit for bit.  T == 0 launches nothing and leaves the
+ * events untouched. */
+int moe_expert_gate_up_timed(const moe_dims* dims, int32_t T, const void* x,
+                             const void* w_gate_up, const int32_t* expert_offsets,
+                             const int32_t* sorted_slots, void* h, void* stream,
+                             void* start_event, void* stop_event);
+
 /* int8 per-channel symmetric weights, the int8-expert variant on the page
  * "Porting a 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section
  * "Can it run on a smaller box? Yes, no, and "deeper than it looks"".

@@ -488,15 +488,16 @@ template <bool GU, int BM, int WM, int WN, int NSTAGE, typename YT>
 hipError_t launch_grouped(int Kd, int Nout, int E, int K, int rows, bool ident, int RT, int NT,
                           const bf16* A, const bf16* W0, const bf16* W1, long long w_stride,
                           const int32_t* offsets, const int32_t* sorted_slots,
-                          const float* topk_w, bf16* hout, YT* yout, hipStream_t s) {
+                          const float* topk_w, bf16* hout, YT* yout, hipStream_t s,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   auto kf = grouped_gemm_kernel<GU, BM, WM, WN, NSTAGE, YT>;
   const int lds = gemm_lds_bytes<GU, BM, NSTAGE>();  // ring or staging (+ row slots, weights)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kf), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kf, dim3(RT * NT), dim3(64 * WM * WN), lds, s, Kd, Nout, E, K, rows,
-                     (int)ident, NT, A, W0, W1, w_stride, offsets, sorted_slots, topk_w, hout,
-                     yout);
+  launch_maybe_timed(kf, dim3(RT * NT), dim3(64 * WM * WN), lds, s, ev_start, ev_stop, Kd, Nout, E,
+                     K, rows, (int)ident, NT, A, W0, W1, w_stride, offsets, sorted_slots, topk_w,
+                     hout, yout);
   return hipSuccess;
 }
 
@@ -524,12 +525,13 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
     bf16* h = static_cast<bf16*>(a.h);
     const hipError_t e = launch_grouped<true, 256, 4, 4, 4, float>(
           a.H, a.N, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
-          x, wg, wu, a.w_stride, a.offsets, a.sorted_slots, nullptr, h, nullptr, s);
+          x, wg, wu, a.w_stride, a.offsets, a.sorted_slots, nullptr, h, nullptr, s, a.ev_start,
+          a.ev_stop);
     if (e != hipSuccess) return e;
   } else {
     dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.N + kFT - 1) / kFT);
-    hipLaunchKernelGGL(gate_up_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.K, a.rows,
-                       (int)a.ident, static_cast<const float*>(a.x),
+    launch_maybe_timed(gate_up_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, a.H, a.N,
+                       a.E, a.K, a.rows, (int)a.ident, static_cast<const float*>(a.x),
                        static_cast<const float*>(a.w_gate), static_cast<const float*>(a.w_up),
                        a.w_stride, a.offsets, a.sorted_slots, static_cast<float*>(a.h));
   }

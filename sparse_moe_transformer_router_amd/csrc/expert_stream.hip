@@ -428,11 +428,11 @@ template <typename WQ, int WK, int MB, int NS, int NC>
 void launch_gu(const GateUpArgs& a, hipStream_t s) {
   const long long cgs = (a.N + 16 * NC - 1) / (16 * NC);
   dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
-  hipLaunchKernelGGL((gate_up_stream_kernel<WQ, WK, MB, NS, NC>), grid, dim3(64 * WK), 0, s, a.H,
-                     a.N, a.E, a.K, a.rows, (int)a.ident, static_cast<const bf16*>(a.x),
-                     static_cast<const WQ*>(a.w_gate), static_cast<const WQ*>(a.w_up), a.w_stride,
-                     a.s_gate, a.s_up, a.s_stride, a.offsets, a.sorted_slots,
-                     static_cast<bf16*>(a.h));
+  launch_maybe_timed(gate_up_stream_kernel<WQ, WK, MB, NS, NC>, grid, dim3(64 * WK), 0, s,
+                     a.ev_start, a.ev_stop, a.H, a.N, a.E, a.K, a.rows, (int)a.ident,
+                     static_cast<const bf16*>(a.x), static_cast<const WQ*>(a.w_gate),
+                     static_cast<const WQ*>(a.w_up), a.w_stride, a.s_gate, a.s_up, a.s_stride,
+                     a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
 }
 
 template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>

@@ -3,6 +3,7 @@
 // by the C ABI layer before any launcher is called.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,8 +80,23 @@ struct GateUpArgs {
   const void* s_gate;
   const void* s_up;
   long long s_stride;
+  // Optional events recorded by the kernel's own dispatch packet (extended
+  // launch) at its start and end; null: none.
+  hipEvent_t ev_start, ev_stop;
 };
 hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s);
+
+// Launches kernel f like hipLaunchKernelGGL, or with the extended launch
+// when either event is set, so that the events time exactly that kernel
+// without packets of their own between launches.
+template <typename F, typename... Args>
+inline void launch_maybe_timed(F f, dim3 grid, dim3 block, unsigned shmem, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+  if (ev_start != nullptr || ev_stop != nullptr)
+    hipExtLaunchKernelGGL(f, grid, block, shmem, s, ev_start, ev_stop, 0, args...);
+  else
+    hipLaunchKernelGGL(f, grid, block, shmem, s, args...);
+}
 
 // Down projection of the gated rows; row r of group e goes to output row
 // sorted_slots[r] (or r when ident), scaled by topk_w of that slot (1 when

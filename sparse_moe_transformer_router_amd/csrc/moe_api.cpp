@@ -206,7 +206,8 @@ int run_dispatch(const moe_dims* d, int32_t T, const int32_t* idx, int32_t* coun
 }
 
 int run_gate_up(const moe_dims* d, int32_t T, const void* x, const void* w_gate_up,
-                const int32_t* offsets, const int32_t* sorted, void* h, hipStream_t s) {
+                const int32_t* offsets, const int32_t* sorted, void* h, hipStream_t s,
+                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   const size_t act = dtype_size(d->act_dtype);
   const long long H = d->hidden, I = d->expert_inter;
   moe::GateUpArgs g{};
@@ -217,6 +218,7 @@ int run_gate_up(const moe_dims* d, int32_t T, const void* x, const void* w_gate_
   g.w_up = static_cast<const char*>(w_gate_up) + act * I * H;
   g.w_stride = 2 * I * H;
   g.offsets = offsets; g.sorted_slots = sorted; g.h = h;
+  g.ev_start = ev_start; g.ev_stop = ev_stop;
   hipError_t e = moe::launch_gate_up(g, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert gate_up");
 }
@@ -494,6 +496,22 @@ int moe_expert_gate_up(const moe_dims* dims, int32_t T, const void* x, const voi
   REQUIRE_PTR(sorted_slots); REQUIRE_PTR(h);
   return run_gate_up(dims, T, x, w_gate_up, expert_offsets, sorted_slots, h,
                      static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_gate_up_timed(const moe_dims* dims, int32_t T, const void* x,
+                             const void* w_gate_up, const int32_t* expert_offsets,
+                             const int32_t* sorted_slots, void* h, void* stream,
+                             void* start_event, void* stop_event) {
+  int rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (!start_event || !stop_event) return fail(MOE_ERR_ARG, "start_event and stop_event are required");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(h);
+  return run_gate_up(dims, T, x, w_gate_up, expert_offsets, sorted_slots, h,
+                     static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                     static_cast<hipEvent_t>(stop_event));
 }
 
 int moe_expert_down(const moe_dims* dims, int32_t T, const void* h, const void* w_down,

@@ -59,6 +59,7 @@ def _load():
     L.moe_expert_ffn.argtypes = [D, I32] + [P] * 8 + [SZ, P]
     L.moe_dense_mask_dispatch.argtypes = [D, I32] + [P] * 6
     L.moe_expert_gate_up.argtypes = [D, I32] + [P] * 6
+    L.moe_expert_gate_up_timed.argtypes = [D, I32] + [P] * 8
     L.moe_expert_down.argtypes = [D, I32] + [P] * 7
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
@@ -72,7 +73,7 @@ def _load():
     for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
               "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch",
-              "moe_quantize", "moe_dequantize", "moe_expert_ffn_q"):
+              "moe_quantize", "moe_dequantize", "moe_expert_ffn_q", "moe_expert_gate_up_timed"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -204,6 +205,20 @@ def moe_expert_ffn_q(d, fmt, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_dow
 def moe_expert_gate_up(d, T, x, w_gate_up, offsets, sorted_slots, h, stream=None):
     _check(_lib.moe_expert_gate_up(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up), _ptr(offsets),
                                    _ptr(sorted_slots), _ptr(h), _stream(stream)))
+
+
+def moe_expert_gate_up_timed(d, T, x, w_gate_up, offsets, sorted_slots, h, start, stop,
+                             stream=None):
+    """moe_expert_gate_up recording torch.cuda.Event start / stop on the
+    kernel's own dispatch; both events must have been recorded once before
+    (torch creates its events at their first record)."""
+    hs, he = start.cuda_event, stop.cuda_event
+    if not hs or not he:
+        raise RuntimeError("moe_expert_gate_up_timed: record both events once before use")
+    _check(_lib.moe_expert_gate_up_timed(ctypes.byref(d), T, _ptr(x), _ptr(w_gate_up),
+                                         _ptr(offsets), _ptr(sorted_slots), _ptr(h),
+                                         _stream(stream), ctypes.c_void_p(hs),
+                                         ctypes.c_void_p(he)))
 
 
 def moe_expert_down(d, T, h, w_down, topk_w, offsets, sorted_slots, y_slots, stream=None):

@@ -226,3 +226,16 @@ def test_quantized_format_entry_points_validate_on_the_host():
     d32 = D(act=lib_mod.MOE_F32)
     assert ffn(ctypes.byref(d32), F8, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     assert ffn(ctypes.byref(d), MX, 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
+
+
+def test_timed_gate_up_requires_both_events():
+    d = D()
+    for ev in ((None, FAKE), (FAKE, None), (None, None)):
+        assert L.moe_expert_gate_up_timed(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          *ev) == lib_mod.MOE_ERR_ARG
+        assert "event" in lib_mod.last_error()
+    # argument checks of moe_expert_gate_up come first
+    assert L.moe_expert_gate_up_timed(ctypes.byref(D(hidden=100)), 4, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, None, FAKE, FAKE) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_gate_up_timed(ctypes.byref(d), 4, MISALIGNED, FAKE, FAKE, FAKE, FAKE,
+                                      None, FAKE, FAKE) == lib_mod.MOE_ERR_ARG
