@@ -274,8 +274,12 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
 }
 
 // down: one block = one row tile x WN waves of NC groups of 16 output
-// columns; WK waves split the contraction (the intermediate width N).
-template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>
+// columns; WK waves split the contraction (the intermediate width N).  With
+// AL the tile's activation rows (at most 16 * MB rows of h) are staged once
+// in LDS (dynamic, rows padded by 16 B) and every wave reads its fragments
+// there: the WN waves of a block share the same rows and k range, and a
+// lane's activation loads were as large as its weight loads.
+template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT, bool AL>
 __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     int H, int N, int E, int rows, int ident, const bf16* __restrict__ hbuf,
     const WQ* __restrict__ wd, long long w_stride, const void* __restrict__ sd,
@@ -313,11 +317,16 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       bsr[c] = ssc + min(16 * (wn * NC + c) + fr, H - 1 - cg * 16 * WN * NC) * (N / 32);
   }
   const int nmb = (row1 - row0 + 15) / 16;
+  extern __shared__ __align__(16) unsigned char dyn_lds[];
+  const int ALS = N + 8;  // staged row pitch (bf16)
   const bf16* ap[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = row0 + 16 * mb + fr;
-    ap[mb] = hbuf + (size_t)(r < row1 ? r : row0) * N;
+    if constexpr (AL)
+      ap[mb] = reinterpret_cast<const bf16*>(dyn_lds) + (r < row1 ? r - row0 : 0) * ALS;
+    else
+      ap[mb] = hbuf + (size_t)(r < row1 ? r : row0) * N;
   }
   const int KB = (N + KBK - 1) / KBK;
   const int kb0 = wk * KB / WK, kb1 = (wk + 1) * KB / WK;
@@ -329,13 +338,17 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     for (int c = 0; c < NC; ++c) acc[mb][c] = f32x4{0, 0, 0, 0};
   WRaw<WQ> bb[NS][NC];
   Frag ba[NS][MB][U];
-  auto load = [&](int kb, int slot) {
+  auto load_w = [&](int kb, int slot) {
     const int ks = kb * KBK + LK * fg;  // first weight of this lane's span
     const bool kv = ks < N;
     const int kc = kv ? ks : 0;              // in-bounds start
     const bool kfull = kc + LK <= N;       // else only its first half lies inside
 #pragma unroll
     for (int c = 0; c < NC; ++c) bb[slot][c].load(wrow(wd, wel[c]), kc, bsr[c], kfull);
+  };
+  auto load_a = [&](int kb, int slot) {
+    const int ks = kb * KBK + LK * fg;
+    const int kc = ks < N ? ks : 0;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       if (mb == 0 || mb < nmb)
@@ -344,6 +357,10 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
           const int ku = kc + 16 * u;
           ld_frag(ba[slot][mb][u], ap[mb] + (ku < N ? ku : 0));
         }
+  };
+  auto load = [&](int kb, int slot) {
+    load_w(kb, slot);
+    load_a(kb, slot);
   };
   // The same steady state and tail as gate_up.
   auto steps = [&](int kb, auto tail) {
@@ -371,9 +388,23 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
         }
     }
   };
+  // the first k-blocks' weight loads go out before the activation staging
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (kb0 + s < kb1) load(kb0 + s, s);
+    if (kb0 + s < kb1) load_w(kb0 + s, s);
+  if constexpr (AL) {
+    const int nrows = row1 - row0, cpr = N / 8;  // 16-B chunks per row
+    bf16* al = reinterpret_cast<bf16*>(dyn_lds);
+    for (int i = threadIdx.x; i < nrows * cpr; i += blockDim.x) {
+      const int r = i / cpr, ch = i % cpr;
+      *reinterpret_cast<uint4*>(al + r * ALS + ch * 8) =
+          *reinterpret_cast<const uint4*>(hbuf + (size_t)(row0 + r) * N + ch * 8);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (kb0 + s < kb1) load_a(kb0 + s, s);
   int kb = kb0;
   for (; kb + 2 * NS - 2 < kb1; kb += NS) steps(kb, std::false_type{});
   for (; kb < kb1; kb += NS) steps(kb, std::true_type{});
@@ -435,14 +466,33 @@ void launch_gu(const GateUpArgs& a, hipStream_t s) {
                      a.offsets, a.sorted_slots, static_cast<bf16*>(a.h));
 }
 
+// Activation rows of a down tile staged in LDS while they and the block's
+// staged MXFP4 scales take at most this many bytes (the 26B-A4B experts: 16
+// rows x 712 bf16 = 22.8 KB; MXFP4's 32 KB of scales leave it out, since
+// fewer blocks per CU made it slower), above 8 tokens: at 64 tokens bf16
+// down went 102 -> 97 us; at 8 tokens the staging's fixed cost made it
+// slower (40 -> 44 us).
+constexpr int kDnActLdsMax = 32 * 1024;
+constexpr int kDnActLdsMinTokens = 9;
+
 template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>
 void launch_dn(const DownArgs& a, hipStream_t s) {
   const long long cgs = (a.H + 16 * WN * NC - 1) / (16 * WN * NC);
   dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
-  hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, NC, YT>), grid, dim3(64 * WN * WK), 0,
-                     s, a.H, a.N, a.E, a.rows, (int)a.ident, static_cast<const bf16*>(a.h),
-                     static_cast<const WQ*>(a.w_down), a.w_stride, a.s_down, a.s_stride,
-                     a.offsets, a.sorted_slots, a.topk_w, static_cast<YT*>(a.y));
+  const int al = 16 * MB * (a.N + 8) * 2;
+  const int scales = WFmt<WQ>::kBlockScale ? 16 * WN * NC * kMaxScaleRow : 0;
+  if (al + scales <= kDnActLdsMax && a.T >= kDnActLdsMinTokens)
+    hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, NC, YT, true>), grid,
+                       dim3(64 * WN * WK), al, s, a.H, a.N, a.E, a.rows, (int)a.ident,
+                       static_cast<const bf16*>(a.h), static_cast<const WQ*>(a.w_down),
+                       a.w_stride, a.s_down, a.s_stride, a.offsets, a.sorted_slots, a.topk_w,
+                       static_cast<YT*>(a.y));
+  else
+    hipLaunchKernelGGL((down_stream_kernel<WQ, WN, WK, MB, NS, NC, YT, false>), grid,
+                       dim3(64 * WN * WK), 0, s, a.H, a.N, a.E, a.rows, (int)a.ident,
+                       static_cast<const bf16*>(a.h), static_cast<const WQ*>(a.w_down),
+                       a.w_stride, a.s_down, a.s_stride, a.offsets, a.sorted_slots, a.topk_w,
+                       static_cast<YT*>(a.y));
 }
 
 template <typename YT>
