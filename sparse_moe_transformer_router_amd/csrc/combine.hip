@@ -43,6 +43,27 @@ __device__ __forceinline__ void st8(bf16* p, const float v[8]) {
   *reinterpret_cast<bf16x8*>(p) = b;
 }
 
+// acc[j] += y_t[k][c + j] for k = 0 .. K-1 in ascending order (the
+// combine's fixed order; y_t points at token t's K slot rows of length H).
+// The loads of up to 8 slots are issued before their adds, so K slots cost
+// about K / 8 memory round trips instead of K.
+template <typename YT>
+__device__ __forceinline__ void sum_slots(const YT* __restrict__ y_t, int K, int H, int c,
+                                          float acc[8]) {
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    float v[8][8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (k0 + kk < K) ld8(y_t + (size_t)(k0 + kk) * H + c, v[kk]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (k0 + kk < K) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += v[kk][j];
+      }
+  }
+}
+
 template <typename YT, typename OT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int K,
                                                            const YT* __restrict__ y,
@@ -54,12 +75,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int K,
        i += (long long)gridDim.x * kThreads) {
     const int t = (int)(i / per_row), c = (int)(i % per_row) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < K; ++k) {
-      float v[8];
-      ld8(y + ((size_t)t * K + k) * H + c, v);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += v[j];
-    }
+    sum_slots(y + (size_t)t * K * H, K, H, c, acc);
     if (addend) {
       float v[8];
       ld8(addend + (size_t)t * H + c, v);
@@ -132,13 +148,8 @@ __global__ __launch_bounds__(kThreads) void block_epilogue_kernel(
   float ssm = 0.0f, ssd = 0.0f;
   for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, d[8];
-    for (int k = 0; k < K; ++k) {
-      float v[8];
-      ld8(y + ((size_t)t * K + k) * H + c, v);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += v[j];
-    }
     ld8(dn + (size_t)t * H + c, d);
+    sum_slots(y + (size_t)t * K * H, K, H, c, acc);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       ssm += acc[j] * acc[j];
