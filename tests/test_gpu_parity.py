@@ -219,7 +219,9 @@ def case26b():
     return synth.moe_case(64, seed=0)
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
+# 8 and 9 straddle the switch of the decode down kernel to activation rows
+# staged in LDS
+@pytest.mark.parametrize("T", [1, 8, 9, 16, 64])
 def test_experts_26b_decode(case26b, T):
     c = synth.MoECase(T, case26b.H, case26b.E, case26b.K, case26b.I, True, case26b.eps,
                       synth.Tensor(case26b.x.f32[:T], case26b.x.bf16[:T]), case26b.router_w,
