@@ -510,11 +510,16 @@ void launch_dn_t(const DownArgs& a, hipStream_t s) {
 }  // namespace
 
 // Weight streaming pays while every expert's row group is a few 16-row
-// tiles: at most 64 tokens and, for the expert groups, at most 16 rows per
-// expert on average (the top-K layout of 64 tokens has 4; the all-experts
-// layout has T, and takes the tiled GEMMs).
+// tiles: for the expert groups at most 256 tokens and at most 16 rows per
+// expert on average (top-8 of 128 experts: 256 tokens; the all-experts
+// layout has T rows per expert, and takes the tiled GEMMs past 16 tokens).
+// On the 26B-A4B experts the streaming pair beats the tiled GEMMs at every
+// size up to that limit (256 tokens: 203 + 124 us against 218 + 131) and
+// loses past it (512 tokens: 261 + 173 against 225 + 141).  The dense
+// branch (one 2112-wide MLP) streams its weights once per 32-row tile, and
+// the tiled GEMMs win there past 64 tokens.
 bool use_stream_kernels(int T, int rows, int E, bool ident) {
-  return T <= 64 && (ident || rows <= 16 * E);
+  return ident ? T <= 64 : (T <= 256 && rows <= 16 * E);
 }
 
 // The dense branch (ident) at <= 64 tokens takes 32-row tiles (its weights
@@ -528,7 +533,8 @@ hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s) {
     case WFormat::kMXFP4: launch_gu<fp4x2, 1, 1, 2, 1>(a, s); break;
     case WFormat::kBF16:
       if (a.ident) launch_gu<bf16, 8, 2, 2, 1>(a, s);
-      else launch_gu<bf16, 4, 1, 4, 1>(a, s);
+      else if (a.T <= 64) launch_gu<bf16, 4, 1, 4, 1>(a, s);
+      else launch_gu<bf16, 4, 2, 3, 1>(a, s);  // 16 rows per expert at 128 tokens
       break;
   }
   return hipGetLastError();

@@ -65,20 +65,23 @@ def bf16_path_bound(x, gate_up, down, idx, w):
     T, H = x.shape
     E, I2, _ = gate_up.shape
     I = I2 // 2
-    K = idx.shape[1]
+    idx = np.asarray(idx)
+    w = np.asarray(w, np.float64)
     exact = np.zeros((T, H))
     hterm = np.zeros((T, H))
-    mag = np.zeros((T, H))
-    for t in range(T):
-        for k in range(K):
-            e = int(idx[t, k])
-            gu = gate_up[e].astype(np.float64) @ x[t]
-            g, u = gu[:I], gu[I:]
-            hh = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))) * u
-            wd = down[e].astype(np.float64)
-            exact[t] += float(w[t, k]) * (wd @ hh)
-            a = abs(float(w[t, k])) * (np.abs(wd) @ np.abs(hh))
-            hterm[t] += a
-            mag[t] += a
+    # the (token, slot) pairs of each expert at once; a token picks an expert
+    # at most once, so the rows of tt are distinct
+    for e in range(E):
+        tt, kk = np.nonzero(idx == e)
+        if len(tt) == 0:
+            continue
+        gu = x[tt] @ gate_up[e].astype(np.float64).T
+        g, u = gu[:, :I], gu[:, I:]
+        hh = 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))) * u
+        wd = down[e].astype(np.float64)
+        wk = w[tt, kk][:, None]
+        exact[tt] += wk * (hh @ wd.T)
+        hterm[tt] += np.abs(wk) * (np.abs(hh) @ np.abs(wd).T)
+    mag = hterm
     bound = 2.0 ** -8 * np.abs(exact) * 1.001 + 2.0 ** -8 * hterm + 1e-5 * mag
     return bound, exact

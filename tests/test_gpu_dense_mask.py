@@ -10,12 +10,12 @@ top-K, so the sum over experts is the sparse top-K result.
   a prefill batch and on the fp32 path;
 - as a cross-check of the sparse path: every unselected slot is exactly zero,
   and where both layouts take the same kernels (16 tokens: the weight-streaming
-  kernels; 256: the tiled GEMMs) the per-slot outputs of the selected experts
+  kernels; 320: the tiled GEMMs) the per-slot outputs of the selected experts
   equal the sparse path's bit for bit, since each output element is one dot
   product accumulated in the same order whatever rows share its tile.  At 64
-  tokens the sparse layout (4 rows per expert) streams and the all-experts
-  layout (64 rows per expert) takes the tiled GEMMs, so there the slots agree
-  to the bf16 tolerance.
+  and 256 tokens the sparse layout (4 and 16 rows per expert) streams and the
+  all-experts layout (64 and 256 rows per expert) takes the tiled GEMMs, so
+  there the slots agree to the bf16 tolerance.
 """
 import numpy as np
 import pytest
@@ -108,7 +108,7 @@ def _sub(t: synth.Tensor, T: int) -> synth.Tensor:
     return synth.Tensor(t.f32[:T], None if t.bf16 is None else t.bf16[:T])
 
 
-@pytest.mark.parametrize("T,same_kernels", [(16, True), (64, False), (256, True)])
+@pytest.mark.parametrize("T,same_kernels", [(16, True), (64, False), (256, False), (320, True)])
 def test_dense_mask_26b_matches_oracle_and_sparse_path(T, same_kernels):
     c = synth.moe_case(T, seed=5)
     x = _sub(c.x, T)

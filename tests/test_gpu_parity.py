@@ -216,13 +216,22 @@ def test_experts_small_bf16_and_fp32(seed, T, H, E, K, I):
 
 @pytest.fixture(scope="module")
 def case26b():
-    return synth.moe_case(64, seed=0)
+    return synth.moe_case(256, seed=0)
 
 
 # 8 and 9 straddle the switch of the decode down kernel to activation rows
-# staged in LDS
-@pytest.mark.parametrize("T", [1, 8, 9, 16, 64])
+# staged in LDS, 64 and 65 the switch of gate_up to 32-row tiles; 256 tokens
+# (16 rows per expert) is the largest batch the weight-streaming kernels take
+@pytest.mark.parametrize("T", [1, 8, 9, 16, 64, 65, 128, 256])
 def test_experts_26b_decode(case26b, T):
+    """The expert output (bf16) within its per-element rounding bound at every
+    size, and each fp32 slot within 2e-2 x RMS.  The combined output is also
+    held to 2e-2 x RMS up to 128 tokens; at 256 tokens (720k outputs) the tail
+    of its two bf16 roundings (h before the down projection, then the output)
+    alone goes past the bar: a CPU model of exactly those roundings gives
+    0.0208 x RMS on this case, rounding the exact result alone 0.0124.  The bar
+    is stated for the layer's output, which test_block_26b_decode checks at
+    256 tokens, every row."""
     c = synth.MoECase(T, case26b.H, case26b.E, case26b.K, case26b.I, True, case26b.eps,
                       synth.Tensor(case26b.x.f32[:T], case26b.x.bf16[:T]), case26b.router_w,
                       case26b.router_scale, case26b.per_expert_scale, case26b.gate_up,
@@ -231,7 +240,11 @@ def test_experts_26b_decode(case26b, T):
     idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
     y, out = _expert_path(c, idx, w)
     ref = oracle.experts(c.x.f32, c.gate_up.f32, c.down.f32, idx, w)
-    assert rel_max_err(out, ref) <= BF16_TOL
+    bound, exact = bf16_path_bound(c.x.f32, c.gate_up.f32, c.down.f32, idx, w)
+    np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
+    assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) / bound))
+    if T <= 128:
+        assert rel_max_err(out, ref) <= BF16_TOL
     # each slot on its own (slot k = the k-th ranked expert's weighted output)
     for k in (0, c.K - 1):
         refk = oracle.experts(c.x.f32, c.gate_up.f32, c.down.f32, idx[:, k:k + 1],
@@ -333,11 +346,14 @@ def test_block_small(bf16):
     assert rel_max_err(out, r["out"]) <= tol
 
 
-def test_block_26b_decode():
-    """The full-size layer at a decode batch (64 tokens: the dense branch and
-    the experts take the weight-streaming kernels); every row checked."""
-    b = synth.block_case(64, seed=4)
-    note("block 26B T=64")
+@pytest.mark.parametrize("T", [64, 128, 256])
+def test_block_26b_decode(T):
+    """The full-size layer at decode batches, every row checked: at 64 tokens
+    the dense branch and the experts take the weight-streaming kernels, at 128
+    and 256 the dense branch takes the tiled GEMMs and the experts still
+    stream."""
+    b = synth.block_case(T, seed=4)
+    note(f"block 26B T={T}")
     out, ffn, idx, w = _run_block(b, True)
     r = _oracle_block(b)
     assert np.array_equal(idx, r["idx"])
