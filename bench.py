@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=64, help="decode tokens per step (headline)")
-    ap.add_argument("--sweep", default="1,8,32", help="other decode batches to report")
+    ap.add_argument("--sweep", default="1,8,32,128,256", help="other decode batches to report")
     ap.add_argument("--prefill", type=int, default=4096, help="prefill tokens (0 = skip)")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--xbatches", type=int, default=16, help="input batches rotated over")

@@ -76,7 +76,7 @@ typedef enum moe_status {
   MOE_ERR_HIP = -4           /* a HIP launch reported an error */
 } moe_status;
 
-/* Storage formats of expert weights below bf16 (decode batches):
+/* Storage formats of expert weights below bf16 (batches of up to 256 tokens):
  *   MOE_W_INT8   int8 codes, one fp32 scale per output channel;
  *   MOE_W_FP8    E4M3 codes (OCP 8-bit floating point: bias 7, no
  *                infinities, largest finite 448), one fp32 scale per output
@@ -237,8 +237,8 @@ int moe_expert_gate_up_timed(const moe_dims* dims, int32_t T, const void* x,
  * moe_expert_ffn_int8: moe_expert_ffn with the experts' weights as int8 codes
  * and per-row scales (gate_up: codes [E,2I,H], scales [E,2I]; down: codes
  * [E,H,I], scales [E,H]).  The code rows enter bf16 MFMAs exactly and each
- * output channel is multiplied by its scale after the k-sum.  Decode
- * batches only (T <= 64, act dtype bf16), else MOE_ERR_UNSUPPORTED. */
+ * output channel is multiplied by its scale after the k-sum.  Batches of
+ * T <= 256 tokens only, act dtype bf16, else MOE_ERR_UNSUPPORTED. */
 int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
                       void* stream);
 int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
@@ -277,8 +277,9 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
  * as moe_quantize lays them out).  Codes widen to bf16 exactly in registers
  * (MXFP4 with its block scale; block scales must exceed 2^-125 to stay in
  * bf16's normal range), enter bf16 MFMAs, and int8 / E4M3 output channels
- * are multiplied by their scale after the k-sum.  Decode batches only (T <=
- * 64, act dtype bf16), else MOE_ERR_UNSUPPORTED.
+ * are multiplied by their scale after the k-sum.  The weights are streamed
+ * (no tiled kernels for these formats), so batches of T <= 256 tokens only,
+ * act dtype bf16, else MOE_ERR_UNSUPPORTED.
  *
  * All three: device pointers, 16-byte aligned; MOE_ERR_ARG for an unknown
  * format, bad sizes or pointers. */

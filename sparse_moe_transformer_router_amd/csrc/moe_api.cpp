@@ -14,6 +14,10 @@
 
 namespace {
 
+// Quantized experts run on the weight-streaming kernels only, which pay up to
+// about 16 rows per expert (256 tokens at top-8 of 128 experts).
+constexpr int kMaxQuantTokens = 256;
+
 thread_local std::string g_err;
 
 int fail(int code, const char* fmt, ...) {
@@ -459,7 +463,8 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
   if (wformat_of(fmt, f)) return MOE_ERR_ARG;
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "quantized experts take bf16 activations");
-  if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "quantized experts: decode batches (T <= 64) only");
+  if (T > kMaxQuantTokens)
+    return fail(MOE_ERR_UNSUPPORTED, "quantized experts: T <= %d only", kMaxQuantTokens);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
   REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);

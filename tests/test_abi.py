@@ -146,8 +146,8 @@ def test_int8_entry_points_validate_on_the_host():
     d = D()
     args = [FAKE] * 10
     assert f(ctypes.byref(d), 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
-    assert f(ctypes.byref(d), 65, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
-    assert "T <= 64" in lib_mod.last_error()
+    assert f(ctypes.byref(d), 257, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert "T <= 256" in lib_mod.last_error()
     d32 = D(act=lib_mod.MOE_F32)
     assert f(ctypes.byref(d32), 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     bad = list(args)
@@ -222,7 +222,7 @@ def test_quantized_format_entry_points_validate_on_the_host():
     args = [FAKE] * 10
     assert ffn(ctypes.byref(d), F8, 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
     assert ffn(ctypes.byref(d), 0, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_ARG
-    assert ffn(ctypes.byref(d), MX, 65, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert ffn(ctypes.byref(d), MX, 257, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     d32 = D(act=lib_mod.MOE_F32)
     assert ffn(ctypes.byref(d32), F8, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     assert ffn(ctypes.byref(d), MX, 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
