@@ -11,7 +11,7 @@
 // rounded ones (HIP's default for sqrtf and '/'), and contraction is off in
 // this file so that products written separately stay separate.
 //
-// Small batches (T <= 64, H <= 4096) take two kernels:
+// Small batches (T <= 512, H <= 3072) take two kernels:
 //   router_logits_small  a block takes up to 4 tokens and 4 * EW experts.  Each
 //                 wave first issues the loads of its EW experts' weights (lane
 //                 c holds chunk c in registers), then one wave per token
@@ -20,8 +20,9 @@
 //                 scaled input to LDS in a padded [chunk][65] layout; every
 //                 lane then runs its chunk's chains against LDS, and one lane
 //                 per (token, expert) adds the chunk results in order;
-//   route_topk_dispatch  one wave per token over several blocks; when asked,
-//                 the last block to finish groups the T*K <= 1024 slots.
+//   route_topk_dispatch  one wave per token over several blocks; when asked
+//                 and T*K <= 1024, the last block to finish groups the slots
+//                 (else the dispatch kernels of dispatch.hip follow).
 // Large batches take three:
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
@@ -525,20 +526,29 @@ __global__ __launch_bounds__(kChunkSlots) void route_topk_dispatch_kernel(
 }
 
 template <typename XT, int TB, int EW>
-void launch_small(const RouterArgs& a, hipStream_t s) {
+void launch_small(const RouterArgs& a, bool count, hipStream_t s) {
   const int nc = a.H / kChunk;
   const size_t lds = sizeof(float) * ((size_t)TB * nc * (kChunk + 1) +
                                       4 * TB * EW * (kChunk + 1) + 4 * kWave);
   dim3 grid((a.T + TB - 1) / TB, (a.E + 4 * EW - 1) / (4 * EW));
   hipLaunchKernelGGL((router_logits_small_kernel<XT, TB, EW>), grid, dim3(256), lds, s, a.T, a.H,
                      a.E, a.eps, static_cast<const XT*>(a.x), a.pre_gain, a.router_scale,
-                     a.router_w, a.ws_logits, a.counts != nullptr ? a.ws_counter : nullptr);
+                     a.router_w, a.ws_logits, count ? a.ws_counter : nullptr);
 }
 
 }  // namespace
 
-// Small-batch path (two kernels, dispatch inside the top-K kernel): up to 64
-// tokens, T*K <= 1024 slots, H <= 3072 (LDS within 64 KB).
+// Small-batch logits: up to 512 tokens, H <= 3072 (LDS within 64 KB).  The
+// chunk-parallel kernel spreads a token's 44 chunk chains (26B-A4B) over a
+// wave, while the wide kernel runs them one after another in a thread: at
+// 128 tokens the wide kernel had 16 blocks and took 105 us, this one 30 us
+// (256 tokens: 107 -> 53 us; 512: 112 -> 92 us; at 1024 tokens the wide
+// kernel wins, 115 against 171 us).  The dispatch joins the top-K kernel
+// while the batch has at most 1024 slots.
+constexpr int kSmallLogitsMaxT = 512;
+static bool router_small_logits(int T, int H) {
+  return H / kChunk <= 48 && T <= kSmallLogitsMaxT;
+}
 // Two tokens per thread halve the LDS reads per fma but also the block
 // count; they pay off once 16-token blocks alone give two blocks per CU.
 static int wide_tokens_per_thread(int T, int E) {
@@ -547,24 +557,36 @@ static int wide_tokens_per_thread(int T, int E) {
 }
 
 bool router_fuses_dispatch(int T, int H, int E, int K) {
-  return H / kChunk <= 48 && T <= 64 && T * K <= kChunkSlots;
+  return router_small_logits(T, H) && T * K <= kChunkSlots;
 }
 
 namespace {
+
+DispatchArgs dispatch_args(const RouterArgs& a) {
+  DispatchArgs d{};
+  d.T = a.T; d.E = a.E; d.K = a.K; d.topk_idx = a.topk_idx; d.counts = a.counts;
+  d.offsets = a.offsets; d.sorted_slots = a.sorted_slots; d.ws_blk_counts = a.ws_blk_counts;
+  d.ws_local_rank = a.ws_local_rank;
+  return d;
+}
 
 template <typename XT>
 hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   const XT* x = static_cast<const XT*>(a.x);
   const int nc = a.H / kChunk;
-  if (router_fuses_dispatch(a.T, a.H, a.E, a.K)) {
-    if (a.T == 1) launch_small<XT, 1, 1>(a, s);
-    else if (a.T <= 8) launch_small<XT, 2, 1>(a, s);
-    else launch_small<XT, 4, 2>(a, s);
+  const bool want_dispatch = a.counts != nullptr;
+  if (router_small_logits(a.T, a.H)) {
+    const bool fuse = want_dispatch && router_fuses_dispatch(a.T, a.H, a.E, a.K);
+    if (a.T == 1) launch_small<XT, 1, 1>(a, fuse, s);
+    else if (a.T <= 8) launch_small<XT, 2, 1>(a, fuse, s);
+    else launch_small<XT, 4, 2>(a, fuse, s);
     hipLaunchKernelGGL(route_topk_dispatch_kernel, dim3((a.T + kTopkTok - 1) / kTopkTok),
                        dim3(kChunkSlots), 0, s, a.T, a.E, a.K, a.ws_logits, a.per_expert_scale,
-                       a.topk_idx, a.topk_w, a.counts, a.offsets, a.sorted_slots,
-                       a.ws_counter);
-    return hipGetLastError();
+                       a.topk_idx, a.topk_w, fuse ? a.counts : nullptr, a.offsets,
+                       a.sorted_slots, a.ws_counter);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || fuse || !want_dispatch) return e;
+    return launch_dispatch(dispatch_args(a), s);
   }
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
                      a.eps, x, a.pre_gain, a.ws_r0, a.ws_r);
@@ -588,12 +610,8 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(router_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.E, a.K,
                      a.ws_logits, a.per_expert_scale, a.topk_idx, a.topk_w);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.counts == nullptr) return e;
-  DispatchArgs d{};
-  d.T = a.T; d.E = a.E; d.K = a.K; d.topk_idx = a.topk_idx; d.counts = a.counts;
-  d.offsets = a.offsets; d.sorted_slots = a.sorted_slots; d.ws_blk_counts = a.ws_blk_counts;
-  d.ws_local_rank = a.ws_local_rank;
-  return launch_dispatch(d, s);
+  if (e != hipSuccess || !want_dispatch) return e;
+  return launch_dispatch(dispatch_args(a), s);
 }
 
 }  // namespace

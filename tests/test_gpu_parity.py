@@ -64,7 +64,8 @@ def test_router_tiny_fp32():
     _check_router(synth.tiny_case())
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 32, 63, 64, 200])
+# up to 512 tokens the chunk-parallel logits kernel, past it the wide kernel
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 32, 63, 64, 200, 512, 513])
 def test_router_decode_sizes(T):
     _check_router(synth.moe_case(T, seed=T, I=32, router_scale_std=0.05))
 
@@ -74,7 +75,7 @@ def test_router_prefill_sizes(T, skew):
     _check_router(synth.moe_case(T, seed=11, I=32, skew=skew))
 
 
-@pytest.mark.parametrize("T", [5, 300])
+@pytest.mark.parametrize("T", [5, 300, 700])
 def test_router_with_pre_norm(T):
     c = synth.moe_case(T, seed=12, I=32, router_scale_std=0.05)
     g = (1 + 0.05 * np.random.default_rng(0).standard_normal(c.H)).astype(np.float32)
@@ -82,8 +83,8 @@ def test_router_with_pre_norm(T):
 
 
 @pytest.mark.parametrize("T,H,E,K,bf16", [
-    (150, 128, 6, 2, False),    # E % 4 != 0: lane-per-token tiled kernel
-    (150, 192, 132, 4, True),   # wide kernel, 1 token per thread, two expert blocks, ragged
+    (600, 128, 6, 2, False),    # E % 4 != 0: lane-per-token tiled kernel
+    (600, 192, 132, 4, True),   # wide kernel, 1 token per thread, two expert blocks, ragged
     (4100, 64, 256, 8, False),  # wide kernel, 2 tokens per thread, ragged token tail
 ])
 def test_router_large_batch_kernels(T, H, E, K, bf16):
@@ -96,10 +97,14 @@ def test_router_fp32_large_hidden_and_k_equals_e():
 
 
 @pytest.mark.parametrize("T,skew,pre", [(1, False, False), (13, False, True), (64, False, False),
-                                        (65, False, False), (300, True, True)])
+                                        (65, False, False), (128, False, False),
+                                        (129, False, False), (300, True, True),
+                                        (600, False, True)])
 def test_route_fused(T, skew, pre):
-    """moe_route (router + dispatch in one call; fused into one kernel for
-    small batches) against the oracle's router and dispatch."""
+    """moe_route (router + dispatch in one call) against the oracle's router
+    and dispatch: the dispatch inside the top-K kernel up to 1024 slots (128
+    tokens at top-8), the dispatch kernels after it past that, after the
+    chunk-parallel logits (<= 512 tokens) or the wide kernel."""
     c = synth.moe_case(T, seed=20 + T, I=32, skew=skew, router_scale_std=0.05)
     g = (1 + 0.05 * np.random.default_rng(1).standard_normal(c.H)).astype(np.float32) if pre \
         else None
