@@ -46,7 +46,10 @@ __global__ __launch_bounds__(kChunkSlots) void dispatch_rank_kernel(
 }
 
 // One block: per expert, exclusive scan of the chunk counts (in place), the
-// expert totals and offsets.
+// expert totals and offsets.  A thread's counts are loaded 8 chunks at a time
+// before they are added: one load round trip per chunk had cost 9.5 us at
+// 32 chunks (4096 tokens at top-8).
+constexpr int kScanBatch = 8;
 __global__ __launch_bounds__(kMaxE) void dispatch_scan_kernel(int nblk, int E,
                                                               int32_t* __restrict__ blk_counts,
                                                               int32_t* __restrict__ counts,
@@ -55,10 +58,16 @@ __global__ __launch_bounds__(kMaxE) void dispatch_scan_kernel(int nblk, int E,
   const int e = threadIdx.x;
   if (e < E) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_counts[(size_t)b * E + e];
-      blk_counts[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        c[j] = b0 + j < nblk ? blk_counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) blk_counts[(size_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
     totals[e] = run;
     counts[e] = run;

@@ -11,7 +11,7 @@
 // rounded ones (HIP's default for sqrtf and '/'), and contraction is off in
 // this file so that products written separately stay separate.
 //
-// Small batches (T <= 512, H <= 3072) take two kernels:
+// Small batches (T <= 448, H <= 3072) take two kernels:
 //   router_logits_small  a block takes up to 4 tokens and 4 * EW experts.  Each
 //                 wave first issues the loads of its EW experts' weights (lane
 //                 c holds chunk c in registers), then one wave per token
@@ -27,12 +27,12 @@
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
 //   router_transpose  the weights [E, H] -> [H, E] (when E % 4 == 0);
-//   router_logits_wide  a block takes 16 tokens x 128 experts, a thread 2
-//                 tokens x 4 experts (8 chains).  Per chunk the normalised,
-//                 scaled input (computed once per block) and the transposed
-//                 weights are staged in LDS, double-buffered, and every thread
-//                 runs its 8 chains over the chunk with one 8-B and one 16-B
-//                 LDS read per 8 fmas;
+//   router_logits_split  a block takes 32 tokens x 64 experts, a thread 4
+//                 tokens x 4 experts (16 chains, one 16-B weight and one 16-B
+//                 input LDS read per 16 fmas); the block's G wave groups take
+//                 the chunks in turn (chunk c to group c % G), and the
+//                 groups' chunk results meet in LDS, where group 0 adds them
+//                 in chunk order;
 //   router_logits_tiled  (E % 4 != 0) a block takes 64 tokens x 32 experts,
 //                 lane = token, the expert weights read as LDS broadcasts;
 //   router_topk   one wave per token.
@@ -352,132 +352,129 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(int E, int H,
   }
 }
 
-__device__ __forceinline__ void load4(const float* p, float v[4]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-}
-__device__ __forceinline__ void load4(const bf16* p, float v[4]) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-
-__device__ __forceinline__ void load2(const float* p, float v[2]) {
-  const float2 a = *reinterpret_cast<const float2*>(p);
-  v[0] = a.x; v[1] = a.y;
-}
-__device__ __forceinline__ void load2(const bf16* p, float v[2]) {
-  const unsigned u = *reinterpret_cast<const unsigned*>(p);
-  v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xffff0000u);
-}
-
-// Large batches, E % 4 == 0: block = 8 * TPT tokens x 128 experts; thread
-// (tp, eq) = TPT tokens x experts 4 eq .. 4 eq + 3.  LDS per buffer: the
-// transposed weights of the chunk [64][128] and the router input of the chunk
-// [64][8 * TPT] (row pitch chosen for conflict-free stores and aligned pair
-// loads), in one array with the input first.
-constexpr int kWideE = 128;
-template <typename XT, int TPT>
-__global__ __launch_bounds__(256) void router_logits_wide_kernel(
+// Large batches, E % 4 == 0, chunks split over wave groups: block = 32 tokens
+// x 64 experts, G groups of 128 threads; group g takes chunks g, g + G, ...
+// Thread (tq, eq) of a group runs 16 chains: tokens 4 tq .. 4 tq + 3 x
+// experts 4 eq .. 4 eq + 3, with one 16-B weight read and one 16-B input
+// read per 16 fmas.  Per round every group stages its chunk (transposed
+// weights [64][64], router input [64][32 + 4]) in its own LDS region, runs
+// its chains, and groups 1 .. G-1 leave their chunk results in LDS, which
+// group 0 adds to its totals in chunk order.
+constexpr int kSplitT = 32, kSplitE = 64, kSplitVP = kSplitT + 4;
+template <typename XT, int G>
+__global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
     const float* __restrict__ r0v, const float* __restrict__ rv,
     const float* __restrict__ scale, const float* __restrict__ WT, float* __restrict__ logits) {
-  static_assert(TPT == 1 || TPT == 2, "tokens per thread");
-  constexpr int BT = 8 * TPT;                 // tokens per block
-  constexpr int NV = kChunk * BT / 256;       // input values staged per thread per chunk
-  constexpr int VP = TPT == 2 ? 20 : 12;      // input row pitch (floats)
-  __shared__ __align__(16) float lds[2 * kChunk * VP + 2 * kChunk * kWideE];
-  auto vl = reinterpret_cast<float(*)[kChunk][VP]>(lds);
-  auto wl = reinterpret_cast<float(*)[kChunk][kWideE]>(lds + 2 * kChunk * VP);
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * kWideE;
-  const int tp = tid / 32, eq = tid % 32;
+  __shared__ __align__(16) float wl[G][kChunk][kSplitE];
+  __shared__ __align__(16) float vl[G][kChunk][kSplitVP];
+  __shared__ float ex[G > 1 ? G - 1 : 1][16][128];
+  const int g = threadIdx.x / 128, tig = threadIdx.x % 128;
+  const int tq = tig / 16, eq = tig % 16;
+  const int t0 = blockIdx.x * kSplitT, e0 = blockIdx.y * kSplitE;
   const bool pre = pre_gain != nullptr;
-  // staging of the input: token st, k values sk .. sk + NV - 1 of the chunk
-  const int st = tid % BT, sk = (tid / BT) * NV;
+  const int nc = H / kChunk;
+  const int R = (nc + G - 1) / G;
+  // staging of the input: token st, k values sk .. sk + 15 of the chunk
+  const int st = tig % kSplitT, sk = (tig / kSplitT) * 16;
   const int tcl = min(t0 + st, T - 1);
   const float r0 = pre ? r0v[tcl] : 0.0f, r = rv[tcl];
   const XT* xr = x + (size_t)tcl * H + sk;
-  const int nc = H / kChunk;
 
   float4 wreg[8];
-  float xv[NV], gv[NV], sv[NV];
+  float xv[16], sv[16], gv[16];
   auto gload = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int f = j * 256 + tid, k = f / 32, e = e0 + 4 * (f % 32);
+      const int f = j * 128 + tig, k = f / 16, e = e0 + 4 * (f % 16);
       wreg[j] = e < E ? *reinterpret_cast<const float4*>(WT + (size_t)(c * kChunk + k) * E + e)
                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    if constexpr (NV == 4) load4(xr + c * kChunk, xv);
-    else load2(xr + c * kChunk, xv);
+    load8(xr + c * kChunk, xv);
+    load8(xr + c * kChunk + 8, xv + 8);
+    load8(scale + c * kChunk + sk, sv);
+    load8(scale + c * kChunk + sk + 8, sv + 8);
+    if (pre) {
+      load8(pre_gain + c * kChunk + sk, gv);
+      load8(pre_gain + c * kChunk + sk + 8, gv + 8);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      sv[i] = scale[c * kChunk + sk + i];
-      gv[i] = pre ? pre_gain[c * kChunk + sk + i] : 0.0f;
+      for (int i = 0; i < 16; ++i) gv[i] = 0.0f;
     }
   };
-  auto lstore = [&](int b) {
+  auto lstore = [&]() {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int f = j * 256 + tid;
-      *reinterpret_cast<float4*>(&wl[b][f / 32][4 * (f % 32)]) = wreg[j];
+      const int f = j * 128 + tig;
+      *reinterpret_cast<float4*>(&wl[g][f / 16][4 * (f % 16)]) = wreg[j];
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vl[b][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
+    for (int i = 0; i < 16; ++i) vl[g][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
   };
 
-  float total[TPT][4];
+  float total[4][4];
 #pragma unroll
-  for (int i = 0; i < TPT; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) total[i][j] = 0.0f;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int c = 0; c < nc; ++c) {
-    const int b = c & 1;
-    if (c + 1 < nc) gload(c + 1);
-    float part[TPT][4];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[i][j] = 0.0f;
-#pragma unroll 16
-    for (int k = 0; k < kChunk; ++k) {
-      const float4 w = *reinterpret_cast<const float4*>(&wl[b][k][4 * eq]);
-      float v[TPT];
-      if constexpr (TPT == 2) {
-        const float2 vv = *reinterpret_cast<const float2*>(&vl[b][k][2 * tp]);
-        v[0] = vv.x;
-        v[1] = vv.y;
-      } else {
-        v[0] = vl[b][k][tp];
-      }
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        part[i][0] = __builtin_fmaf(v[i], w.x, part[i][0]);
-        part[i][1] = __builtin_fmaf(v[i], w.y, part[i][1]);
-        part[i][2] = __builtin_fmaf(v[i], w.z, part[i][2]);
-        part[i][3] = __builtin_fmaf(v[i], w.w, part[i][3]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + part[i][j];
-    if (c + 1 < nc) lstore(b ^ 1);
+  if (g < nc) gload(g);
+  for (int rr = 0; rr < R; ++rr) {
+    const int c = rr * G + g;
+    const bool have = c < nc;
+    if (have) lstore();
     __syncthreads();
-  }
+    if (c + G < nc) gload(c + G);
+    float p[4][4];
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int t = t0 + TPT * tp + i;
-    if (t >= T) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 4 * eq + j;
-      if (e < E) logits[(size_t)t * E + e] = total[i][j];
+      for (int j = 0; j < 4; ++j) p[i][j] = 0.0f;
+    if (have) {
+#pragma unroll 8
+      for (int k = 0; k < kChunk; ++k) {
+        const float4 w = *reinterpret_cast<const float4*>(&wl[g][k][4 * eq]);
+        const float4 v = *reinterpret_cast<const float4*>(&vl[g][k][4 * tq]);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i][0] = __builtin_fmaf(vv[i], w.x, p[i][0]);
+          p[i][1] = __builtin_fmaf(vv[i], w.y, p[i][1]);
+          p[i][2] = __builtin_fmaf(vv[i], w.z, p[i][2]);
+          p[i][3] = __builtin_fmaf(vv[i], w.w, p[i][3]);
+        }
+      }
+      if (g > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ex[g - 1][4 * i + j][tig] = p[i][j];
+      }
     }
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + p[i][j];
+#pragma unroll
+      for (int h = 1; h < G; ++h) {
+        if (rr * G + h >= nc) break;  // uniform
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + ex[h - 1][4 * i + j][tig];
+      }
+    }
+  }
+  if (g != 0) return;
+  const int e = e0 + 4 * eq;
+  if (e >= E) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * tq + i;
+    if (t < T)
+      *reinterpret_cast<float4*>(logits + (size_t)t * E + e) =
+          make_float4(total[i][0], total[i][1], total[i][2], total[i][3]);
   }
 }
 
@@ -538,23 +535,25 @@ void launch_small(const RouterArgs& a, bool count, hipStream_t s) {
 
 }  // namespace
 
-// Small-batch logits: up to 512 tokens, H <= 3072 (LDS within 64 KB).  The
+// Small-batch logits: up to 448 tokens, H <= 3072 (LDS within 64 KB).  The
 // chunk-parallel kernel spreads a token's 44 chunk chains (26B-A4B) over a
-// wave, while the wide kernel runs them one after another in a thread: at
-// 128 tokens the wide kernel had 16 blocks and took 105 us, this one 30 us
-// (256 tokens: 107 -> 53 us; 512: 112 -> 92 us; at 1024 tokens the wide
-// kernel wins, 115 against 171 us).  The dispatch joins the top-K kernel
-// while the batch has at most 1024 slots.
-constexpr int kSmallLogitsMaxT = 512;
+// wave; the large-batch kernels run them one after another in a thread and
+// pay a fixed ~80 us for the chunk rounds (the whole route at 128 tokens:
+// 30 us here against 105 us with the earlier 16-token-block kernel; 384
+// tokens: 73 us; at 512 tokens this kernel's 92 us loses to the split
+// kernel's ~80).  The dispatch joins the top-K kernel while the batch has at
+// most 1024 slots.
+constexpr int kSmallLogitsMaxT = 448;
 static bool router_small_logits(int T, int H) {
   return H / kChunk <= 48 && T <= kSmallLogitsMaxT;
 }
-// Two tokens per thread halve the LDS reads per fma but also the block
-// count; they pay off once 16-token blocks alone give two blocks per CU.
-static int wide_tokens_per_thread(int T, int E) {
-  const long long blocks16 = (long long)((T + 15) / 16) * ((E + kWideE - 1) / kWideE);
-  return blocks16 >= 512 ? 2 : 1;
-}
+// Four wave groups (one 8-wave block per CU, 124 KB of LDS) while the grid
+// fits the 256 CUs at one block each; past that two groups (58 KB, two
+// 4-wave blocks per CU).  The whole route at 4096 tokens: 146 us with the
+// earlier kernel (one token per thread, 5 B of LDS per fma), 91 us with
+// four groups; at 8192 tokens with the pre-norm 191 -> 157 us with two
+// groups (four: 179 us).
+constexpr long long kSplitOneBlockPerCu = 256;
 
 bool router_fuses_dispatch(int T, int H, int E, int K) {
   return router_small_logits(T, H) && T * K <= kChunkSlots;
@@ -593,15 +592,13 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   if (a.E % 4 == 0 && a.ws_wt != nullptr) {
     hipLaunchKernelGGL(router_transpose_kernel, dim3((a.H + 31) / 32, (a.E + 31) / 32), dim3(256),
                        0, s, a.E, a.H, a.router_w, a.ws_wt);
-    const dim3 eg(1, (a.E + kWideE - 1) / kWideE);
-    if (wide_tokens_per_thread(a.T, a.E) == 2)
-      hipLaunchKernelGGL((router_logits_wide_kernel<XT, 2>), dim3((a.T + 15) / 16, eg.y), dim3(256),
-                         0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
-                         a.ws_wt, a.ws_logits);
+    const dim3 sg((a.T + kSplitT - 1) / kSplitT, (a.E + kSplitE - 1) / kSplitE);
+    if ((long long)sg.x * sg.y <= kSplitOneBlockPerCu)
+      hipLaunchKernelGGL((router_logits_split_kernel<XT, 4>), sg, dim3(512), 0, s, a.T, a.H, a.E,
+                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.ws_wt, a.ws_logits);
     else
-      hipLaunchKernelGGL((router_logits_wide_kernel<XT, 1>), dim3((a.T + 7) / 8, eg.y), dim3(256),
-                         0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale,
-                         a.ws_wt, a.ws_logits);
+      hipLaunchKernelGGL((router_logits_split_kernel<XT, 2>), sg, dim3(256), 0, s, a.T, a.H, a.E,
+                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.ws_wt, a.ws_logits);
   } else {
     hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
                        dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,

@@ -64,8 +64,9 @@ def test_router_tiny_fp32():
     _check_router(synth.tiny_case())
 
 
-# up to 512 tokens the chunk-parallel logits kernel, past it the wide kernel
-@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 32, 63, 64, 200, 512, 513])
+# up to 448 tokens the chunk-parallel logits kernel, past it the chunk-split
+# kernel (four wave groups here)
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 32, 63, 64, 200, 448, 449])
 def test_router_decode_sizes(T):
     _check_router(synth.moe_case(T, seed=T, I=32, router_scale_std=0.05))
 
@@ -84,8 +85,11 @@ def test_router_with_pre_norm(T):
 
 @pytest.mark.parametrize("T,H,E,K,bf16", [
     (600, 128, 6, 2, False),    # E % 4 != 0: lane-per-token tiled kernel
-    (600, 192, 132, 4, True),   # wide kernel, 1 token per thread, two expert blocks, ragged
-    (4100, 64, 256, 8, False),  # wide kernel, 2 tokens per thread, ragged token tail
+    # chunk-split kernel; 4 groups up to 256 blocks, else 2
+    (600, 192, 132, 4, True),   # 4 groups, 3 chunks (group 3 idle), ragged expert block
+    (1000, 320, 64, 4, False),  # 4 groups, 5 chunks: a last round with one group
+    (4100, 64, 256, 8, False),  # 2 groups, 1 chunk, ragged token tail
+    (9000, 192, 128, 8, True),  # 2 groups, 3 chunks: a last round with one group
 ])
 def test_router_large_batch_kernels(T, H, E, K, bf16):
     _check_router(synth.tiny_case(seed=T + E, T=T, H=H, E=E, K=K, I=32, bf16=bf16))
