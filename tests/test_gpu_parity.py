@@ -71,7 +71,9 @@ def test_router_decode_sizes(T):
     _check_router(synth.moe_case(T, seed=T, I=32, router_scale_std=0.05))
 
 
-@pytest.mark.parametrize("T,skew", [(257, False), (4096, True)])
+# 4096 tokens: the chunk-split kernel's four-group form (256 blocks), 4128:
+# its two-group form (258 blocks)
+@pytest.mark.parametrize("T,skew", [(257, False), (4096, True), (4128, False)])
 def test_router_prefill_sizes(T, skew):
     _check_router(synth.moe_case(T, seed=11, I=32, skew=skew))
 
@@ -108,7 +110,7 @@ def test_route_fused(T, skew, pre):
     """moe_route (router + dispatch in one call) against the oracle's router
     and dispatch: the dispatch inside the top-K kernel up to 1024 slots (128
     tokens at top-8), the dispatch kernels after it past that, after the
-    chunk-parallel logits (<= 512 tokens) or the wide kernel."""
+    chunk-parallel logits (<= 448 tokens) or the chunk-split kernel."""
     c = synth.moe_case(T, seed=20 + T, I=32, skew=skew, router_scale_std=0.05)
     g = (1 + 0.05 * np.random.default_rng(1).standard_normal(c.H)).astype(np.float32) if pre \
         else None
