@@ -487,6 +487,67 @@ def block_measure(torch, lib, T, steps, warmup, seed, layers):
             "binding": "hbm" if byts / HBM_PEAK_GBS * 1e3 > fl / BF16_PEAK_TFLOPS else "mfma"}
 
 
+def block_quant_measure(torch, lib, layers, T, steps, warmup, seed):
+    """The whole layer at a decode batch with its expert and dense-MLP weights
+    in each of QUANT_FORMATS (gemma4_ffn_block_q), quantized on the GPU from
+    the layers' bf16 weights, beside the bf16 layer on the same weights."""
+    res = {"bf16": block_measure(torch, lib, T, steps, warmup, seed, layers)}
+    dims = lib.dims(H, E, K, I, D, 1e-6, lib.MOE_BF16, lib.MOE_F32)
+    ws = lib.workspace(dims, T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_039 * seed + T)
+    xs = [torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    for name, (fmt, per_byte, sbytes, desc) in QUANT_FORMATS.items():
+        def quant(wt):
+            rows, n = wt.numel() // wt.shape[-1], wt.shape[-1]
+            q = torch.empty(rows * n // per_byte, dtype=torch.uint8, device="cuda")
+            sc = (torch.empty(rows * n // 32, dtype=torch.uint8, device="cuda") if fmt == 3
+                  else torch.empty(rows, dtype=torch.float32, device="cuda"))
+            lib.moe_quantize(fmt, wt, q, sc)
+            return q, sc
+        qlayers = []
+        for ly in layers:
+            mats = [*quant(ly.dense[0]), *quant(ly.dense[1]), *quant(ly.dense[2])]
+            exp = [*quant(ly.gu), *quant(ly.dn)]
+            keep = (*ly.gains, *mats, ly.rw, ly.rs, ly.pes, *exp)
+            qlayers.append((keep, lib.ffn_weights_q(fmt, *keep, 0.06)))
+        torch.cuda.synchronize()
+
+        def step(i):
+            lib.gemma4_ffn_block_q(dims, T, xs[i % 2], qlayers[i % len(qlayers)][1], out, None,
+                                   idx, None, ws)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        us = []
+        for i in range(len(qlayers)):
+            step(i)
+            torch.cuda.synchronize()
+            us.append(int(torch.unique(idx).numel()))
+        U = sum(us) / len(us)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for i in range(steps):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
+        WINDOWS[f"block_{name}_{T}"] = (t0, time.perf_counter())
+        ms = a.elapsed_time(b) / steps
+        per_expert = (2 * I * H + H * I) // per_byte + 2 * I * sbytes(H) + H * sbytes(I)
+        dense = (3 * D * H) // per_byte + 2 * D * sbytes(H) + H * sbytes(D)
+        byts = U * per_expert + dense + ROUTER_BYTES + 2 * T * H * 2
+        res[name] = {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+                     "distinct_experts": U, "weights": desc, "hbm_bytes": byts,
+                     "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "speedup_vs_bf16": res["bf16"]["ms_per_step"] / ms}
+        del qlayers
+        torch.cuda.empty_cache()
+    return res
+
+
 def stack_measure(torch, lib, layers, T_dec, steps, T_pre, seed):
     """A stack of independently seeded blocks: decode steps whose input is the
     previous step's output, and one prefill pass."""
@@ -893,6 +954,12 @@ def main():
         block = block_measure(torch, lib, args.block, max(5, args.steps // 5),
                               max(2, args.warmup // 5), args.seed, layers[:2])
         done(f"layer {args.block}")
+    block_q = None
+    if args.block > 0:
+        block_q = block_quant_measure(torch, lib, layers[:2], args.batch,
+                                      max(10, args.steps // 2), max(2, args.warmup // 2),
+                                      args.seed)
+        done(f"layer {args.batch}, quantized weights")
     stack = None
     if args.stack > 0:
         stack = stack_measure(torch, lib, layers[:args.stack], args.batch, args.stack_steps,
@@ -952,6 +1019,7 @@ def main():
         "quantized_experts_decode": quant,
         "tiny_f32": tiny,
         "block": block,
+        "block_decode_quantized": block_q,
         "stack": stack,
         "cpu_oracle_other_configs": cpu_configs,
     }

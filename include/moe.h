@@ -326,6 +326,51 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* The same layer with the experts' and the dense MLP's weights stored in a
+ * format below bf16 (moe_wformat), the int8 option of the page "Porting a
+ * 128-expert MoE (Gemma-4 26B-A4B) to AWS Inferentia2", section "Can it run
+ * on a smaller box? Yes, no, and "deeper than it looks"" (there for the
+ * expert and dense MLP weights), and the 8-bit / 4-bit formats of section
+ * "The fp4 rabbit hole (two of them, both dead ends)".  Every matrix is
+ * quantized per output row as moe_quantize lays it out: the dense gate and
+ * up [D, H] and down [H, D] each with their own scales, the experts' gate_up
+ * [E, 2I, H] and down [E, H, I].  Norm gains, router weights and
+ * layer_scalar stay fp32; activations are bf16 (act_dtype MOE_BF16).  The
+ * codes widen to bf16 exactly in registers, as in moe_expert_ffn_q, so the
+ * result is the bf16 layer on the dequantized weights.  All matrices go
+ * through the weight-streaming kernels (there are no tiled kernels for these
+ * formats): T <= 256.  Otherwise as gemma4_ffn_block, including the side
+ * stream of the dense branch.  MOE_ERR_UNSUPPORTED for act_dtype MOE_F32,
+ * dense_inter == 0 or T > 256; MOE_ERR_ARG for an unknown format or a
+ * missing pointer. */
+typedef struct gemma4_ffn_weights_q {
+  int32_t fmt;                   /* moe_wformat of every quantized matrix */
+  const float* g_pre;            /* [H] the five RMSNorm gains, as in gemma4_ffn_weights */
+  const float* g_pre2;
+  const float* g_post1;
+  const float* g_post2;
+  const float* g_post;
+  const void* dense_gate_q;      /* [D, H] codes */
+  const void* dense_gate_scale;  /* its scales (fp32 [D], or E8M0 [D, H/32] for MXFP4) */
+  const void* dense_up_q;        /* [D, H] */
+  const void* dense_up_scale;
+  const void* dense_down_q;      /* [H, D] */
+  const void* dense_down_scale;
+  const float* router_w;         /* [E, H] fp32 */
+  const float* router_scale;     /* [H] */
+  const float* per_expert_scale; /* [E] */
+  const void* gate_up_q;         /* [E, 2I, H] codes */
+  const void* gate_up_scale;
+  const void* down_q;            /* [E, H, I] codes */
+  const void* down_scale;
+  float layer_scalar;
+} gemma4_ffn_weights_q;
+
+int gemma4_ffn_block_q(const moe_dims* dims, int32_t T, const void* residual,
+                       const gemma4_ffn_weights_q* weights, void* out, float* ffn_out,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

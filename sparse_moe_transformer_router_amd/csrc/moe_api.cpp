@@ -310,6 +310,99 @@ int run_combine(const moe_dims* d, int32_t T, const void* y, const void* addend,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
 }
 
+// The matrices of one layer: in the activation dtype (quant == false), or
+// codes and scales in format fmt.  Gains, router and layer_scalar are fp32.
+struct LayerW {
+  const float *g_pre, *g_pre2, *g_post1, *g_post2, *g_post;
+  const float *router_w, *router_scale, *per_expert_scale;
+  float layer_scalar;
+  bool quant;
+  moe::WFormat fmt;
+  const void *dg, *dgs, *du, *dus, *dd, *dds;  // dense gate, up, down (and scales)
+  const void *gu, *gus, *dn, *dns;             // experts' gate_up, down (and scales)
+};
+
+// One dual-path layer: pre-norms; the dense branch on the side stream; router,
+// dispatch and experts on the caller's stream; the epilogue after the join.
+int run_layer(const moe_dims* dims, int32_t T, const void* residual, const LayerW& lw,
+              void* out, float* ffn_out, int32_t* topk_idx, float* topk_w, void* ws,
+              hipStream_t s) {
+  int rc;
+  const Layout L = layout(dims, T);
+  const bool bf = dims->act_dtype == MOE_BF16;
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  void* y = at<void>(ws, L.y);
+  void* xd = at<void>(ws, L.xd);
+  void* xm = at<void>(ws, L.xm);
+  void* hd = at<void>(ws, L.hd);
+  void* dnb = at<void>(ws, L.dn);
+
+  moe::PreNormArgs pn{};
+  pn.T = T; pn.H = dims->hidden; pn.eps = dims->eps; pn.bf16 = bf;
+  pn.x = residual; pn.g_pre = lw.g_pre; pn.g_pre2 = lw.g_pre2; pn.xd = xd; pn.xm = xm;
+  hipError_t e = moe::launch_prenorm(pn, s);
+  if (e != hipSuccess) return hip_fail(e, "ffn layer (prenorm)");
+
+  // dense branch on the side stream, after the pre-norms
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  if ((e = side_stream(side)) != hipSuccess) return hip_fail(e, "ffn layer (side stream)");
+  hipStream_t s2 = side->stream;
+  if ((e = hipEventRecord(side->fork, s)) != hipSuccess ||
+      (e = hipStreamWaitEvent(s2, side->fork, 0)) != hipSuccess)
+    return hip_fail(e, "ffn layer (fork)");
+
+  moe::GateUpArgs g{};
+  g.T = T; g.H = dims->hidden; g.N = dims->dense_inter; g.E = 1; g.K = 1; g.rows = T;
+  g.ident = true; g.bf16 = bf; g.x = xd; g.w_gate = lw.dg; g.w_up = lw.du;
+  g.w_stride = 0; g.offsets = nullptr; g.sorted_slots = nullptr; g.h = hd;
+  moe::DownArgs dd{};
+  dd.T = T; dd.H = dims->hidden; dd.N = dims->dense_inter; dd.E = 1; dd.K = 1; dd.rows = T;
+  dd.ident = true; dd.bf16 = bf; dd.y_bf16 = dims->slot_dtype == MOE_BF16; dd.h = hd;
+  dd.w_down = lw.dd; dd.w_stride = 0; dd.offsets = nullptr; dd.sorted_slots = nullptr;
+  dd.topk_w = nullptr; dd.y = dnb;
+  if (lw.quant) {
+    // one group: the per-expert strides are never applied
+    g.w_fmt = lw.fmt; g.s_gate = lw.dgs; g.s_up = lw.dus; g.s_stride = 0;
+    dd.w_fmt = lw.fmt; dd.s_down = lw.dds; dd.s_stride = 0;
+    if ((e = moe::launch_gate_up_stream(g, s2)) != hipSuccess)
+      return hip_fail(e, "ffn layer (dense gate_up, quantized weights)");
+    if ((e = moe::launch_down_stream(dd, s2)) != hipSuccess)
+      return hip_fail(e, "ffn layer (dense down, quantized weights)");
+  } else {
+    if ((e = moe::launch_gate_up(g, s2)) != hipSuccess)
+      return hip_fail(e, "ffn layer (dense gate_up)");
+    if ((e = moe::launch_down(dd, s2)) != hipSuccess)
+      return hip_fail(e, "ffn layer (dense down)");
+  }
+  if ((e = hipEventRecord(side->join, s2)) != hipSuccess)
+    return hip_fail(e, "ffn layer (join)");
+
+  // router and experts on the caller's stream, meanwhile
+  if ((rc = run_router(dims, T, residual, lw.router_w, lw.router_scale, lw.per_expert_scale,
+                       lw.g_pre2, idx, w, counts, offsets, sorted, ws, s)))
+    return rc;
+  rc = lw.quant ? run_expert_ffn_q(dims, lw.fmt, T, xm, lw.gu, lw.gus, lw.dn, lw.dns, w,
+                                   offsets, sorted, y, ws, s)
+                : run_expert_ffn(dims, T, xm, lw.gu, lw.dn, w, offsets, sorted, y, ws, s);
+  if (rc) return rc;
+  if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess)
+    return hip_fail(e, "ffn layer (join)");
+
+  moe::EpilogueArgs ep{};
+  ep.T = T; ep.H = dims->hidden; ep.K = dims->top_k; ep.eps = dims->eps;
+  ep.layer_scalar = lw.layer_scalar; ep.y_bf16 = dims->slot_dtype == MOE_BF16; ep.act_bf16 = bf;
+  ep.y = y; ep.dn = dnb; ep.x = residual; ep.g_post1 = lw.g_post1; ep.g_post2 = lw.g_post2;
+  ep.g_post = lw.g_post; ep.out = out; ep.ffn_out = ffn_out;
+  if ((e = moe::launch_block_epilogue(ep, s)) != hipSuccess)
+    return hip_fail(e, "ffn layer (epilogue)");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -589,69 +682,59 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
   REQUIRE_PTR(wt->router_w); REQUIRE_PTR(wt->router_scale); REQUIRE_PTR(wt->per_expert_scale);
   REQUIRE_PTR(wt->w_gate_up); REQUIRE_PTR(wt->w_down);
   if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  LayerW lw{};
+  lw.g_pre = wt->g_pre; lw.g_pre2 = wt->g_pre2; lw.g_post1 = wt->g_post1;
+  lw.g_post2 = wt->g_post2; lw.g_post = wt->g_post;
+  lw.router_w = wt->router_w; lw.router_scale = wt->router_scale;
+  lw.per_expert_scale = wt->per_expert_scale; lw.layer_scalar = wt->layer_scalar;
+  lw.quant = false;
+  lw.dg = wt->dense_gate; lw.du = wt->dense_up; lw.dd = wt->dense_down;
+  lw.gu = wt->w_gate_up; lw.dn = wt->w_down;
+  return run_layer(dims, T, residual, lw, out, ffn_out, topk_idx, topk_w, ws,
+                   static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Layout L = layout(dims, T);
-  const bool bf = dims->act_dtype == MOE_BF16;
-  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
-  float* w = topk_w ? topk_w : at<float>(ws, L.w);
-  int32_t* counts = at<int32_t>(ws, L.counts);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* sorted = at<int32_t>(ws, L.sorted);
-  void* y = at<void>(ws, L.y);
-  void* xd = at<void>(ws, L.xd);
-  void* xm = at<void>(ws, L.xm);
-  void* hd = at<void>(ws, L.hd);
-  void* dn = at<void>(ws, L.dn);
-
-  moe::PreNormArgs pn{};
-  pn.T = T; pn.H = dims->hidden; pn.eps = dims->eps; pn.bf16 = bf;
-  pn.x = residual; pn.g_pre = wt->g_pre; pn.g_pre2 = wt->g_pre2; pn.xd = xd; pn.xm = xm;
-  hipError_t e = moe::launch_prenorm(pn, s);
-  if (e != hipSuccess) return hip_fail(e, "gemma4_ffn_block (prenorm)");
-
-  // dense branch on the side stream, after the pre-norms
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* side = nullptr;
-  if ((e = side_stream(side)) != hipSuccess) return hip_fail(e, "gemma4_ffn_block (side stream)");
-  hipStream_t s2 = side->stream;
-  if ((e = hipEventRecord(side->fork, s)) != hipSuccess ||
-      (e = hipStreamWaitEvent(s2, side->fork, 0)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (fork)");
-
-  moe::GateUpArgs g{};
-  g.T = T; g.H = dims->hidden; g.N = dims->dense_inter; g.E = 1; g.K = 1; g.rows = T;
-  g.ident = true; g.bf16 = bf; g.x = xd; g.w_gate = wt->dense_gate; g.w_up = wt->dense_up;
-  g.w_stride = 0; g.offsets = nullptr; g.sorted_slots = nullptr; g.h = hd;
-  if ((e = moe::launch_gate_up(g, s2)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (dense gate_up)");
-  moe::DownArgs dd{};
-  dd.T = T; dd.H = dims->hidden; dd.N = dims->dense_inter; dd.E = 1; dd.K = 1; dd.rows = T;
-  dd.ident = true; dd.bf16 = bf; dd.y_bf16 = dims->slot_dtype == MOE_BF16; dd.h = hd;
-  dd.w_down = wt->dense_down; dd.w_stride = 0; dd.offsets = nullptr; dd.sorted_slots = nullptr;
-  dd.topk_w = nullptr; dd.y = dn;
-  if ((e = moe::launch_down(dd, s2)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (dense down)");
-  if ((e = hipEventRecord(side->join, s2)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (join)");
-
-  // router and experts on the caller's stream, meanwhile
-  if ((rc = run_router(dims, T, residual, wt->router_w, wt->router_scale, wt->per_expert_scale,
-                       wt->g_pre2, idx, w, counts, offsets, sorted, ws, s)))
-    return rc;
-  if ((rc = run_expert_ffn(dims, T, xm, wt->w_gate_up, wt->w_down, w, offsets, sorted, y, ws, s)))
-    return rc;
-  if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (join)");
-
-  moe::EpilogueArgs ep{};
-  ep.T = T; ep.H = dims->hidden; ep.K = dims->top_k; ep.eps = dims->eps;
-  ep.layer_scalar = wt->layer_scalar; ep.y_bf16 = dims->slot_dtype == MOE_BF16; ep.act_bf16 = bf;
-  ep.y = y; ep.dn = dn; ep.x = residual; ep.g_post1 = wt->g_post1; ep.g_post2 = wt->g_post2;
-  ep.g_post = wt->g_post; ep.out = out; ep.ffn_out = ffn_out;
-  if ((e = moe::launch_block_epilogue(ep, s)) != hipSuccess)
-    return hip_fail(e, "gemma4_ffn_block (epilogue)");
-  return MOE_OK;
+int gemma4_ffn_block_q(const moe_dims* dims, int32_t T, const void* residual,
+                       const gemma4_ffn_weights_q* wt, void* out, float* ffn_out,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  if (dims->dense_inter <= 0)
+    return fail(MOE_ERR_UNSUPPORTED, "gemma4_ffn_block_q needs dense_inter > 0");
+  if (dims->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "quantized layer takes bf16 activations");
+  if (T > kMaxQuantTokens)
+    return fail(MOE_ERR_UNSUPPORTED, "quantized layer: T <= %d only", kMaxQuantTokens);
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  if (!wt) return fail(MOE_ERR_ARG, "weights is NULL");
+  moe::WFormat f;
+  if (wformat_of(wt->fmt, f)) return MOE_ERR_ARG;
+  REQUIRE_PTR(residual); REQUIRE_PTR(out); OPTIONAL_PTR(ffn_out);
+  OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
+  REQUIRE_PTR(wt->g_pre); REQUIRE_PTR(wt->g_pre2); REQUIRE_PTR(wt->g_post1);
+  REQUIRE_PTR(wt->g_post2); REQUIRE_PTR(wt->g_post);
+  REQUIRE_PTR(wt->dense_gate_q); REQUIRE_PTR(wt->dense_gate_scale);
+  REQUIRE_PTR(wt->dense_up_q); REQUIRE_PTR(wt->dense_up_scale);
+  REQUIRE_PTR(wt->dense_down_q); REQUIRE_PTR(wt->dense_down_scale);
+  REQUIRE_PTR(wt->router_w); REQUIRE_PTR(wt->router_scale); REQUIRE_PTR(wt->per_expert_scale);
+  REQUIRE_PTR(wt->gate_up_q); REQUIRE_PTR(wt->gate_up_scale);
+  REQUIRE_PTR(wt->down_q); REQUIRE_PTR(wt->down_scale);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  LayerW lw{};
+  lw.g_pre = wt->g_pre; lw.g_pre2 = wt->g_pre2; lw.g_post1 = wt->g_post1;
+  lw.g_post2 = wt->g_post2; lw.g_post = wt->g_post;
+  lw.router_w = wt->router_w; lw.router_scale = wt->router_scale;
+  lw.per_expert_scale = wt->per_expert_scale; lw.layer_scalar = wt->layer_scalar;
+  lw.quant = true; lw.fmt = f;
+  lw.dg = wt->dense_gate_q; lw.dgs = wt->dense_gate_scale;
+  lw.du = wt->dense_up_q; lw.dus = wt->dense_up_scale;
+  lw.dd = wt->dense_down_q; lw.dds = wt->dense_down_scale;
+  lw.gu = wt->gate_up_q; lw.gus = wt->gate_up_scale;
+  lw.dn = wt->down_q; lw.dns = wt->down_scale;
+  return run_layer(dims, T, residual, lw, out, ffn_out, topk_idx, topk_w, ws,
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

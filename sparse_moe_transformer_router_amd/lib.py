@@ -36,6 +36,14 @@ class Gemma4FfnWeights(ctypes.Structure):
         [("layer_scalar", ctypes.c_float)]
 
 
+class Gemma4FfnWeightsQ(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32)] + [(n, ctypes.c_void_p) for n in (
+        "g_pre", "g_pre2", "g_post1", "g_post2", "g_post", "dense_gate_q", "dense_gate_scale",
+        "dense_up_q", "dense_up_scale", "dense_down_q", "dense_down_scale", "router_w",
+        "router_scale", "per_expert_scale", "gate_up_q", "gate_up_scale", "down_q",
+        "down_scale")] + [("layer_scalar", ctypes.c_float)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libmoe error {code}: {msg}")
@@ -70,10 +78,13 @@ def _load():
     L.moe_expert_ffn_q.argtypes = [D, I32, I32] + [P] * 10 + [SZ, P]
     L.gemma4_ffn_block.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeights)] + [P] * 5 + \
         [SZ, P]
+    L.gemma4_ffn_block_q.argtypes = [D, I32, P, ctypes.POINTER(Gemma4FfnWeightsQ)] + [P] * 5 + \
+        [SZ, P]
     for f in ("moe_router", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
               "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch",
-              "moe_quantize", "moe_dequantize", "moe_expert_ffn_q", "moe_expert_gate_up_timed"):
+              "moe_quantize", "moe_dequantize", "moe_expert_ffn_q", "moe_expert_gate_up_timed",
+              "gemma4_ffn_block_q"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -246,6 +257,24 @@ def ffn_weights(g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, d
     ts = (g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, dense_down, router_w,
           router_scale, per_expert_scale, w_gate_up, w_down)
     return Gemma4FfnWeights(*[_ptr(t) for t in ts], float(layer_scalar))
+
+
+def ffn_weights_q(fmt, g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate_q, dense_gate_scale,
+                  dense_up_q, dense_up_scale, dense_down_q, dense_down_scale, router_w,
+                  router_scale, per_expert_scale, gate_up_q, gate_up_scale, down_q, down_scale,
+                  layer_scalar) -> Gemma4FfnWeightsQ:
+    ts = (g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate_q, dense_gate_scale, dense_up_q,
+          dense_up_scale, dense_down_q, dense_down_scale, router_w, router_scale,
+          per_expert_scale, gate_up_q, gate_up_scale, down_q, down_scale)
+    return Gemma4FfnWeightsQ(int(fmt), *[_ptr(t) for t in ts], float(layer_scalar))
+
+
+def gemma4_ffn_block_q(d, T, residual, weights: Gemma4FfnWeightsQ, out, ffn_out, topk_idx,
+                       topk_w, ws, stream=None):
+    _check(_lib.gemma4_ffn_block_q(ctypes.byref(d), T, _ptr(residual), ctypes.byref(weights),
+                                   _ptr(out), _ptr(ffn_out), _ptr(topk_idx), _ptr(topk_w),
+                                   _ptr(ws), ws.numel() if ws is not None else 0,
+                                   _stream(stream)))
 
 
 def gemma4_ffn_block(d, T, residual, weights: Gemma4FfnWeights, out, ffn_out, topk_idx, topk_w,

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_expected_calls():
     fns = declared_functions()
     for name in ("moe_router", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                 "gemma4_ffn_block", "moe_forward", "moe_workspace_size", "moe_last_error"):
+                 "gemma4_ffn_block", "gemma4_ffn_block_q", "moe_forward", "moe_workspace_size",
+                 "moe_last_error"):
         assert name in fns
 
 
@@ -121,6 +122,44 @@ def test_block_requires_dense_branch_and_weights():
     assert L.gemma4_ffn_block(ctypes.byref(d), 4, FAKE, ctypes.byref(w), FAKE, None, None, None,
                               FAKE, 1 << 40, None) == lib_mod.MOE_ERR_ARG
     assert "dense_up" in lib_mod.last_error()
+
+
+def test_quantized_block_validates():
+    """gemma4_ffn_block_q: a no-op at 0 tokens, and every refusal before any
+    launch (format, dtype, token limit, dense branch, pointers, workspace)."""
+    Lq = L.gemma4_ffn_block_q
+    Lq.argtypes = [ctypes.POINTER(lib_mod.MoeDims), ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.POINTER(lib_mod.Gemma4FfnWeightsQ)] + [ctypes.c_void_p] * 5 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    d = D()
+    dp = ctypes.byref(d)
+    assert Lq(dp, 0, None, None, None, None, None, None, None, 0, None) == lib_mod.MOE_OK
+    w = lib_mod.Gemma4FfnWeightsQ()
+    for f, _ in w._fields_[1:-1]:
+        setattr(w, f, 0x10000)
+    w.fmt = lib_mod.MOE_W_INT8
+    wp = ctypes.byref(w)
+    args = (FAKE, wp, FAKE, None, None, None, FAKE, 1 << 40, None)
+    assert Lq(dp, 257, *args) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert "T <= 256" in lib_mod.last_error()
+    d32 = D(act=lib_mod.MOE_F32)
+    assert Lq(ctypes.byref(d32), 4, *args) == lib_mod.MOE_ERR_UNSUPPORTED
+    d0 = D(dense_inter=0)
+    assert Lq(ctypes.byref(d0), 4, *args) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert Lq(dp, 4, FAKE, None, FAKE, None, None, None, FAKE, 1 << 40,
+              None) == lib_mod.MOE_ERR_ARG
+    w.fmt = 9
+    assert Lq(dp, 4, *args) == lib_mod.MOE_ERR_ARG and "format" in lib_mod.last_error()
+    w.fmt = lib_mod.MOE_W_MXFP4
+    w.dense_down_scale = None
+    assert Lq(dp, 4, *args) == lib_mod.MOE_ERR_ARG
+    assert "dense_down_scale" in lib_mod.last_error()
+    w.dense_down_scale = 0x10000
+    w.gate_up_q = 0x10004
+    assert Lq(dp, 4, *args) == lib_mod.MOE_ERR_ARG and "aligned" in lib_mod.last_error()
+    w.gate_up_q = 0x10000
+    assert Lq(dp, 4, FAKE, wp, FAKE, None, None, None, FAKE, 0,
+              None) == lib_mod.MOE_ERR_WORKSPACE
 
 
 def test_other_calls_validate():
