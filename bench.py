@@ -606,6 +606,55 @@ def stack_measure(torch, lib, layers, T_dec, steps, T_pre, seed):
     return res
 
 
+def stack_quant_decode(torch, lib, layers, T, steps, seed, name="int8"):
+    """The stack's decode steps with every layer's expert and dense-MLP weights
+    quantized on the GPU (gemma4_ffn_block_q), each step's input the previous
+    step's output, as in stack_measure."""
+    fmt, per_byte, sbytes, desc = QUANT_FORMATS[name]
+    dims = lib.dims(H, E, K, I, D, 1e-6, lib.MOE_BF16, lib.MOE_F32)
+    ws = lib.workspace(dims, T)
+
+    def quant(wt):
+        rows, n = wt.numel() // wt.shape[-1], wt.shape[-1]
+        q = torch.empty(rows * n // per_byte, dtype=torch.uint8, device="cuda")
+        sc = (torch.empty(rows * n // 32, dtype=torch.uint8, device="cuda") if fmt == 3
+              else torch.empty(rows, dtype=torch.float32, device="cuda"))
+        lib.moe_quantize(fmt, wt, q, sc)
+        return q, sc
+    ql = []
+    for ly in layers:
+        keep = (*ly.gains, *quant(ly.dense[0]), *quant(ly.dense[1]), *quant(ly.dense[2]), ly.rw,
+                ly.rs, ly.pes, *quant(ly.gu), *quant(ly.dn))
+        ql.append((keep, lib.ffn_weights_q(fmt, *keep, 0.06)))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1_000_081 * seed + 7)
+    bufs = [torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16), None]
+    bufs[1] = torch.empty_like(bufs[0])
+    n = len(ql)
+
+    def one_step(cur):
+        for li, (_, w) in enumerate(ql):
+            lib.gemma4_ffn_block_q(dims, T, bufs[(cur + li) % 2], w, bufs[(cur + li + 1) % 2],
+                                   None, None, None, ws)
+        return (cur + n) % 2
+    cur = one_step(0)  # warm-up step
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        cur = one_step(cur)
+    b.record()
+    torch.cuda.synchronize()
+    WINDOWS[f"stack_{name}_decode_{T}"] = (t0, time.perf_counter())
+    ms = a.elapsed_time(b) / steps
+    finite = bool(torch.isfinite(bufs[cur].float()).all().item())
+    del ql
+    torch.cuda.empty_cache()
+    return {"layers": n, "tokens": T, "steps": steps, "weights": desc, "ms_per_step": ms,
+            "tokens_per_s": T / (ms * 1e-3), "output_finite": finite}
+
+
 def tiny_measure(torch, lib, steps, warmup):
     """The tiny fp32 configuration (16 tokens, hidden 64, 8 experts, top-2,
     intermediate 32) through moe_forward."""
@@ -964,6 +1013,8 @@ def main():
     if args.stack > 0:
         stack = stack_measure(torch, lib, layers[:args.stack], args.batch, args.stack_steps,
                               args.stack_prefill, args.seed)
+        stack["decode_int8"] = stack_quant_decode(torch, lib, layers[:args.stack], args.batch,
+                                                  args.stack_steps, args.seed)
         done(f"stack of {args.stack} layers")
 
     clocks_sampler.stop()
