@@ -35,7 +35,10 @@
  *     Two calls in flight must not share a workspace.
  *   - Pointers must be 16-byte aligned.
  *   - Preconditions that are not checked: inputs are finite; topk_idx given to
- *     moe_dispatch lies in [0, E) with K distinct experts per token; the
+ *     moe_dispatch lies in [0, E) with K distinct experts per token (a slot
+ *     whose id is outside [0, E) is dropped: it is counted for no expert,
+ *     is missing from sorted_slots, expert_offsets[E] falls short of T*K,
+ *     and its y_slots row is left unwritten); the
  *     offsets / sorted_slots given to moe_expert_ffn are moe_dispatch's output
  *     for the same topk_idx.
  *   - Results are deterministic: no floating-point atomics; the same inputs
@@ -108,7 +111,15 @@ typedef struct moe_dims {
   int32_t dense_inter;   /* D (2112); 0 = no dense branch */
   float eps;             /* RMSNorm epsilon (1e-6), inside the square root */
   int32_t act_dtype;     /* moe_dtype of activations and expert / dense weights */
-  int32_t slot_dtype;    /* moe_dtype of y_slots and of the dense branch output */
+  int32_t slot_dtype;    /* moe_dtype of y_slots and of the dense branch output.
+                          * MOE_F32 is the default and the one held to the
+                          * accuracy bar (max |err| <= 2e-2 x RMS of an exact
+                          * evaluation).  MOE_BF16 halves the slot traffic but
+                          * rounds every slot once more and is OUTSIDE that
+                          * bar (0.026 x RMS on one 64-token 26B-A4B batch);
+                          * each bf16 slot is the fp32 slot rounded to
+                          * nearest-even, so its extra error is at most 2^-8
+                          * of each slot's magnitude. */
 } moe_dims;
 
 /* Weights of one dual-path layer (all device pointers). */
@@ -341,8 +352,9 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
  * through the weight-streaming kernels (there are no tiled kernels for these
  * formats): T <= 256.  Otherwise as gemma4_ffn_block, including the side
  * stream of the dense branch.  MOE_ERR_UNSUPPORTED for act_dtype MOE_F32,
- * dense_inter == 0 or T > 256; MOE_ERR_ARG for an unknown format or a
- * missing pointer. */
+ * dense_inter == 0, T > 256, or MXFP4 with dense_inter > 8192 (its kernels
+ * stage the block scales of a contraction of at most 8192 weights);
+ * MOE_ERR_ARG for an unknown format or a missing pointer. */
 typedef struct gemma4_ffn_weights_q {
   int32_t fmt;                   /* moe_wformat of every quantized matrix */
   const float* g_pre;            /* [H] the five RMSNorm gains, as in gemma4_ffn_weights */

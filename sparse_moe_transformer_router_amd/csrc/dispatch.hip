@@ -14,7 +14,8 @@
 // scanned across blocks by a single-block kernel, which also forms the expert
 // offsets.  A lone chunk (T*K <= 1024, every decode batch) runs all of it in
 // one kernel; the router can also run that lone-chunk dispatch itself, right
-// after its top-K (see the router kernels).
+// after its top-K (see the router kernels).  An expert id outside [0, E) in a
+// caller's topk_idx is dropped: its slot joins no group and is not listed.
 #include "launch.h"
 #include "route_dev.h"
 
@@ -27,8 +28,10 @@ __global__ __launch_bounds__(kChunkSlots) void dispatch_single_kernel(
   __shared__ int wave_base[kChunkWaves][kMaxE];
   __shared__ int totals[kMaxE];
   __shared__ int offs[kMaxE + 1];
-  const bool valid = (int)threadIdx.x < S;
-  const int e = valid ? topk_idx[threadIdx.x] : 0;
+  // an expert id outside [0, E) takes part in no group (it is dropped)
+  const int e0 = (int)threadIdx.x < S ? topk_idx[threadIdx.x] : -1;
+  const bool valid = (unsigned)e0 < (unsigned)E;
+  const int e = valid ? e0 : 0;
   dispatch_lone_chunk(e, valid, E, counts, offsets, sorted_slots, wave_base, totals, offs);
 }
 
@@ -38,8 +41,9 @@ __global__ __launch_bounds__(kChunkSlots) void dispatch_rank_kernel(
   __shared__ int wave_base[kChunkWaves][kMaxE];
   __shared__ int totals[kMaxE];
   const int s = blockIdx.x * kChunkSlots + threadIdx.x;
-  const bool valid = s < S;
-  const int e = valid ? topk_idx[s] : 0;
+  const int e0 = s < S ? topk_idx[s] : -1;
+  const bool valid = (unsigned)e0 < (unsigned)E;  // ids outside [0, E) are dropped
+  const int e = valid ? e0 : 0;
   const int r = chunk_rank(e, valid, E, wave_base, totals);
   if (valid) local_rank[s] = r;
   if ((int)threadIdx.x < E) blk_counts[(size_t)blockIdx.x * E + threadIdx.x] = totals[threadIdx.x];
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(kChunkSlots) void dispatch_scatter_kernel(
   const int s = blockIdx.x * kChunkSlots + threadIdx.x;
   if (s >= S) return;
   const int e = topk_idx[s];
+  if ((unsigned)e >= (unsigned)E) return;
   sorted_slots[offsets[e] + blk_base[(size_t)blockIdx.x * E + e] + local_rank[s]] = s;
 }
 

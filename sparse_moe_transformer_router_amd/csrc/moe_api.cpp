@@ -290,6 +290,10 @@ int run_expert_ffn_q(const moe_dims* d, moe::WFormat fmt, int32_t T, const void*
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down (quantized weights)");
 }
 
+// MXFP4 kernels stage a block's E8M0 scale rows in LDS, one byte per 32
+// weights of a contraction of at most this length.
+constexpr int kMaxMxContraction = 8192;
+
 // Format code of the ABI -> the kernels' format, or -1 if unknown.
 int wformat_of(int32_t fmt, moe::WFormat& f) {
   switch (fmt) {
@@ -711,6 +715,9 @@ int gemma4_ffn_block_q(const moe_dims* dims, int32_t T, const void* residual,
   if (!wt) return fail(MOE_ERR_ARG, "weights is NULL");
   moe::WFormat f;
   if (wformat_of(wt->fmt, f)) return MOE_ERR_ARG;
+  if (f == moe::WFormat::kMXFP4 && dims->dense_inter > kMaxMxContraction)
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP4 weights: dense_inter=%d exceeds %d",
+                dims->dense_inter, kMaxMxContraction);
   REQUIRE_PTR(residual); REQUIRE_PTR(out); OPTIONAL_PTR(ffn_out);
   OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
   REQUIRE_PTR(wt->g_pre); REQUIRE_PTR(wt->g_pre2); REQUIRE_PTR(wt->g_post1);

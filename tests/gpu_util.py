@@ -52,7 +52,7 @@ def ws_logits_view(ws: torch.Tensor, T: int, E: int) -> torch.Tensor:
     return ws[off: off + 4 * T * E].view(torch.float32).view(T, E)
 
 
-def bf16_path_bound(x, gate_up, down, idx, w):
+def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False):
     """Per-element error bound of the bf16 expert path against the exact result.
 
     The bf16 path rounds twice: h = gelu(gate) * up is rounded to bf16 before
@@ -60,7 +60,10 @@ def bf16_path_bound(x, gate_up, down, idx, w):
     round-to-nearest moves a value v by at most 2^-8 |v| (8 significant bits),
     so |gpu - exact| <= 2^-8 |out| + sum_k |w_k| (|W_d[e_k]| @ |h_k|) 2^-8, plus
     fp32 accumulation error (taken as 1e-5 of the summed magnitudes).  Inputs
-    are the exactly widened bf16 values.  Returns (bound [T,H], exact [T,H])."""
+    are the exactly widened bf16 values.  With bf16_slots the K per-slot
+    outputs are also rounded to bf16 before their sum, which adds at most
+    2^-8 |w_k y_k| <= 2^-8 |w_k| (|W_d[e_k]| @ |h_k|) per slot.
+    Returns (bound [T,H], exact [T,H])."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     E, I2, _ = gate_up.shape
@@ -84,4 +87,6 @@ def bf16_path_bound(x, gate_up, down, idx, w):
         hterm[tt] += np.abs(wk) * (np.abs(hh) @ np.abs(wd).T)
     mag = hterm
     bound = 2.0 ** -8 * np.abs(exact) * 1.001 + 2.0 ** -8 * hterm + 1e-5 * mag
+    if bf16_slots:
+        bound += 2.0 ** -8 * hterm * 1.001
     return bound, exact

@@ -160,6 +160,13 @@ def test_quantized_block_validates():
     w.gate_up_q = 0x10000
     assert Lq(dp, 4, FAKE, wp, FAKE, None, None, None, FAKE, 0,
               None) == lib_mod.MOE_ERR_WORKSPACE
+    # MXFP4 stages a contraction of at most 8192 weights' block scales
+    dwide = D(dense_inter=8224)
+    assert Lq(ctypes.byref(dwide), 4, *args) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert "dense_inter" in lib_mod.last_error()
+    w.fmt = lib_mod.MOE_W_INT8
+    assert Lq(ctypes.byref(dwide), 4, FAKE, wp, FAKE, None, None, None, FAKE, 0,
+              None) == lib_mod.MOE_ERR_WORKSPACE
 
 
 def test_other_calls_validate():

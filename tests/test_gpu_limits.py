@@ -50,8 +50,9 @@ def test_limits_small_layers(seed, T, H, E, K, I):
 def test_largest_batch_26b():
     """65536 tokens (the largest T; 524288 token-slots) through the router,
     the dispatch and the tiled expert GEMMs at 26B shapes: logits bit for bit,
-    routing and dispatch exact, and sampled rows of the output within 2e-2 x
-    RMS of the oracle."""
+    routing and dispatch exact, sampled rows of the output within 2e-2 x RMS
+    of the oracle, and whole row tiles slot by slot (the hottest expert's
+    ragged last tile, every row of the rarest expert, the first tile)."""
     T = 65536
     c = synth.moe_case(T, seed=6)
     note(f"largest batch T={T}: router and dispatch")
@@ -84,3 +85,13 @@ def test_largest_batch_26b():
                            {0, T - 1}))
     ref = oracle.experts(c.x.f32[rows], c.gate_up.f32, c.down.f32, oi[rows], ow[rows])
     assert rel_max_err(host(out)[rows], ref) <= BF16_TOL
+    # whole row tiles: the last 256 sorted rows (the ragged tail) of the
+    # hottest expert and every row of the rarest one, slot by slot
+    hot, rare = int(np.argmax(oc)), int(np.argmin(oc))
+    picks = np.concatenate([os_[oo[hot + 1] - 256:oo[hot + 1]], os_[oo[rare]:oo[rare + 1]],
+                            os_[:64]])
+    tok, kk = picks // c.K, picks % c.K
+    yh = host(y.view(T * c.K, c.H)[torch.from_numpy(picks.astype(np.int64)).cuda()])
+    ref = oracle.experts(c.x.f32[tok], c.gate_up.f32, c.down.f32, oi[tok, kk][:, None],
+                         ow[tok, kk][:, None])
+    assert rel_max_err(yh, ref) <= BF16_TOL

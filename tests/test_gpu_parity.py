@@ -263,31 +263,66 @@ def test_experts_26b_decode(case26b, T):
         assert rel_max_err(y[:, k], refk) <= BF16_TOL
 
 
-def test_experts_26b_prefill_skewed_sampled():
-    """4096 skewed tokens through the full path; the oracle checks a sample of
-    rows that includes tokens of the hottest and of the rarest experts."""
+def _per_slot_refs(c, idx, w):
+    """The oracle's output of each slot on its own: [T, K, H] fp64."""
+    return np.stack([oracle.experts(c.x.f32, c.gate_up.f32, c.down.f32, idx[:, k:k + 1],
+                                    w[:, k:k + 1]) for k in range(c.K)], 1)
+
+
+def test_experts_26b_prefill_skewed_all_rows():
+    """4096 skewed tokens (hottest expert ~3100 slots, a dozen experts empty),
+    every row of every slot, through moe_route, moe_expert_ffn and moe_combine
+    (the calls of moe_forward).
+
+    - routing, counts, offsets and the slot permutation exact;
+    - every fp32 slot, and the in-order fp32 sum of each token's slots, within
+      2e-2 x RMS of the oracle;
+    - the bf16 output equal to that sum rounded once to nearest-even, bit for
+      bit, and within the per-element rounding bound of the bf16 path.
+    The whole-tensor bar is not put on the bf16 output itself: under this
+    load the largest outputs reach ~13 x RMS, so rounding the exact result to
+    bf16 alone moves it by 0.026 x RMS."""
     c = synth.moe_case(4096, seed=0, skew=True)
-    note("experts 26B prefill 4096 skewed")
+    note("experts 26B prefill 4096 skewed, all rows")
     d = _dims(c)
-    ws = lib.workspace(d, c.T)
+    T, K, E = c.T, c.K, c.E
+    ws = lib.workspace(d, T)
     x = dev_tensor(c.x, True)
-    out = torch.empty(c.T, c.H, dtype=torch.bfloat16, device="cuda")
-    idx = torch.empty(c.T, c.K, dtype=torch.int32, device="cuda")
-    w = torch.empty(c.T, c.K, dtype=torch.float32, device="cuda")
-    lib.moe_forward(d, c.T, x, dev_f32(c.router_w), dev_f32(c.router_scale),
-                    dev_f32(c.per_expert_scale), dev_tensor(c.gate_up, True),
-                    dev_tensor(c.down, True), out, idx, w, ws)
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    lib.moe_route(d, T, x, dev_f32(c.router_w), dev_f32(c.router_scale),
+                  dev_f32(c.per_expert_scale), None, idx, w, counts, offsets, ss, ws)
+    y = torch.empty(T, K, c.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, c.H, dtype=torch.bfloat16, device="cuda")
+    lib.moe_expert_ffn(d, T, x, dev_tensor(c.gate_up, True), dev_tensor(c.down, True), w,
+                       offsets, ss, y, ws)
+    lib.moe_combine(d, T, y, None, out)
     torch.cuda.synchronize()
-    oi, ow = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    oi, ow = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, K, c.eps)
     assert np.array_equal(host(idx), oi)
-    counts = np.bincount(oi.ravel(), minlength=c.E)
-    assert counts.max() > 1000 and (counts == 0).sum() + (counts < 20).sum() > 0
-    hot, rare = np.argmax(counts), np.argmin(np.where(counts > 0, counts, 1 << 30))
-    rows = set(np.where((oi == hot).any(1))[0][:12]) | set(np.where((oi == rare).any(1))[0][:12])
-    rows |= set(np.random.default_rng(0).choice(c.T, 16, replace=False)) | {0, c.T - 1}
-    rows = np.array(sorted(rows))
-    ref = oracle.experts(c.x.f32[rows], c.gate_up.f32, c.down.f32, oi[rows], ow[rows])
-    assert rel_max_err(host(out)[rows], ref) <= BF16_TOL
+    np.testing.assert_allclose(host(w), ow, rtol=1e-6, atol=0)
+    oc, oo, os_ = oracle.dispatch(oi, E)
+    assert np.array_equal(host(counts), oc)
+    assert np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(ss), os_)
+    assert oc.max() > 1000 and (oc == 0).sum() > 0
+    yh = host(y)
+    refs = _per_slot_refs(c, oi, ow)
+    for k in range(K):
+        assert rel_max_err(yh[:, k], refs[:, k]) <= BF16_TOL, k
+    acc = np.zeros((T, c.H), np.float32)
+    for k in range(K):
+        acc = acc + yh[:, k]                        # fp32, slot order, from +0
+    ref = refs.sum(1)
+    assert rel_max_err(acc, ref) <= BF16_TOL
+    got = host(out)
+    assert np.array_equal(got, torch.from_numpy(acc).to(torch.bfloat16).float().numpy())
+    bound, exact = bf16_path_bound(c.x.f32, c.gate_up.f32, c.down.f32, oi, ow)
+    np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / bound))
 
 
 # ---------------------------------------------------------------------------
@@ -373,17 +408,16 @@ def test_block_26b_decode(T):
     assert rel_max_err(out, r["out"]) <= BF16_TOL
 
 
-def test_block_26b_sampled():
-    """The full-size layer (2048 tokens); the oracle evaluates a sample of rows."""
+def test_block_26b_2048_all_rows():
+    """The full-size layer at 2048 tokens (about 128 slots per expert, the
+    tiled GEMMs for the experts and the dense branch), every row: routing
+    exact, the pre-residual output o and the layer output within 2e-2 x RMS of
+    the oracle."""
     b = synth.block_case(2048, seed=0)
-    note("block 26B T=2048")
+    note("block 26B T=2048, all rows")
     out, ffn, idx, w = _run_block(b, True)
-    m = b.moe
-    oi, ow = oracle.router(m.x.f32, m.router_w, m.router_scale, m.per_expert_scale, m.K,
-                           pre_gain=b.g_pre2)
-    assert np.array_equal(idx, oi)
-    rows = np.array(sorted(set(np.random.default_rng(1).choice(m.T, 24, replace=False)) |
-                           {0, m.T - 1}))
-    r = _oracle_block(b, rows)
-    assert rel_max_err(ffn[rows], r["o"]) <= BF16_TOL
-    assert rel_max_err(out[rows], r["out"]) <= BF16_TOL
+    r = _oracle_block(b)
+    assert np.array_equal(idx, r["idx"])
+    np.testing.assert_allclose(w, r["w"], rtol=1e-6)
+    assert rel_max_err(ffn, r["o"]) <= BF16_TOL
+    assert rel_max_err(out, r["out"]) <= BF16_TOL

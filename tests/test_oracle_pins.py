@@ -145,6 +145,79 @@ def test_router_pre_gain_of_one_is_the_plain_router():
     np.testing.assert_allclose(lg1, lg2, rtol=1e-5, atol=1e-6)
 
 
+def _pre_gain_case(T=48, H=256, E=32, K=8, seed=11):
+    """Router input with a strongly non-unit per-channel gain, so that each
+    misreading of the fused pre_feedforward_layernorm_2 moves the logits far
+    more than fp32 rounding does."""
+    c = _case(T=T, H=H, E=E, K=K, seed=seed)
+    g = np.random.default_rng(seed).uniform(0.25, 2.5, H).astype(np.float32)
+    return c, g
+
+
+def _t64(a):
+    return torch.tensor(np.asarray(a, np.float64))
+
+
+def test_router_pre_gain_one_hot_closed_form():
+    """One-hot router weights (W_r[e] = unit vector at channel e) expose the
+    router input itself: logit_e = RMSNorm(RMSNorm(x) * g)[e] * router_scale[e],
+    with both norms from torch's rms_norm in fp64 (the router on
+    pre_feedforward_layernorm_2(x), the diagram of the page's dual-path FFN).
+    Dropping the gain or applying it after the router's own norm fails."""
+    c, g = _pre_gain_case()
+    rw = np.zeros((c.E, c.H), np.float32)
+    rw[np.arange(c.E), np.arange(c.E)] = 1.0
+    _, _, logits = oracle.router(c.x.f32, rw, c.router_scale, c.per_expert_scale, c.K, c.eps,
+                                 pre_gain=g, want_logits=True)
+    H = c.H
+    x = _t64(c.x.f32)
+    v = F.rms_norm(x, (H,), _t64(g), eps=1e-6)
+    exact = (F.rms_norm(v, (H,), eps=1e-6) * _t64(c.router_scale)).numpy()[:, :c.E]
+    # fp32 error: two norms (each a 256-long sum of squares, a sqrt, a divide,
+    # two products) on values of order 1: far below 1e-5 relative
+    np.testing.assert_allclose(logits, exact, rtol=2e-6, atol=2e-7)
+    # the pin has teeth: each plausible misreading is far outside that bound
+    no_gain = (F.rms_norm(F.rms_norm(x, (H,), eps=1e-6), (H,), eps=1e-6)
+               * _t64(c.router_scale)).numpy()[:, :c.E]
+    gain_after = (F.rms_norm(F.rms_norm(x, (H,), eps=1e-6), (H,), eps=1e-6) * _t64(g)
+                  * _t64(c.router_scale)).numpy()[:, :c.E]
+    for wrong in (no_gain, gain_after):
+        assert np.max(np.abs(wrong - exact)) > 1e-2 * np.max(np.abs(exact))
+
+
+def test_router_pre_gain_random_weights_fp64_exact():
+    """Random router weights: the oracle's fp32 logits against the fp64
+    composition (torch rms_norm with the gain, the router's unweighted
+    rms_norm times router_scale, then the projection), within the fp32 error
+    bound of the dot product plus the relative error of the fp32 router
+    input; and the oracle's top-K equals the exact top-K wherever the gap
+    between the K-th and (K+1)-th exact logit exceeds twice that bound."""
+    c, g = _pre_gain_case(T=96, H=512, E=64, K=8, seed=12)
+    idx, _, logits = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale,
+                                   c.K, c.eps, pre_gain=g, want_logits=True)
+    H = c.H
+    v = F.rms_norm(_t64(c.x.f32), (H,), _t64(g), eps=1e-6)
+    vhat = (F.rms_norm(v, (H,), eps=1e-6) * _t64(c.router_scale)).numpy()
+    W = c.router_w.astype(np.float64)
+    exact = vhat @ W.T
+    mag = np.abs(vhat) @ np.abs(W).T
+    # dot product: n * u per term; router input: ~16 roundings of relative u
+    bound = (H + 16) * 2.0 ** -24 * mag + 1e-9
+    assert np.all(np.abs(logits - exact) <= bound)
+    order = np.argsort(-exact, axis=1, kind="stable")
+    top = np.take_along_axis(exact, order, 1)
+    gap = top[:, c.K - 1] - top[:, c.K]
+    tol = 2 * np.take_along_axis(bound, order[:, c.K - 1:c.K + 1], 1).max(1)
+    clear = gap > tol
+    assert clear.sum() >= 0.9 * len(clear)
+    for t in np.nonzero(clear)[0]:
+        assert set(idx[t].tolist()) == set(order[t, :c.K].tolist())
+    # misplacing the gain changes the routing of most tokens
+    _, _, lg_no = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K,
+                                c.eps, want_logits=True)
+    assert np.max(np.abs(lg_no - exact)) > 100 * np.max(bound)
+
+
 # ---------------------------------------------------------------------------
 # Dispatch: numpy bincount and stable argsort
 # ---------------------------------------------------------------------------
