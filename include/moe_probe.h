@@ -17,8 +17,9 @@ extern "C" {
 /* Number of blocks (and of block_xor entries) the read probe uses. */
 int moe_probe_read_blocks(void);
 
-/* Streams `bytes` (a positive multiple of 16; buf 16-byte aligned) once with
- * 16-byte loads and writes the XOR of every 32-bit word each block read to
+/* Streams `bytes` (a positive multiple of 16; buf 16-byte aligned) once,
+ * each block one contiguous chunk, each lane 32 contiguous bytes per step
+ * (two 16-byte loads), and writes the XOR of every 32-bit word each block read to
  * block_xor[moe_probe_read_blocks()]; the XOR of those equals the XOR of all
  * words of the buffer. */
 int moe_probe_stream_read(const void* buf, long long bytes, uint32_t* block_xor, void* stream);

@@ -16,23 +16,41 @@
 namespace {
 
 constexpr int kReadThreads = 256;
+constexpr int kReadBlocks = 256 * 8;
 constexpr int kReadUnroll = 4;
+constexpr int kStep = kReadThreads * 2;  // 16-byte units a block reads per step
 
+// Each block streams one contiguous chunk of the buffer (so the blocks in
+// flight spread over all memory channels), a lane taking 32 contiguous bytes
+// per step (four lanes use a whole 128-byte line at once), kReadUnroll steps
+// of loads issued before their results are used.
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(
     const uint4* __restrict__ p, long long n16, uint32_t* __restrict__ block_xor) {
   uint32_t acc = 0;
-  const long long stride = (long long)gridDim.x * kReadThreads;
-  long long i = (long long)blockIdx.x * kReadThreads + threadIdx.x;
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
-    uint4 v[kReadUnroll];
+  const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+  const long long chunk = (per + kStep - 1) / kStep * kStep;
+  const long long begin = (long long)blockIdx.x * chunk;
+  const long long end = min(begin + chunk, n16);
+  long long i = begin + 2 * threadIdx.x;
+  for (; i + (kReadUnroll - 1) * kStep + 1 < end; i += kReadUnroll * kStep) {
+    uint4 v[kReadUnroll][2];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < kReadUnroll; ++u) {
+      v[u][0] = p[i + u * kStep];
+      v[u][1] = p[i + u * kStep + 1];
+    }
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < kReadUnroll; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc ^= v[u][j].x ^ v[u][j].y ^ v[u][j].z ^ v[u][j].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (; i < end; i += kStep) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    if (i + 1 < end) {
+      const uint4 b = p[i + 1];
+      acc ^= b.x ^ b.y ^ b.z ^ b.w;
+    }
   }
   __shared__ uint32_t red[kReadThreads];
   red[threadIdx.x] = acc;
@@ -78,7 +96,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
 
 extern "C" {
 
-int moe_probe_read_blocks(void) { return 256 * 16; }
+int moe_probe_read_blocks(void) { return kReadBlocks; }
 
 int moe_probe_stream_read(const void* buf, long long bytes, uint32_t* block_xor, void* stream) {
   if (!buf || !block_xor || bytes <= 0 || bytes % 16 != 0) return -1;

@@ -143,6 +143,45 @@ def tiny_case(seed: int = 0, T: int = 16, H: int = 64, E: int = 8, K: int = 2,
                    gu, dn)
 
 
+def moe_x(T: int, seed: int = 0, skew: bool = False, H: int = H_26B, bf16: bool = True,
+          layer: int = 0) -> Tensor:
+    """The experts-only case's input x [T, H] ~ N(0,1) (channel 0 set to 1
+    when skew), exactly as moe_case draws it.  The first rows of a larger
+    draw equal a smaller draw of the same seed."""
+    x = _normal(seed, "x", (T, H), 1.0, layer=layer, bf16=False).f32
+    if skew:
+        x[:, 0] = 1.0
+    if bf16:
+        bits = f32_to_bf16_bits(x)
+        return Tensor(bf16_bits_to_f32(bits).reshape(T, H), bits.reshape(T, H))
+    return Tensor(x)
+
+
+def moe_router_weights(seed: int = 0, skew: bool = False, H: int = H_26B, E: int = E_26B,
+                       weight_std: float = 0.02, router_scale_std: float = 0.0,
+                       layer: int = 0):
+    """(router_w [E,H] fp32, router_scale [H], per_expert_scale [E]) as
+    moe_case draws them."""
+    rw = _normal(seed, "router_w", (E, H), weight_std, layer=layer, bf16=False).f32
+    if skew:
+        rw[:, 0] = _normal(seed, "router_bias", (E,), 1.0, layer=layer, bf16=False).f32
+    if router_scale_std > 0:
+        rs = (1.0 + _normal(seed, "router_scale", (H,), router_scale_std, layer=layer,
+                            bf16=False).f32).astype(np.float32)
+    else:
+        rs = np.ones(H, np.float32)
+    pes = _uniform(seed, "per_expert_scale", (E,), 0.5, 1.5, layer=layer)
+    return rw, rs, pes
+
+
+def moe_expert_weights(seed: int = 0, H: int = H_26B, E: int = E_26B, I: int = I_26B,
+                       weight_std: float = 0.02, bf16: bool = True, layer: int = 0):
+    """(gate_up [E,2I,H], down [E,H,I]) as moe_case draws them."""
+    gu = _normal(seed, "gate_up", (E, 2 * I, H), weight_std, layer=layer, bf16=bf16)
+    dn = _normal(seed, "down", (E, H, I), weight_std, layer=layer, bf16=bf16)
+    return gu, dn
+
+
 def moe_case(T: int, seed: int = 0, skew: bool = False, H: int = H_26B, E: int = E_26B,
              K: int = K_26B, I: int = I_26B, weight_std: float = 0.02,
              bf16: bool = True, router_scale_std: float = 0.0, layer: int = 0) -> MoECase:
@@ -153,25 +192,9 @@ def moe_case(T: int, seed: int = 0, skew: bool = False, H: int = H_26B, E: int =
     channel 0 of every token is set to 1 and router_w[:,0] = b ~ N(0,1), so
     that after the router's RMSNorm each expert's logit is shifted by about b_e.
     """
-    x = _normal(seed, "x", (T, H), 1.0, layer=layer, bf16=False).f32
-    if skew:
-        x[:, 0] = 1.0
-    if bf16:
-        bits = f32_to_bf16_bits(x)
-        xt = Tensor(bf16_bits_to_f32(bits).reshape(T, H), bits.reshape(T, H))
-    else:
-        xt = Tensor(x)
-    rw = _normal(seed, "router_w", (E, H), weight_std, layer=layer, bf16=False).f32
-    if skew:
-        rw[:, 0] = _normal(seed, "router_bias", (E,), 1.0, layer=layer, bf16=False).f32
-    if router_scale_std > 0:
-        rs = (1.0 + _normal(seed, "router_scale", (H,), router_scale_std, layer=layer,
-                            bf16=False).f32).astype(np.float32)
-    else:
-        rs = np.ones(H, np.float32)
-    pes = _uniform(seed, "per_expert_scale", (E,), 0.5, 1.5, layer=layer)
-    gu = _normal(seed, "gate_up", (E, 2 * I, H), weight_std, layer=layer, bf16=bf16)
-    dn = _normal(seed, "down", (E, H, I), weight_std, layer=layer, bf16=bf16)
+    xt = moe_x(T, seed, skew, H, bf16, layer)
+    rw, rs, pes = moe_router_weights(seed, skew, H, E, weight_std, router_scale_std, layer)
+    gu, dn = moe_expert_weights(seed, H, E, I, weight_std, bf16, layer)
     return MoECase(T, H, E, K, I, bf16, 1e-6, xt, rw, rs, pes, gu, dn)
 
 

@@ -52,7 +52,7 @@ def ws_logits_view(ws: torch.Tensor, T: int, E: int) -> torch.Tensor:
     return ws[off: off + 4 * T * E].view(torch.float32).view(T, E)
 
 
-def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False):
+def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False, out_rounded=True):
     """Per-element error bound of the bf16 expert path against the exact result.
 
     The bf16 path rounds twice: h = gelu(gate) * up is rounded to bf16 before
@@ -62,7 +62,9 @@ def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False):
     fp32 accumulation error (taken as 1e-5 of the summed magnitudes).  Inputs
     are the exactly widened bf16 values.  With bf16_slots the K per-slot
     outputs are also rounded to bf16 before their sum, which adds at most
-    2^-8 |w_k y_k| <= 2^-8 |w_k| (|W_d[e_k]| @ |h_k|) per slot.
+    2^-8 |w_k y_k| <= 2^-8 |w_k| (|W_d[e_k]| @ |h_k|) per slot.  With
+    out_rounded=False the result is taken before its final rounding (an fp32
+    slot output or an fp32 sum of slots), which drops the 2^-8 |out| term.
     Returns (bound [T,H], exact [T,H])."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
@@ -86,7 +88,8 @@ def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False):
         exact[tt] += wk * (hh @ wd.T)
         hterm[tt] += np.abs(wk) * (np.abs(hh) @ np.abs(wd).T)
     mag = hterm
-    bound = 2.0 ** -8 * np.abs(exact) * 1.001 + 2.0 ** -8 * hterm + 1e-5 * mag
+    bound = (2.0 ** -8 * np.abs(exact) * 1.001 if out_rounded else 0.0) + \
+        2.0 ** -8 * hterm + 1e-5 * mag
     if bf16_slots:
         bound += 2.0 ** -8 * hterm * 1.001
     return bound, exact

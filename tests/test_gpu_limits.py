@@ -51,8 +51,9 @@ def test_largest_batch_26b():
     """65536 tokens (the largest T; 524288 token-slots) through the router,
     the dispatch and the tiled expert GEMMs at 26B shapes: logits bit for bit,
     routing and dispatch exact, sampled rows of the output within 2e-2 x RMS
-    of the oracle, and whole row tiles slot by slot (the hottest expert's
-    ragged last tile, every row of the rarest expert, the first tile)."""
+    of the oracle, and whole row tiles slot by slot within the per-element
+    rounding bound (the hottest expert's ragged last tile, every row of the
+    rarest expert, the first tile)."""
     T = 65536
     c = synth.moe_case(T, seed=6)
     note(f"largest batch T={T}: router and dispatch")
@@ -94,4 +95,7 @@ def test_largest_batch_26b():
     yh = host(y.view(T * c.K, c.H)[torch.from_numpy(picks.astype(np.int64)).cuda()])
     ref = oracle.experts(c.x.f32[tok], c.gate_up.f32, c.down.f32, oi[tok, kk][:, None],
                          ow[tok, kk][:, None])
-    assert rel_max_err(yh, ref) <= BF16_TOL
+    bound, exact = bf16_path_bound(c.x.f32[tok], c.gate_up.f32, c.down.f32,
+                                   oi[tok, kk][:, None], ow[tok, kk][:, None], out_rounded=False)
+    np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
+    assert np.all(np.abs(yh - ref) <= bound), float(np.max(np.abs(yh - ref) / bound))

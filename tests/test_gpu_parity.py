@@ -275,13 +275,16 @@ def test_experts_26b_prefill_skewed_all_rows():
     (the calls of moe_forward).
 
     - routing, counts, offsets and the slot permutation exact;
-    - every fp32 slot, and the in-order fp32 sum of each token's slots, within
-      2e-2 x RMS of the oracle;
+    - the in-order fp32 sum of each token's slots within 2e-2 x RMS of the
+      oracle, and every fp32 slot within its per-element rounding bound;
     - the bf16 output equal to that sum rounded once to nearest-even, bit for
       bit, and within the per-element rounding bound of the bf16 path.
     The whole-tensor bar is not put on the bf16 output itself: under this
     load the largest outputs reach ~13 x RMS, so rounding the exact result to
-    bf16 alone moves it by 0.026 x RMS."""
+    bf16 alone moves it by 0.026 x RMS.  Nor on a single slot: h rounded to
+    bf16 before the down projection moves the first slot by up to 0.023 x its
+    RMS here (a CPU model of that one rounding gives the same), while the sum
+    of the eight slots, the experts' result, stays near 0.015."""
     c = synth.moe_case(4096, seed=0, skew=True)
     note("experts 26B prefill 4096 skewed, all rows")
     d = _dims(c)
@@ -312,7 +315,11 @@ def test_experts_26b_prefill_skewed_all_rows():
     yh = host(y)
     refs = _per_slot_refs(c, oi, ow)
     for k in range(K):
-        assert rel_max_err(yh[:, k], refs[:, k]) <= BF16_TOL, k
+        bk, ek = bf16_path_bound(c.x.f32, c.gate_up.f32, c.down.f32, oi[:, k:k + 1],
+                                 ow[:, k:k + 1], out_rounded=False)
+        np.testing.assert_allclose(ek, refs[:, k], rtol=1e-9, atol=1e-12)
+        err = np.abs(yh[:, k] - refs[:, k])
+        assert np.all(err <= bk), (k, float(np.max(err / bk)))
     acc = np.zeros((T, c.H), np.float32)
     for k in range(K):
         acc = acc + yh[:, k]                        # fp32, slot order, from +0
