@@ -318,6 +318,23 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
                 const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
                 float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as moe_forward (bit for bit: the same kernels),
+ * but the workspace is a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (allocated with the code object when
+ * the library loads on a device, held until the process ends) instead of a
+ * caller buffer; the call makes no allocation of its own.  Sizes whose
+ * workspace (moe_workspace_size) exceeds that array are refused with
+ * MOE_ERR_WORKSPACE (at 26B-A4B shapes: up to 527 tokens).  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (two
+ * streams, or threads) race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                        const float* router_scale, const float* per_expert_scale,
+                        const void* w_gate_up, const void* w_down, void* out,
+                        int32_t* topk_idx, float* topk_w, void* stream);
+
 /* One dual-path feed-forward layer (the page's diagram):
  *   xd = RMSNorm_pre(x); xm = RMSNorm_pre2(x)
  *   moe = experts(xm) routed on pre_feedforward_layernorm_2(x) (moe_router)

@@ -172,6 +172,43 @@ int check_ws(const moe_dims* d, int32_t T, const void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing --------------------
+// moe_forward_noalloc takes its workspace from this file-scope device array
+// instead of a caller's buffer.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is only a
+// host-side stand-in: the device address of a GPU's copy comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept; only that address is ever handed to kernels.  Every call on a GPU
+// shares the array and finds the last call's contents; the path clears what
+// it needs cleared itself (the router's completion counter is zeroed by its
+// logits kernel), and calls that overlap on one GPU race.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+hipError_t noalloc_scratch(void*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+int run_forward(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                const float* router_scale, const float* per_expert_scale,
+                const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
+                float* topk_w, void* ws, hipStream_t s);
+
 // ---- launch sequences (arguments already checked) -------------------------
 
 // Router, and when counts is not null the dispatch as well (fused into the
@@ -651,7 +688,43 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
   REQUIRE_PTR(per_expert_scale); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(out);
   OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
   if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_forward(dims, T, x, router_w, router_scale, per_expert_scale, w_gate_up, w_down,
+                     out, topk_idx, topk_w, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                        const float* router_scale, const float* per_expert_scale,
+                        const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
+                        float* topk_w, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(router_w); REQUIRE_PTR(router_scale);
+  REQUIRE_PTR(per_expert_scale); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(out);
+  OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
+  const size_t need = layout(dims, T).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: T=%d needs %zu bytes of scratch, the library's array "
+                "holds %zu",
+                T, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = noalloc_scratch(ws);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc (scratch address)");
+  return run_forward(dims, T, x, router_w, router_scale, per_expert_scale, w_gate_up, w_down,
+                     out, topk_idx, topk_w, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_forward(const moe_dims* dims, int32_t T, const void* x, const float* router_w,
+                const float* router_scale, const float* per_expert_scale,
+                const void* w_gate_up, const void* w_down, void* out, int32_t* topk_idx,
+                float* topk_w, void* ws, hipStream_t s) {
+  int rc;
   const Layout L = layout(dims, T);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
   float* w = topk_w ? topk_w : at<float>(ws, L.w);
@@ -666,6 +739,10 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
     return rc;
   return run_combine(dims, T, y, nullptr, out, s);
 }
+
+}  // namespace
+
+extern "C" {
 
 int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
                      const gemma4_ffn_weights* wt, void* out, float* ffn_out,

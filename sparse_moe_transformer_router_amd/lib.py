@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_W_INT8, MOE_W_FP8, MOE_W_MXFP4 = 1, 2, 3
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # the no-allocation entry point's device array
 
 
 class MoeDims(ctypes.Structure):
@@ -71,6 +72,7 @@ def _load():
     L.moe_expert_down.argtypes = [D, I32] + [P] * 7
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
+    L.moe_forward_noalloc.argtypes = [D, I32] + [P] * 10
     L.moe_quantize_int8.argtypes = [ctypes.c_int64, I32, P, P, P, P]
     L.moe_expert_ffn_int8.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.moe_quantize.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P]
@@ -84,7 +86,7 @@ def _load():
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
               "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch",
               "moe_quantize", "moe_dequantize", "moe_expert_ffn_q", "moe_expert_gate_up_timed",
-              "gemma4_ffn_block_q"):
+              "gemma4_ffn_block_q", "moe_forward_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -249,6 +251,15 @@ def moe_forward(d, T, x, router_w, router_scale, per_expert_scale, w_gate_up, w_
                             _ptr(per_expert_scale), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
                             _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
                             ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_forward_noalloc(d, T, x, router_w, router_scale, per_expert_scale, w_gate_up, w_down,
+                        out, topk_idx, topk_w, stream=None):
+    """moe_forward with the library's own device scratch array as workspace."""
+    _check(_lib.moe_forward_noalloc(ctypes.byref(d), T, _ptr(x), _ptr(router_w),
+                                    _ptr(router_scale), _ptr(per_expert_scale), _ptr(w_gate_up),
+                                    _ptr(w_down), _ptr(out), _ptr(topk_idx), _ptr(topk_w),
+                                    _stream(stream)))
 
 
 def ffn_weights(g_pre, g_pre2, g_post1, g_post2, g_post, dense_gate, dense_up, dense_down,

@@ -285,3 +285,22 @@ def test_timed_gate_up_requires_both_events():
                                       FAKE, None, FAKE, FAKE) == lib_mod.MOE_ERR_UNSUPPORTED
     assert L.moe_expert_gate_up_timed(ctypes.byref(d), 4, MISALIGNED, FAKE, FAKE, FAKE, FAKE,
                                       None, FAKE, FAKE) == lib_mod.MOE_ERR_ARG
+
+
+def test_noalloc_forward_validates_on_the_host():
+    """moe_forward_noalloc: a no-op at 0 tokens, and the refusals (pointers,
+    a workspace larger than the library's device array) come before any HIP
+    call."""
+    d = D(dense_inter=0)
+    dp = ctypes.byref(d)
+    f = L.moe_forward_noalloc
+    assert f(dp, 0, None, None, None, None, None, None, None, None, None, None) == lib_mod.MOE_OK
+    assert f(dp, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+             None) == lib_mod.MOE_ERR_ARG
+    assert f(dp, 4, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+             None) == lib_mod.MOE_ERR_ARG
+    assert L.moe_workspace_size(dp, 527) <= lib_mod.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_workspace_size(dp, 528) > lib_mod.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(dp, 528, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+             None) == lib_mod.MOE_ERR_WORKSPACE
+    assert "scratch" in lib_mod.last_error()
