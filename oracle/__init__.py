@@ -69,6 +69,12 @@ def lib():
                      "oracle_quantize_mxfp4_rows", "oracle_dequantize_mxfp4_rows"):
             getattr(L, name).argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
             getattr(L, name).restype = None
+        L.oracle_quantize_mx8_rows.argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
+        L.oracle_quantize_mx8_rows.restype = None
+        L.oracle_dequantize_mx8_rows.argtypes = [ctypes.c_longlong, _I, _P, _P, _P]
+        L.oracle_dequantize_mx8_rows.restype = None
+        L.oracle_experts_mx8.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.oracle_experts_mx8.restype = None
         L.oracle_e4m3_value.argtypes = [_I]
         L.oracle_e4m3_value.restype = ctypes.c_double
         L.oracle_e2m1_value.argtypes = [_I]
@@ -285,3 +291,54 @@ def experts_mxfp4(xin, gate_up_q, gate_up_e8, down_q, down_e8, idx, w):
     """The sparse expert loop (fp64) on the dequantized MXFP4 weights."""
     return experts(xin, dequantize_mxfp4(gate_up_q, gate_up_e8),
                    dequantize_mxfp4(down_q, down_e8), idx, w)
+
+
+def quantize_mx8(v):
+    """MXFP8 along the last axis (a multiple of 32): returns (E4M3 codes uint8,
+    same shape; E8M0 scale codes uint8 [..., n/32])."""
+    v = _f64(v)
+    shape = v.shape
+    n = shape[-1]
+    assert n % 32 == 0
+    q = np.zeros(shape, np.uint8)
+    e8 = np.zeros(shape[:-1] + (n // 32,), np.uint8)
+    lib().oracle_quantize_mx8_rows(int(np.prod(shape[:-1])), n, _p(v), _p(q), _p(e8))
+    return q, e8
+
+
+def dequantize_mx8(q, e8):
+    """value(code) * 2^(e8 - 127), exact (fp64)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    e8 = np.ascontiguousarray(e8, dtype=np.uint8)
+    out = np.zeros(q.shape, np.float64)
+    lib().oracle_dequantize_mx8_rows(int(np.prod(q.shape[:-1])), q.shape[-1], _p(q), _p(e8),
+                                     _p(out))
+    return out
+
+
+def experts_mx8(xin, gate_up, down, idx, w):
+    """The sparse expert loop (fp64) with MXFP8 activations: the input row and
+    the gated product are each replaced by their MXFP8 value before their
+    projections; gate_up / down are weight values.  Returns [T,H] fp64."""
+    x = _f64(xin)
+    T, H = x.shape
+    gu, dn = _f32(gate_up), _f32(down)
+    E, I2, _ = gu.shape
+    idx = _i32(idx)
+    K = idx.shape[1]
+    w = _f32(w)
+    out = np.zeros((T, H), np.float64)
+    lib().oracle_experts_mx8(T, H, E, K, I2 // 2, _p(x), _p(gu), _p(dn), _p(idx), _p(w), _p(out))
+    return out
+
+
+def experts_fp8_mx8(xin, gate_up_q, gate_up_s, down_q, down_s, idx, w):
+    """E4M3 per-channel weights with MXFP8 activations (fp64 loop)."""
+    return experts_mx8(xin, dequantize_fp8(gate_up_q, gate_up_s),
+                       dequantize_fp8(down_q, down_s), idx, w)
+
+
+def experts_mxfp4_mx8(xin, gate_up_q, gate_up_e8, down_q, down_e8, idx, w):
+    """MXFP4 weights with MXFP8 activations (fp64 loop)."""
+    return experts_mx8(xin, dequantize_mxfp4(gate_up_q, gate_up_e8),
+                       dequantize_mxfp4(down_q, down_e8), idx, w)

@@ -493,6 +493,119 @@ void oracle_dequantize_mxfp4_rows(long long rows, int cols, const uint8_t* q, co
     }
 }
 
+/* -------------------------------------------------------------------------
+ * Activations for the 8-bit / 4-bit matrix cores.  Running the E4M3 and
+ * MXFP4 experts of the page's low-precision options on matrix units that
+ * multiply 8-bit or 4-bit operands natively means the activations enter the
+ * product in 8 bits as well (the page gives no rule for them; its int8
+ * variant kept the activations wide).  Reading taken: MXFP8 in the OCP
+ * Microscaling sense, the same block structure as the MXFP4 weights: blocks
+ * of 32 consecutive values along the contraction share one E8M0 scale
+ * 2^shared with shared = floor(log2(max |v|)) - 8 (8 is E4M3's largest
+ * exponent), clamped to [-127, 127]; each element is the E4M3 value nearest
+ * to v / 2^shared (ties to the even mantissa, magnitudes past 448 take 448)
+ * with the sign of v; a block of zeros gets scale code 0 and zero codes.
+ * Both the expert input x (blocks along H) and the gated product h = GELU(g)
+ * * u (blocks along I) are quantized so before their projections; the
+ * products and sums themselves are exact (fp64 here).
+ * ------------------------------------------------------------------------- */
+static void mx8_block(const double* v, int n, uint8_t* q, uint8_t* e8) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  int shared = -127;
+  if (amax > 0.0) {
+    shared = (int)floor(log2(amax)) - 8;
+    while (ldexp(1.0, shared + 8) > amax) --shared;
+    while (ldexp(1.0, shared + 9) <= amax) ++shared;
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+  }
+  *e8 = (uint8_t)(amax > 0.0 ? shared + 127 : 0);
+  for (int i = 0; i < n; ++i) {
+    int code = 0;
+    if (amax > 0.0) {
+      code = nearest_code(fabs(v[i]) / ldexp(1.0, shared), 0x7F, oracle_e4m3_value);
+      if (v[i] < 0.0) code |= 0x80;
+    }
+    q[i] = (uint8_t)code;
+  }
+}
+
+static double mx8_value(uint8_t code, uint8_t e8) {
+  return oracle_e4m3_value(code) * ldexp(1.0, (int)e8 - 127);
+}
+
+/* MXFP8 along each row (cols % 32 == 0): codes q [rows, cols], E8M0 scale
+ * codes e8 [rows, cols / 32]. */
+void oracle_quantize_mx8_rows(long long rows, int cols, const double* v, uint8_t* q,
+                              uint8_t* e8) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r)
+    for (int b = 0; b < nb; ++b)
+      mx8_block(v + r * cols + 32 * b, 32, q + r * cols + 32 * b, e8 + r * nb + b);
+}
+
+/* value(code) * 2^(e8 - 127), exact in fp64. */
+void oracle_dequantize_mx8_rows(long long rows, int cols, const uint8_t* q, const uint8_t* e8,
+                                double* out) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c)
+      out[r * cols + c] = mx8_value(q[r * cols + c], e8[r * nb + c / 32]);
+}
+
+/* In place: each row of 32-blocks replaced by its MXFP8 value. */
+static void mx8_round_row(double* v, int n) {
+  uint8_t q[32], e8;
+  for (int b = 0; b < n; b += 32) {
+    mx8_block(v + b, 32, q, &e8);
+    for (int i = 0; i < 32; ++i) v[b + i] = mx8_value(q[i], e8);
+  }
+}
+
+/* The sparse expert loop with MXFP8 activations (H % 32 == 0, I % 32 == 0):
+ * as oracle_experts, but the token's input row is replaced by its MXFP8
+ * value before the gate / up projections, and the gated product a (length
+ * I) by its MXFP8 value before the down projection.  gate_up / down are the
+ * weights' values (the dequantized codes). */
+void oracle_experts_mx8(int T, int H, int E, int K, int I, const double* xin,
+                        const float* gate_up, const float* down, const int32_t* idx,
+                        const float* w, double* out) {
+  (void)E;
+#pragma omp parallel
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)(2 * H + I));
+    double* a = y + H;
+    double* xq = a + I;
+#pragma omp for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+      double* o = out + (size_t)t * H;
+      memcpy(xq, xin + (size_t)t * H, sizeof(double) * (size_t)H);
+      mx8_round_row(xq, H);
+      for (int h = 0; h < H; ++h) o[h] = 0.0;
+      for (int k = 0; k < K; ++k) {
+        int e = idx[(size_t)t * K + k];
+        const float* wg = gate_up + (size_t)e * 2 * I * H;
+        const float* wu = wg + (size_t)I * H;
+        const float* wd = down + (size_t)e * H * I;
+        for (int i = 0; i < I; ++i) {
+          double g = dot_f64(xq, wg + (size_t)i * H, H);
+          double u = dot_f64(xq, wu + (size_t)i * H, H);
+          a[i] = oracle_gelu_tanh(g) * u;
+        }
+        mx8_round_row(a, I);
+        for (int j = 0; j < H; ++j) y[j] = dot_f64(a, wd + (size_t)j * I, I);
+        double wk = (double)w[(size_t)t * K + k];
+        for (int h = 0; h < H; ++h) o[h] += wk * y[h];
+      }
+    }
+    free(y);
+  }
+}
+
 /* Number of OpenMP threads the parallel loops use. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -12,11 +12,12 @@
 // group whose rows are the tokens themselves.
 //
 // bf16 path at prefill sizes (decode sizes use the weight-streaming kernels):
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation on 128 x 128 block tiles;
-// A rows are gathered from the token matrix while they are staged into LDS;
-// A and weight tiles are double-buffered in LDS.  gate_up's epilogue applies
-// GELU(gate) * up and rounds h to bf16; down's epilogue multiplies each row by
-// its routing weight and writes it to the slot-major output.
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation on 256 x 256 block tiles
+// of 16 waves; A rows are gathered from the token matrix by the per-lane
+// source addresses of direct global -> LDS copies into a 4-stage ring shared
+// with the weight tiles.  gate_up's epilogue applies GELU(gate) * up and
+// rounds h to bf16; down's epilogue multiplies each row by its routing weight
+// and writes it to the slot-major output; both leave through LDS-staged rows.
 // fp32 path (debug): the same tiling idea on the vector ALUs in fp32.
 #include <type_traits>
 
@@ -47,9 +48,11 @@ __device__ __forceinline__ bool get_row_tile(bool ident, int rows, const int32_t
 // Block tile: BM (256 or 128) rows x 256 output columns (gate_up: 128 gate
 // columns and the matching 128 up columns), k-tile 32.  Each k-tile of A (gathered rows) and B
 // (weight rows) goes global -> LDS directly (global_load_lds, 16 B per lane)
-// into a ring of NSTAGE stages of 32 KB, NSTAGE - 1 tiles in flight while one
-// is consumed.  An LDS row is 64 B (32 k values); the 16-B chunk c of row r is
-// stored at position c ^ ((r >> 2) & 3), which keeps the fragment reads of
+// into a ring of NSTAGE stages of 32 KB.  A stage is refilled as soon as the
+// barrier in the middle of its k-tile has passed (its last fragments were
+// read in the first half), so up to NSTAGE - 1 tiles are in flight while one
+// is consumed, and a tile is requested 2.5 k-tiles before it is needed.  An
+// LDS row is 64 B (32 k values); the 16-B chunk c of row r is stored at position c ^ ((r >> 2) & 3), which keeps the fragment reads of
 // v_mfma_f32_32x32x16_bf16 free of bank conflicts.  WM x WN waves each own a
 // (BM / WM) x (256 / WN) sub-tile.  In a fixed issue order, a wave reads the
 // fragments of the next half k-tile and issues its share of the next
@@ -243,10 +246,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c[i], c[TM + j], acc[i][j], 0, 0, 0);
     };
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
+    for (int s = 0; s < NSTAGE; ++s)
 #pragma unroll
       for (int j = 0; j < LPW; ++j) copy(s, j);
-    wait_vmem<(NSTAGE - 2) * LPW>();
+    wait_vmem<(NSTAGE - 1) * LPW>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int f = 0; f < NF; ++f) rd(smem, 0, f, f0);
@@ -263,17 +266,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_lds();
-      // tile kt+1 has landed for every wave; ring slot (kt-1) % NSTAGE is free
-      wait_vmem<(NSTAGE - 3) * LPW>();
+      // tile kt+1 has landed for every wave; after the barrier no wave reads
+      // tile kt any more, so its ring slot takes tile kt+NSTAGE
+      wait_vmem<(NSTAGE - 2) * LPW>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // second half: MFMAs on f1, reads of tile kt+1's first-half fragments,
-      // copies of tile kt+NSTAGE-1
+      // copies of tile kt+NSTAGE
 #pragma unroll
       for (int m = 0; m < NMF; ++m) {
         if (m < NF) rd(sn, 0, m, f0);
         mf(m, f1);
-        if (m >= NMF - LPW) copy(kt + NSTAGE - 1, m - (NMF - LPW));
+        if (m >= NMF - LPW) copy(kt + NSTAGE, m - (NMF - LPW));
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_lds();
