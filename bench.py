@@ -370,10 +370,13 @@ QUANT_FORMATS = {
 }
 
 
-def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed):
+def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed, native=False):
     """Decode with the experts' weights quantized on the GPU (from the same
-    weight copies) into one of QUANT_FORMATS: route, experts, combine."""
+    weight copies) into one of QUANT_FORMATS: route, experts, combine.  With
+    native, the experts run on the 8-bit / 4-bit matrix instructions with
+    MXFP8 activations (moe_expert_ffn_mx) instead of widening the codes."""
     fmt, per_byte, sbytes, desc = QUANT_FORMATS[name]
+    experts = lib.moe_expert_ffn_mx if native else lib.moe_expert_ffn_q
 
     def quant(wt):
         rows, n = wt.numel() // wt.shape[-1], wt.shape[-1]
@@ -401,8 +404,7 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed)
         lib.moe_route(d, T, x, rw, rs, pes, None, r.idx, r.w, r.counts, r.offsets, r.sorted, r.ws)
         if ev is not None:
             ev[1].record()
-        lib.moe_expert_ffn_q(d, fmt, T, x, guq, gus, dnq, dns, r.w, r.offsets, r.sorted, r.y,
-                             r.ws)
+        experts(d, fmt, T, x, guq, gus, dnq, dns, r.w, r.offsets, r.sorted, r.y, r.ws)
         if ev is not None:
             ev[2].record()
         lib.moe_combine(d, T, r.y, None, r.out)
@@ -419,7 +421,7 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed)
         step(warmup + i)
     b.record()
     torch.cuda.synchronize()
-    WINDOWS[f"{name}_decode_{T}"] = (t0, time.perf_counter())
+    WINDOWS[f"{name}{'_native' if native else ''}_decode_{T}"] = (t0, time.perf_counter())
     ms = a.elapsed_time(b) / steps
     # per-segment times from an instrumented pass after the timed region
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -440,6 +442,8 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed)
     step_bytes = U * per_expert + ROUTER_BYTES + 2 * T * H * 2
     return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
             "distinct_experts": U, "kernel_ms": seg, "weights": desc,
+            "matrix_path": ("8-bit / 4-bit scaled matrix instructions, MXFP8 activations"
+                            if native else "codes widened to bf16, bf16 matrix instructions"),
             "expert_bytes_per_expert": per_expert,
             "experts_gbs": expert_bytes / (seg["experts"] * 1e-3) / 1e9,
             "experts_hbm_frac": expert_bytes / (seg["experts"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -1056,6 +1060,14 @@ def main():
         quant[name] = quant_decode_measure(torch, lib, wl, name, args.batch, args.steps,
                                            args.warmup, args.xbatches, args.seed)
         done(f"{name} experts decode")
+    native = {}
+    for name in (("fp8", "mxfp4") if args.quant else ()):
+        native[name] = {}
+        for b in sorted({1, 8, args.batch, 256}):
+            native[name][str(b)] = quant_decode_measure(torch, lib, wl, name, b, args.steps,
+                                                        args.warmup, args.xbatches, args.seed,
+                                                        native=True)
+        done(f"{name} experts on the 8/4-bit matrix instructions, decode")
 
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
     done("tiny fp32")
@@ -1087,7 +1099,8 @@ def main():
     # A probe figure is a ceiling only if no kernel of this run beat it; the
     # fractions against it are reported only then.
     best_read = max([r["gate_up_gbs"] for r in [head, *sweep.values()]] +
-                    [r["experts_gbs"] for r in quant.values()])
+                    [r["experts_gbs"] for r in quant.values()] +
+                    [v["experts_gbs"] for m in native.values() for v in m.values()])
     ach["read_probe_is_ceiling"] = ach["hbm_read_gbs"] >= best_read
     ach["best_kernel_read_gbs"] = best_read
     read_ceiling = ach["hbm_read_gbs"] if ach["read_probe_is_ceiling"] else None
@@ -1097,7 +1110,7 @@ def main():
     if prefill is not None:
         prefill["grouped_gemm_frac_of_achievable_mfma"] = (prefill["grouped_gemm_tflops"] /
                                                            ach["mfma_bf16_tflops"])
-    for r in quant.values():
+    for r in [*quant.values(), *[v for m in native.values() for v in m.values()]]:
         r["experts_frac_of_achievable_read"] = (r["experts_gbs"] / read_ceiling
                                                 if read_ceiling else None)
 
@@ -1145,6 +1158,7 @@ def main():
         "prefill": prefill,
         "dense_masked_ablation": dense_mask or None,
         "quantized_experts_decode": quant,
+        "quantized_experts_native_decode": native or None,
         "tiny_f32": tiny,
         "block": block,
         "block_decode_quantized": block_q,

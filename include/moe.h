@@ -90,7 +90,10 @@ typedef enum moe_status {
 typedef enum moe_wformat {
   MOE_W_INT8 = 1,
   MOE_W_FP8 = 2,
-  MOE_W_MXFP4 = 3
+  MOE_W_MXFP4 = 3,
+  MOE_W_MXFP8 = 4   /* E4M3 codes with one E8M0 scale per 32 consecutive values
+                     * of a row (OCP Microscaling MXFP8): the activation format
+                     * of moe_expert_ffn_mx; moe_quantize / moe_dequantize only */
 } moe_wformat;
 
 typedef enum moe_dtype {
@@ -292,6 +295,13 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
  * (no tiled kernels for these formats), so batches of T <= 256 tokens only,
  * act dtype bf16, else MOE_ERR_UNSUPPORTED.
  *
+ *   MOE_W_MXFP8  q uint8 [rows, cols], scale uint8 [rows, cols / 32]: per
+ *                32-value block, shared = floor(log2 max |w|) - 8 clamped to
+ *                [-127, 127], scale code = shared + 127, element = E4M3
+ *                nearest to w / 2^shared (ties to the even mantissa, 448 at
+ *                most); a zero block gives scale code 0 and codes 0.  cols %
+ *                32 == 0.  Dequantized: value * 2^(scale - 127), exact.  Not
+ *                a weight format of moe_expert_ffn_q / gemma4_ffn_block_q.
  * All three: device pointers, 16-byte aligned; MOE_ERR_ARG for an unknown
  * format, bad sizes or pointers. */
 int moe_quantize(int32_t fmt, int64_t rows, int32_t cols, const void* w, void* q, void* scale,
@@ -303,6 +313,29 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
                      const void* w_down_scale, const float* topk_w,
                      const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* The E4M3 and MXFP4 experts on gfx950's 8-bit / 4-bit matrix instructions
+ * (the FP8 and microscaling fp4 options of the page "Porting a 128-expert MoE
+ * (Gemma-4 26B-A4B) to AWS Inferentia2", section "The fp4 rabbit hole (two
+ * of them, both dead ends)"): the weights are multiplied in their own format,
+ * never widened.  The activations enter those products in 8 bits too, as
+ * MXFP8 (MOE_W_MXFP8 above: per block of 32 consecutive values along the
+ * contraction, shared = floor(log2 max |v|) - 8 clamped to [-127, 127],
+ * element = the E4M3 value nearest to v / 2^shared, ties to the even
+ * mantissa, saturating at 448; a zero block gets scale code 0): the expert
+ * input x before gate_up, and the gated product h = gelu_tanh(gate) * up
+ * (from its fp32 value) before down.  Products accumulate in fp32; E4M3
+ * weights' row scales multiply the k-sums.  So y_slots[t,k,:] = topk_w[t,k]
+ * * down[e] MX(gelu_tanh(gate[e] MX(x_t)) * (up[e] MX(x_t))), MX() being the
+ * MXFP8 value.  fmt: MOE_W_FP8 or MOE_W_MXFP4, weights and scales as
+ * moe_quantize lays them out.  act dtype bf16; up to 256 tokens with at most
+ * 16 rows per expert on average (T * top_k <= 16 * num_experts), else
+ * MOE_ERR_UNSUPPORTED; the workspace as for moe_expert_ffn. */
+int moe_expert_ffn_mx(const moe_dims* dims, int32_t fmt, int32_t T, const void* x,
+                      const void* w_gate_up_q, const void* w_gate_up_scale, const void* w_down_q,
+                      const void* w_down_scale, const float* topk_w,
+                      const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* The experts' scatter-add: out[t] = sum_{k=0..K-1} y_slots[t,k] (fp32, k
  * ascending, no atomics) + addend[t] (if addend is not NULL).

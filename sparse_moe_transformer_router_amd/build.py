@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
-SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_stream.hip", "combine.hip", "quant.hip",
-           "moe_api.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_stream.hip", "expert_mx.hip",
+           "combine.hip", "quant.hip", "moe_api.cpp"]
 # Measurement probes (achievable read and MFMA rates), a library of their own.
 PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

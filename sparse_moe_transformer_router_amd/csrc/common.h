@@ -116,6 +116,49 @@ __device__ __forceinline__ int xcd_item(int b, int n_items) {
   return l < cnt ? x * q + min(x, r) + l : -1;
 }
 
+// The block's work item: row tile (of at most bm rows of one expert, or of
+// the tokens when ident) and column group cg of CG, from the XCD-aware
+// mapping of xcd_item over the real number of items, so that the column
+// groups of a row tile (which read the same activation rows) share one XCD's
+// L2.  1-D grid of at least (row tile bound) * CG blocks.
+__device__ __forceinline__ bool stream_item(bool ident, int rows, const int32_t* offsets, int E,
+                                            int bm, int CG, int& e, int& row0, int& row1,
+                                            int& cg) {
+  RowTileScan sc;
+  int R;
+  if (ident) {
+    R = (rows + bm - 1) / bm;
+  } else {
+    row_tile_scan(offsets, E, bm, sc);
+    R = sc.total;
+  }
+  const int item = xcd_item(blockIdx.x, R * CG);
+  if (item < 0) return false;
+  const int rt = item / CG;
+  cg = item % CG;
+  if (ident) {
+    e = 0;
+    row0 = rt * bm;
+    row1 = min(row0 + bm, rows);
+  } else {
+    row_tile_lookup(sc, offsets, bm, rt, e, row0, row1);
+  }
+  // the same for every lane: scalar registers, scalar branches
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  row1 = __builtin_amdgcn_readfirstlane(row1);
+  cg = __builtin_amdgcn_readfirstlane(cg);
+  return true;
+}
+
+// Upper bound on the number of bm-row tiles over all groups (host side).
+inline int tile_count_bound(bool ident, int rows, int T, int E, int bm) {
+  if (ident) return (rows + bm - 1) / bm;
+  const long long a = ((long long)rows + (long long)E * (bm - 1)) / bm;
+  const long long b = (long long)E * ((T + bm - 1) / bm);
+  return (int)(a < b ? a : b);
+}
+
 // Returns false if `tile` is past the last tile.
 __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E,
                                               int bm, int tile, int& e_out, int& row0,

@@ -1,0 +1,534 @@
+// Experts on the 8-bit / 4-bit matrix cores: the E4M3 and MXFP4 expert
+// weights of the low-precision options on the page "Porting a 128-expert MoE
+// (Gemma-4 26B-A4B) to AWS Inferentia2" (section "The fp4 rabbit hole (two of
+// them, both dead ends)"), multiplied in their own formats by gfx950's scaled
+// matrix instructions (v_mfma_scale_f32_*_f8f6f4), with no widening of the
+// weight stream.  The activations enter those products as MXFP8: E4M3
+// elements with one E8M0 scale per 32 consecutive values along the
+// contraction, the block structure of the MXFP4 weights (the OCP
+// Microscaling format); the expert input x is quantized so before gate_up
+// (a kernel of its own), the gated product h in gate_up's epilogue, from its
+// fp32 value.
+//
+// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (checked on the part
+// against a host model): lane l holds row (or column) l % 16 and lane group
+// g = l / 16; an 8-bit operand's 32 bytes are k = 16g .. 16g + 15 followed
+// by k = 64 + 16g .. 64 + 16g + 15; a 4-bit operand's 16 bytes are k = 32g
+// .. 32g + 31, the even k in the low nibble; the lane's scale byte (byte 0
+// of its scale operand) covers k = 32g .. 32g + 31 of its row, whatever the
+// data layout.  For the 32x32x64 form: row l % 32, group g = l / 32, an
+// 8-bit operand's bytes k = 16g .. 16g + 15 then 32 + 16g .. 32 + 16g + 15,
+// a 4-bit operand's k = 32g .. 32g + 31.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "wformat.h"
+
+namespace moe {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Operand format codes of the scaled matrix instructions.
+constexpr int kOpFp8 = 0, kOpFp4 = 4;
+constexpr uint32_t kUnitScale = 127;  // E8M0 code of 1.0
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantization of bf16 rows (cols % 32 == 0): one thread per 32-value
+// block.  shared = floor(log2 max |v|) - 8 (E4M3's largest exponent),
+// clamped to [-127, 127]; element = e4m3_encode(v / 2^shared), exact
+// scaling; a block of zeros gets scale code 0 and zero codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx8_quantize_kernel(long long nblocks, int cols,
+                                                           const bf16* __restrict__ in,
+                                                           uint8_t* __restrict__ q,
+                                                           uint8_t* __restrict__ e8) {
+  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const int nb = cols / 32;
+  const long long r = b / nb, c0 = (b % nb) * 32;
+  const uint4* src = reinterpret_cast<const uint4*>(in + r * cols + c0);
+  uint32_t p[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    p[4 * i] = u.x;
+    p[4 * i + 1] = u.y;
+    p[4 * i + 2] = u.z;
+    p[4 * i + 3] = u.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(p[i] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(p[i] & 0xffff0000u)));
+  }
+  uint32_t code8 = 0, out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // floor(log2 amax) = ex - 1, exactly
+    const int shared = min(max(ex - 1 - 8, -127), 127);
+    code8 = (uint32_t)(shared + 127);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t bits = (i & 1) ? (p[i / 2] & 0xffff0000u) : (p[i / 2] << 16);
+      out[i / 4] |= e4m3_encode(ldexpf(__uint_as_float(bits), -shared)) << (8 * (i % 4));
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + r * cols + c0);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  e8[b] = (uint8_t)code8;
+}
+
+// MXFP8 codes back to fp32 values: e4m3(code) * 2^(e8 - 127), exact (the
+// product of an E4M3 value and a power of two down to 2^-136 is an fp32
+// number).  One thread per 32-value block.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
+  float v = ex == 0 ? (float)m * 0.001953125f  // m / 8 * 2^-6
+                    : __uint_as_float(((ex + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void mx8_dequantize_kernel(long long nblocks, int cols,
+                                                             const uint8_t* __restrict__ q,
+                                                             const uint8_t* __restrict__ e8,
+                                                             float* __restrict__ out) {
+  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const int nb = cols / 32;
+  const long long r = b / nb, c0 = (b % nb) * 32;
+  const float sc = e8m0_to_f32(e8[b]);
+  const uint8_t* src = q + r * cols + c0;
+  float* dst = out + r * cols + c0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dst[i] = e4m3_value(src[i]) * sc;
+}
+
+// One lane's operand of a 128-k block.  o0 / o1: byte offsets (within the
+// row) of its two 16-byte halves (8-bit formats) or of its one half (4-bit),
+// already clamped into the row; v0 / v1: whether each half lies inside the
+// contraction (else it contributes zero codes).
+template <int OP>
+__device__ __forceinline__ i32x8 ld_op(const uint8_t* row, int o0, int o1, bool v0, bool v1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(row + o0);
+  uint4 b = make_uint4(0, 0, 0, 0);
+  if constexpr (OP == kOpFp8) b = *reinterpret_cast<const uint4*>(row + o1);
+  const uint4 za = keep4(a, v0), zb = keep4(b, v1);
+  return i32x8{(int)za.x, (int)za.y, (int)za.z, (int)za.w,
+               (int)zb.x, (int)zb.y, (int)zb.z, (int)zb.w};
+}
+
+// Byte offsets and validity of lane group g's share of 128-k block kb of a
+// row of Kd values (8-bit operands: two 16-byte halves; 4-bit: one).
+template <int OP>
+__device__ __forceinline__ void op_span(int kb, int g, int Kd, int& o0, int& o1, bool& v0,
+                                        bool& v1) {
+  const int k0 = kb * 128;
+  if constexpr (OP == kOpFp8) {
+    const int a = k0 + 16 * g, b = k0 + 64 + 16 * g;
+    v0 = a + 16 <= Kd;
+    v1 = b + 16 <= Kd;
+    o0 = v0 ? a : 0;
+    o1 = v1 ? b : 0;
+  } else {
+    const int a = k0 + 32 * g;  // values
+    v0 = a + 32 <= Kd;
+    v1 = false;
+    o0 = v0 ? a / 2 : 0;
+    o1 = 0;
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, uint32_t sa, i32x8 b, uint32_t sb, f32x4 c,
+                                         std::integral_constant<int, kOpFp8>) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kOpFp8, kOpFp8, 0, (int)sa, 0,
+                                                          (int)sb);
+}
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, uint32_t sa, i32x8 b, uint32_t sb, f32x4 c,
+                                         std::integral_constant<int, kOpFp4>) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kOpFp8, kOpFp4, 0, (int)sa, 0,
+                                                          (int)sb);
+}
+
+// Weight formats of this path: E4M3 codes with an fp32 scale per output row
+// (the scaled instruction gets a unit scale, the row scale multiplies the
+// k-sum), or MXFP4 codes with their E8M0 block scales.
+template <int OP> struct MxWeights {
+  static constexpr int kPerByte = OP == kOpFp4 ? 2 : 1;
+  static constexpr bool kChannelScale = OP == kOpFp8;
+};
+
+// ---------------------------------------------------------------------------
+// Decode sizes: the weights streamed once per 16 * MB-row tile of an expert.
+// gate_up: one block = one row tile x NC groups of 16 gate + 16 up columns;
+// WK waves split the contraction H in 128-k blocks.  Each lane loads its
+// weight spans straight into registers, NS - 1 k-blocks ahead of the
+// matrix instructions; loads are unconditional (addresses clamped into
+// their rows, out-of-range spans zeroed at load), so the waits count only
+// what a step needs.
+// ---------------------------------------------------------------------------
+template <int OP, int WK, int MB, int NS, int NC>
+__global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
+    int H, int N, int E, int K, int rows, const uint8_t* __restrict__ xq,
+    const uint8_t* __restrict__ xs, const uint8_t* __restrict__ wg,
+    const uint8_t* __restrict__ wu, long long w_stride, const void* __restrict__ sg,
+    const void* __restrict__ su, long long s_stride, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slots, uint8_t* __restrict__ hq,
+    uint8_t* __restrict__ hs) {
+  typedef MxWeights<OP> W;
+  static_assert(NS >= 2, "the load ring needs two slots or more");
+  static_assert(NC % 2 == 0, "a 32-column MXFP8 block of h spans two column groups");
+  __shared__ f32x4 red[WK][MB][NC][2][kWave];
+  int e, row0, row1, cg;
+  const int CG = (N + 16 * NC - 1) / (16 * NC);
+  if (!stream_item(false, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int fr = lane % 16, g = lane / 16;
+  const int n0 = cg * 16 * NC + fr;  // column of group c: n0 + 16 c
+  const int rowb = H / W::kPerByte, nsb = H / 32;  // bytes and scale bytes per weight row
+  const uint8_t* grow[NC];
+  const uint8_t* urow[NC];
+  const uint8_t* gsc[NC];
+  const uint8_t* usc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const long long n = min(n0 + 16 * c, N - 1);
+    grow[c] = wg + (e * w_stride + n * H) / W::kPerByte;
+    urow[c] = wu + (e * w_stride + n * H) / W::kPerByte;
+    gsc[c] = usc[c] = nullptr;
+    if constexpr (!W::kChannelScale) {
+      gsc[c] = static_cast<const uint8_t*>(sg) + e * s_stride + n * nsb;
+      usc[c] = static_cast<const uint8_t*>(su) + e * s_stride + n * nsb;
+    }
+  }
+  const int nmb = (row1 - row0 + 15) / 16;
+  const uint8_t* arow[MB];
+  const uint8_t* asc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = row0 + 16 * mb + fr, rr = r < row1 ? r : row0;
+    const long long tok = sorted_slots[rr] / K;
+    arow[mb] = xq + tok * H;
+    asc[mb] = xs + tok * nsb;
+  }
+  (void)rowb;
+  const int KB = (H + 127) / 128;
+  const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
+
+  f32x4 accg[MB][NC], accu[MB][NC];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) accg[mb][c] = accu[mb][c] = f32x4{0, 0, 0, 0};
+  i32x8 ra[NS][MB], rg[NS][NC], ru[NS][NC];
+  uint32_t sa[NS][MB], sgw[NS][NC], suw[NS][NC];
+  auto load = [&](int kb, int slot) {
+    int o0, o1;
+    bool v0, v1;
+    op_span<kOpFp8>(kb, g, H, o0, o1, v0, v1);
+    const int sb = min(kb * 4 + g, nsb - 1);  // natural 32-block of this lane
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1, v0, v1);
+      sa[slot][mb] = asc[mb][sb];
+    }
+    op_span<OP>(kb, g, H, o0, o1, v0, v1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      rg[slot][c] = ld_op<OP>(grow[c], o0, o1, v0, v1);
+      ru[slot][c] = ld_op<OP>(urow[c], o0, o1, v0, v1);
+      if constexpr (W::kChannelScale) {
+        sgw[slot][c] = suw[slot][c] = kUnitScale;
+      } else {
+        sgw[slot][c] = gsc[c][sb];
+        suw[slot][c] = usc[c][sb];
+      }
+    }
+  };
+  auto step = [&](int slot) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb == 0 || mb < nmb) {
+          accg[mb][c] = mfma_mx(ra[slot][mb], sa[slot][mb], rg[slot][c], sgw[slot][c],
+                                accg[mb][c], std::integral_constant<int, OP>{});
+          accu[mb][c] = mfma_mx(ra[slot][mb], sa[slot][mb], ru[slot][c], suw[slot][c],
+                                accu[mb][c], std::integral_constant<int, OP>{});
+        }
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (kb0 + s < kb1) load(kb0 + s, s);
+  int kb = kb0;
+  // steady state: every load of the unrolled NS steps lies inside the range
+  for (; kb + 2 * NS - 2 < kb1; kb += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      load(kb + s + NS - 1, (s + NS - 1) % NS);
+      step(s);
+    }
+  }
+  for (; kb < kb1; kb += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (kb + s >= kb1) break;
+      if (kb + s + NS - 1 < kb1) load(kb + s + NS - 1, (s + NS - 1) % NS);
+      step(s);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      red[wave][mb][c][0][lane] = accg[mb][c];
+      red[wave][mb][c][1][lane] = accu[mb][c];
+    }
+  __syncthreads();
+  if (wave != 0) return;
+  // h = GELU(gate) * up in fp32, then MXFP8 per 32 columns straight from
+  // fp32: column groups 2j and 2j + 1 form one 32-column block; its maximum
+  // over the 16 lanes of a lane group (one row each) comes from xor shuffles.
+  const int nsh = N / 32;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nmb) break;
+#pragma unroll
+    for (int c2 = 0; c2 < NC; c2 += 2) {
+      f32x4 hv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = c2 + j, n = n0 + 16 * c;
+        f32x4 gv = red[0][mb][c][0][lane], uv = red[0][mb][c][1][lane];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) {
+          gv += red[w][mb][c][0][lane];
+          uv += red[w][mb][c][1][lane];
+        }
+        if constexpr (W::kChannelScale) {
+          const int nn = min(n, N - 1);
+          gv *= static_cast<const float*>(sg)[(size_t)e * s_stride + nn];
+          uv *= static_cast<const float*>(su)[(size_t)e * s_stride + nn];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[j][r] = gelu_tanh(gv[r]) * uv[r];
+      }
+      const int blk0 = n0 - fr + 16 * c2;  // first column of the 32-column block
+      if (blk0 >= N) break;                // uniform: the block lies past the last column
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = fmaxf(fabsf(hv[0][r]), fabsf(hv[1][r]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        uint32_t code8 = 0, q0 = 0, q1 = 0;
+        if (m > 0.0f) {
+          int ex;
+          (void)frexpf(m, &ex);
+          const int shared = min(max(ex - 1 - 8, -127), 127);
+          code8 = (uint32_t)(shared + 127);
+          q0 = e4m3_encode(ldexpf(hv[0][r], -shared));
+          q1 = e4m3_encode(ldexpf(hv[1][r], -shared));
+        }
+        const int row = row0 + 16 * mb + 4 * g + r;
+        if (row < row1) {
+          uint8_t* dst = hq + (size_t)row * N + blk0 + fr;
+          dst[0] = (uint8_t)q0;
+          dst[16] = (uint8_t)q1;
+          if (fr == 0) hs[(size_t)row * nsh + blk0 / 32] = (uint8_t)code8;
+        }
+      }
+    }
+  }
+}
+
+// down: one block = one row tile x WN waves of NC groups of 16 output
+// columns (the contraction, the expert width, is short and is not split).
+// A = the tile's rows of h in MXFP8 (expert-sorted order).
+template <int OP, int WN, int MB, int NS, int NC, typename YT>
+__global__ __launch_bounds__(64 * WN) void down_mx_kernel(
+    int H, int N, int E, int rows, const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+    const uint8_t* __restrict__ wd, long long w_stride, const void* __restrict__ sd,
+    long long s_stride, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
+    YT* __restrict__ y) {
+  typedef MxWeights<OP> W;
+  static_assert(NS >= 2, "the load ring needs two slots or more");
+  int e, row0, row1, cg;
+  const int CG = (H + 16 * WN * NC - 1) / (16 * WN * NC);
+  if (!stream_item(false, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int fr = lane % 16, g = lane / 16;
+  const int n0 = (cg * WN + wave) * 16 * NC + fr;  // output column of group c: n0 + 16 c
+  const int nsb = N / 32;
+  const uint8_t* brow[NC];
+  const uint8_t* bsc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const long long n = min(n0 + 16 * c, H - 1);
+    brow[c] = wd + (e * w_stride + n * N) / W::kPerByte;
+    bsc[c] = nullptr;
+    if constexpr (!W::kChannelScale)
+      bsc[c] = static_cast<const uint8_t*>(sd) + e * s_stride + n * nsb;
+  }
+  const int nmb = (row1 - row0 + 15) / 16;
+  const uint8_t* arow[MB];
+  const uint8_t* asc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = row0 + 16 * mb + fr, rr = r < row1 ? r : row0;
+    arow[mb] = hq + (long long)rr * N;
+    asc[mb] = hs + (long long)rr * nsb;
+  }
+  const int KB = (N + 127) / 128;
+  f32x4 acc[MB][NC];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[mb][c] = f32x4{0, 0, 0, 0};
+  i32x8 ra[NS][MB], rb[NS][NC];
+  uint32_t sa[NS][MB], sb[NS][NC];
+  auto load = [&](int kb, int slot) {
+    int o0, o1;
+    bool v0, v1;
+    op_span<kOpFp8>(kb, g, N, o0, o1, v0, v1);
+    const int s8 = min(kb * 4 + g, nsb - 1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1, v0, v1);
+      sa[slot][mb] = asc[mb][s8];
+    }
+    op_span<OP>(kb, g, N, o0, o1, v0, v1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      rb[slot][c] = ld_op<OP>(brow[c], o0, o1, v0, v1);
+      sb[slot][c] = W::kChannelScale ? kUnitScale : (uint32_t)bsc[c][s8];
+    }
+  };
+  auto step = [&](int slot) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb == 0 || mb < nmb)
+          acc[mb][c] = mfma_mx(ra[slot][mb], sa[slot][mb], rb[slot][c], sb[slot][c], acc[mb][c],
+                               std::integral_constant<int, OP>{});
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KB) load(s, s);
+  int kb = 0;
+  for (; kb + 2 * NS - 2 < KB; kb += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      load(kb + s + NS - 1, (s + NS - 1) % NS);
+      step(s);
+    }
+  }
+  for (; kb < KB; kb += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (kb + s >= KB) break;
+      if (kb + s + NS - 1 < KB) load(kb + s + NS - 1, (s + NS - 1) % NS);
+      step(s);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int n = n0 + 16 * c;
+    const bool nvalid = n < H;
+    float chs = 1.0f;
+    if constexpr (W::kChannelScale)
+      if (nvalid) chs = static_cast<const float*>(sd)[(size_t)e * s_stride + n];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= nmb) break;
+      const f32x4 v = acc[mb][c] * chs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * mb + 4 * g + r;
+        if (row >= row1 || !nvalid) continue;
+        const int slot = sorted_slots[row];
+        y[(size_t)slot * H + n] = from_f32<YT>(topk_w[slot] * v[r]);
+      }
+    }
+  }
+}
+
+template <int OP, int WK, int MB, int NS, int NC>
+void launch_gu_mx(const MxArgs& a, hipStream_t s) {
+  const long long cgs = (a.I + 16 * NC - 1) / (16 * NC);
+  dim3 grid((unsigned)(tile_count_bound(false, a.rows, a.T, a.E, 16 * MB) * cgs));
+  const long long I = a.I, H = a.H;
+  const uint8_t* gq = static_cast<const uint8_t*>(a.gate_up_q);
+  const int pb = MxWeights<OP>::kPerByte;
+  const uint8_t* uq = gq + I * H / pb;
+  const void* gs = a.gate_up_s;
+  const void* us;
+  long long ss;
+  if constexpr (OP == kOpFp8) {
+    us = static_cast<const float*>(gs) + I;
+    ss = 2 * I;
+  } else {
+    us = static_cast<const uint8_t*>(gs) + I * (H / 32);
+    ss = 2 * I * (H / 32);
+  }
+  hipLaunchKernelGGL((gate_up_mx_kernel<OP, WK, MB, NS, NC>), grid, dim3(64 * WK), 0, s, a.H,
+                     a.I, a.E, a.K, a.rows, a.xq, a.xs, gq, uq, 2 * I * H, gs, us, ss, a.offsets,
+                     a.sorted_slots, a.hq, a.hs);
+}
+
+template <int OP, int WN, int MB, int NS, int NC, typename YT>
+void launch_dn_mx(const MxArgs& a, hipStream_t s) {
+  const long long cgs = (a.H + 16 * WN * NC - 1) / (16 * WN * NC);
+  dim3 grid((unsigned)(tile_count_bound(false, a.rows, a.T, a.E, 16 * MB) * cgs));
+  const long long I = a.I, H = a.H;
+  const long long ss = OP == kOpFp8 ? H : H * (I / 32);
+  hipLaunchKernelGGL((down_mx_kernel<OP, WN, MB, NS, NC, YT>), grid, dim3(64 * WN), 0, s, a.H,
+                     a.I, a.E, a.rows, a.hq, a.hs, static_cast<const uint8_t*>(a.down_q), H * I,
+                     a.down_s, ss, a.offsets, a.sorted_slots, a.topk_w, static_cast<YT*>(a.y));
+}
+
+template <int OP>
+void launch_mx_stream(const MxArgs& a, hipStream_t s) {
+  constexpr int NCG = OP == kOpFp4 ? 4 : 2;
+  if (a.T <= 128) launch_gu_mx<OP, 2, 1, 3, NCG>(a, s);
+  else launch_gu_mx<OP, 2, 2, 3, NCG>(a, s);
+  if (a.y_bf16) launch_dn_mx<OP, 4, 1, 2, 1, bf16>(a, s);
+  else launch_dn_mx<OP, 4, 1, 2, 1, float>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_mx8_quantize(long long rows, int cols, const void* in, uint8_t* q,
+                               uint8_t* e8, hipStream_t s) {
+  const long long nb = rows * (cols / 32);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx8_quantize_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, nb,
+                     cols, static_cast<const bf16*>(in), q, e8);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx8_dequantize(long long rows, int cols, const uint8_t* q, const uint8_t* e8,
+                                 float* out, hipStream_t s) {
+  const long long nb = rows * (cols / 32);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx8_dequantize_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                     nb, cols, q, e8, out);
+  return hipGetLastError();
+}
+
+bool mx_uses_stream_kernels(int T, int rows, int E) { return T <= 256 && rows <= 16 * E; }
+
+hipError_t launch_expert_ffn_mx(const MxArgs& a, hipStream_t s) {
+  if (!mx_uses_stream_kernels(a.T, a.rows, a.E)) return hipErrorInvalidValue;
+  hipError_t e = launch_mx8_quantize(a.T, a.H, a.x, a.xq, a.xs, s);
+  if (e != hipSuccess) return e;
+  if (a.fmt == WFormat::kFP8) launch_mx_stream<kOpFp8>(a, s);
+  else launch_mx_stream<kOpFp4>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

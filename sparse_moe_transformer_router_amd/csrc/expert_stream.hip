@@ -71,41 +71,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The block's work item: row tile (of at most bm rows of one expert, or of
-// the tokens when ident) and column group cg of CG, from the XCD-aware
-// mapping of common.h over the real number of items, so that the column
-// groups of a row tile (which read the same activation rows) share one XCD's
-// L2.  1-D grid of at least (row tile bound) * CG blocks.
-__device__ __forceinline__ bool stream_item(bool ident, int rows, const int32_t* offsets, int E,
-                                            int bm, int CG, int& e, int& row0, int& row1,
-                                            int& cg) {
-  RowTileScan sc;
-  int R;
-  if (ident) {
-    R = (rows + bm - 1) / bm;
-  } else {
-    row_tile_scan(offsets, E, bm, sc);
-    R = sc.total;
-  }
-  const int item = xcd_item(blockIdx.x, R * CG);
-  if (item < 0) return false;
-  const int rt = item / CG;
-  cg = item % CG;
-  if (ident) {
-    e = 0;
-    row0 = rt * bm;
-    row1 = min(row0 + bm, rows);
-  } else {
-    row_tile_lookup(sc, offsets, bm, rt, e, row0, row1);
-  }
-  // the same for every lane: scalar registers, scalar branches
-  e = __builtin_amdgcn_readfirstlane(e);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  row1 = __builtin_amdgcn_readfirstlane(row1);
-  cg = __builtin_amdgcn_readfirstlane(cg);
-  return true;
-}
-
 // gate_up: one block = one row tile (<= 16 * MB rows) x NC groups of 16 gate
 // + 16 up columns; its WK waves split H.  A wave's activation fragments serve
 // all NC groups, so narrow weight formats stream more bytes per wave.

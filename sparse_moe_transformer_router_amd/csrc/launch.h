@@ -54,7 +54,7 @@ hipError_t launch_dense_mask(int T, int E, int K, const int32_t* topk_idx, const
 
 // Storage format of the expert weights (decode sizes only below bf16): see
 // wformat.h.  The values equal the moe_wformat codes of include/moe.h.
-enum class WFormat : int { kBF16 = 0, kInt8 = 1, kFP8 = 2, kMXFP4 = 3 };
+enum class WFormat : int { kBF16 = 0, kInt8 = 1, kFP8 = 2, kMXFP4 = 3, kMXFP8 = 4 };
 
 // Grouped gated-MLP over row groups.  Group e owns rows [offsets[e],
 // offsets[e+1]) of the sorted order; row r reads input row
@@ -138,6 +138,36 @@ hipError_t launch_quantize_mxfp4(long long rows, int cols, const void* w, uint8_
 // Codes back to fp32 values (times their scales), with the experts' widening.
 hipError_t launch_dequantize(WFormat f, long long rows, int cols, const void* q,
                              const void* scale, float* out, hipStream_t s);
+
+// Experts on the 8-bit / 4-bit matrix cores (expert_mx.hip): MXFP8
+// activations times E4M3 (fp32 scale per output row) or MXFP4 weights.
+struct MxArgs {
+  int T, H, I, E, K;
+  int rows;                    // T * K
+  WFormat fmt;                 // kFP8 or kMXFP4
+  bool y_bf16;
+  const void* x;               // [T,H] bf16 expert input
+  uint8_t* xq;                 // [T,H] MXFP8 codes of x (workspace)
+  uint8_t* xs;                 // [T,H/32] their E8M0 scales (workspace)
+  uint8_t* hq;                 // [rows,I] MXFP8 codes of the gated product h, sorted
+                               // order (workspace)
+  uint8_t* hs;                 // [rows,I/32] (workspace)
+  const void* gate_up_q;       // [E,2I,H] codes (MXFP4: two per byte)
+  const void* gate_up_s;       // fp32 [E,2I] (E4M3) or E8M0 [E,2I,H/32] (MXFP4)
+  const void* down_q;          // [E,H,I]
+  const void* down_s;          // fp32 [E,H] or E8M0 [E,H,I/32]
+  const int32_t* offsets;
+  const int32_t* sorted_slots;
+  const float* topk_w;
+  void* y;                     // [T*K,H] slot dtype
+};
+hipError_t launch_expert_ffn_mx(const MxArgs& a, hipStream_t s);
+bool mx_uses_stream_kernels(int T, int rows, int E);
+// MXFP8 codes and E8M0 block scales of rows x cols bf16 (cols % 32 == 0).
+hipError_t launch_mx8_quantize(long long rows, int cols, const void* in, uint8_t* q,
+                               uint8_t* e8, hipStream_t s);
+hipError_t launch_mx8_dequantize(long long rows, int cols, const uint8_t* q, const uint8_t* e8,
+                                 float* out, hipStream_t s);
 
 struct CombineArgs {
   int T, H, K;

@@ -92,6 +92,7 @@ struct Layout {
   size_t h;                         // expert gate_up output
   size_t idx, w, counts, offsets, sorted, y;  // experts-only path / layer
   size_t xd, xm, hd, dn;            // layer only
+  size_t xq, xs, hq, hs;            // MXFP8 activations of the 8-bit / 4-bit experts
   size_t wt;                        // router weights transposed
   size_t counter;                   // small-batch top-K completion counter
   size_t total;
@@ -124,6 +125,10 @@ Layout layout(const moe_dims* d, long long T) {
   L.xm = take(act * T * d->hidden);
   L.hd = take(act * T * d->dense_inter);
   L.dn = take(slot * T * d->hidden);
+  L.xq = take((size_t)T * d->hidden);
+  L.xs = take((size_t)T * (d->hidden / 32));
+  L.hq = take((size_t)S * d->expert_inter);
+  L.hs = take((size_t)S * (d->expert_inter / 32));
   L.wt = take(4 * (size_t)d->num_experts * d->hidden);
   L.counter = take(4);
   L.total = o;
@@ -337,6 +342,7 @@ int wformat_of(int32_t fmt, moe::WFormat& f) {
     case MOE_W_INT8: f = moe::WFormat::kInt8; return 0;
     case MOE_W_FP8: f = moe::WFormat::kFP8; return 0;
     case MOE_W_MXFP4: f = moe::WFormat::kMXFP4; return 0;
+    case MOE_W_MXFP8: f = moe::WFormat::kMXFP8; return 0;
     default: return fail(MOE_ERR_ARG, "weight format %d unknown", fmt);
   }
 }
@@ -545,7 +551,7 @@ int moe_quantize(int32_t fmt, int64_t rows, int32_t cols, const void* w, void* q
   moe::WFormat f;
   if (wformat_of(fmt, f)) return MOE_ERR_ARG;
   if (rows < 0 || rows > (int64_t)1 << 36) return fail(MOE_ERR_ARG, "rows out of range");
-  const int align = f == moe::WFormat::kMXFP4 ? 32 : 8;
+  const int align = f == moe::WFormat::kMXFP4 || f == moe::WFormat::kMXFP8 ? 32 : 8;
   if (cols <= 0 || cols % align != 0)
     return fail(MOE_ERR_ARG, "cols must be a positive multiple of %d", align);
   if (rows == 0) return MOE_OK;
@@ -553,6 +559,10 @@ int moe_quantize(int32_t fmt, int64_t rows, int32_t cols, const void* w, void* q
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (f) {
+    case moe::WFormat::kMXFP8:
+      e = moe::launch_mx8_quantize(rows, cols, w, static_cast<uint8_t*>(q),
+                                   static_cast<uint8_t*>(scale), s);
+      break;
     case moe::WFormat::kInt8:
       e = moe::launch_quantize_rows(rows, cols, w, static_cast<int8_t*>(q),
                                     static_cast<float*>(scale), s);
@@ -575,13 +585,18 @@ int moe_dequantize(int32_t fmt, int64_t rows, int32_t cols, const void* q, const
   moe::WFormat f;
   if (wformat_of(fmt, f)) return MOE_ERR_ARG;
   if (rows < 0 || rows > (int64_t)1 << 36) return fail(MOE_ERR_ARG, "rows out of range");
-  const int align = f == moe::WFormat::kMXFP4 ? 32 : 16;
+  const int align = f == moe::WFormat::kMXFP4 || f == moe::WFormat::kMXFP8 ? 32 : 16;
   if (cols <= 0 || cols % align != 0)
     return fail(MOE_ERR_ARG, "cols must be a positive multiple of %d", align);
   if (rows == 0) return MOE_OK;
   REQUIRE_PTR(q); REQUIRE_PTR(scale); REQUIRE_PTR(out);
-  hipError_t e = moe::launch_dequantize(f, rows, cols, q, scale, out,
-                                        static_cast<hipStream_t>(stream));
+  hipError_t e =
+      f == moe::WFormat::kMXFP8
+          ? moe::launch_mx8_dequantize(rows, cols, static_cast<const uint8_t*>(q),
+                                       static_cast<const uint8_t*>(scale), out,
+                                       static_cast<hipStream_t>(stream))
+          : moe::launch_dequantize(f, rows, cols, q, scale, out,
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dequantize");
 }
 
@@ -595,6 +610,8 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
   g_err.clear();
   moe::WFormat f;
   if (wformat_of(fmt, f)) return MOE_ERR_ARG;
+  if (f == moe::WFormat::kMXFP8)
+    return fail(MOE_ERR_ARG, "MXFP8 is an activation format, not an expert weight format here");
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "quantized experts take bf16 activations");
   if (T > kMaxQuantTokens)
@@ -607,6 +624,42 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
   return run_expert_ffn_q(dims, f, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
                           topk_w, expert_offsets, sorted_slots, y_slots, ws,
                           static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn_mx(const moe_dims* dims, int32_t fmt, int32_t T, const void* x,
+                      const void* w_gate_up_q, const void* w_gate_up_scale, const void* w_down_q,
+                      const void* w_down_scale, const float* topk_w,
+                      const int32_t* expert_offsets, const int32_t* sorted_slots, void* y_slots,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims, true)) || (rc = check_tokens(dims, T))) return rc;
+  g_err.clear();
+  moe::WFormat f;
+  if (wformat_of(fmt, f)) return MOE_ERR_ARG;
+  if (f != moe::WFormat::kFP8 && f != moe::WFormat::kMXFP4)
+    return fail(MOE_ERR_ARG, "moe_expert_ffn_mx takes E4M3 or MXFP4 expert weights");
+  if (dims->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "8-bit / 4-bit experts take bf16 activations");
+  if (!moe::mx_uses_stream_kernels(T, T * dims->top_k, dims->num_experts))
+    return fail(MOE_ERR_UNSUPPORTED, "8-bit / 4-bit experts: at most 256 tokens and 16 rows "
+                                     "per expert on average");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
+  REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots); REQUIRE_PTR(y_slots);
+  if ((rc = check_ws(dims, T, ws, ws_bytes))) return rc;
+  const Layout L = layout(dims, T);
+  moe::MxArgs a{};
+  a.T = T; a.H = dims->hidden; a.I = dims->expert_inter; a.E = dims->num_experts;
+  a.K = dims->top_k; a.rows = T * dims->top_k; a.fmt = f;
+  a.y_bf16 = dims->slot_dtype == MOE_BF16;
+  a.x = x; a.xq = at<uint8_t>(ws, L.xq); a.xs = at<uint8_t>(ws, L.xs);
+  a.hq = at<uint8_t>(ws, L.hq); a.hs = at<uint8_t>(ws, L.hs);
+  a.gate_up_q = w_gate_up_q; a.gate_up_s = w_gate_up_scale;
+  a.down_q = w_down_q; a.down_s = w_down_scale;
+  a.offsets = expert_offsets; a.sorted_slots = sorted_slots; a.topk_w = topk_w; a.y = y_slots;
+  hipError_t e = moe::launch_expert_ffn_mx(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_mx");
 }
 
 int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
@@ -792,6 +845,8 @@ int gemma4_ffn_block_q(const moe_dims* dims, int32_t T, const void* residual,
   if (!wt) return fail(MOE_ERR_ARG, "weights is NULL");
   moe::WFormat f;
   if (wformat_of(wt->fmt, f)) return MOE_ERR_ARG;
+  if (f == moe::WFormat::kMXFP8)
+    return fail(MOE_ERR_ARG, "MXFP8 is an activation format, not a weight format here");
   if (f == moe::WFormat::kMXFP4 && dims->dense_inter > kMaxMxContraction)
     return fail(MOE_ERR_UNSUPPORTED, "MXFP4 weights: dense_inter=%d exceeds %d",
                 dims->dense_inter, kMaxMxContraction);

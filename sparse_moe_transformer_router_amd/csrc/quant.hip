@@ -52,35 +52,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(long long rows, int 
 }
 
 // E4M3 per output channel (OCP 8-bit floating point, the format of
-// wformat.h): s = max |w| / 448 and code = E4M3 nearest to w / s (both
-// divisions correctly rounded fp32; half-way cases to the even mantissa;
-// magnitudes at or past 448 take 448); the sign bit is w < 0; a row of zeros
-// gets s = 0 and codes 0.  The rounding works in the value's binade: its
-// exponent E and 3 fraction bits rint((|v| / 2^E - 1) * 8) (exact scalings),
-// a carry into the next binade when that gives 8, and below 2^-6 the
-// subnormal grid rint(|v| * 2^9).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7E;
-  } else if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 is the smallest normal, code 0x08
-  } else {
-    int ex;
-    (void)frexpf(a, &ex);  // a = f * 2^ex, f in [0.5, 1)
-    int E = ex - 1;
-    uint32_t m = (uint32_t)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
-    if (m == 8) {
-      m = 0;
-      ++E;
-    }
-    code = ((uint32_t)(E + 7) << 3) | m;
-    if (code > 0x7E) code = 0x7E;
-  }
-  return code | (v < 0.0f ? 0x80u : 0u);
-}
-
+// wformat.h): s = max |w| / 448 and code = e4m3_encode(w / s) (wformat.h),
+// the division correctly rounded fp32; a row of zeros gets s = 0 and codes 0.
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(long long rows, int cols,
                                                            const bf16* __restrict__ w,
                                                            uint8_t* __restrict__ q,

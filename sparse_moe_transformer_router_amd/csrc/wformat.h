@@ -51,6 +51,34 @@ template <> struct WFmt<fp4x2> {
   static constexpr bool kChannelScale = false, kBlockScale = true;
 };
 
+// E4M3 code nearest to v (OCP 8-bit floating point: half-way cases to the
+// even mantissa; magnitudes at or past 448 take 448); the sign bit is v < 0.  The rounding works in the value's binade: its
+// exponent E and 3 fraction bits rint((|v| / 2^E - 1) * 8) (exact scalings),
+// a carry into the next binade when that gives 8, and below 2^-6 the
+// subnormal grid rint(|v| * 2^9).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7E;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 is the smallest normal, code 0x08
+  } else {
+    int ex;
+    (void)frexpf(a, &ex);  // a = f * 2^ex, f in [0.5, 1)
+    int E = ex - 1;
+    uint32_t m = (uint32_t)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
+    if (m == 8) {
+      m = 0;
+      ++E;
+    }
+    code = ((uint32_t)(E + 7) << 3) | m;
+    if (code > 0x7E) code = 0x7E;
+  }
+  return code | (v < 0.0f ? 0x80u : 0u);
+}
+
+
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 keep4(uint4 q, bool v) {

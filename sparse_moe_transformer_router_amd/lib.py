@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_W_INT8, MOE_W_FP8, MOE_W_MXFP4 = 1, 2, 3
+MOE_W_INT8, MOE_W_FP8, MOE_W_MXFP4, MOE_W_MXFP8 = 1, 2, 3, 4
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # the no-allocation entry point's device array
 
 
@@ -73,6 +73,7 @@ def _load():
     L.moe_combine.argtypes = [D, I32, P, P, P, P]
     L.moe_forward.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.moe_forward_noalloc.argtypes = [D, I32] + [P] * 10
+    L.moe_expert_ffn_mx.argtypes = [D, I32, I32] + [P] * 10 + [SZ, P]
     L.moe_quantize_int8.argtypes = [ctypes.c_int64, I32, P, P, P, P]
     L.moe_expert_ffn_int8.argtypes = [D, I32] + [P] * 10 + [SZ, P]
     L.moe_quantize.argtypes = [I32, ctypes.c_int64, I32, P, P, P, P]
@@ -86,7 +87,7 @@ def _load():
               "moe_expert_down", "moe_combine", "moe_forward", "gemma4_ffn_block",
               "moe_quantize_int8", "moe_expert_ffn_int8", "moe_dense_mask_dispatch",
               "moe_quantize", "moe_dequantize", "moe_expert_ffn_q", "moe_expert_gate_up_timed",
-              "gemma4_ffn_block_q", "moe_forward_noalloc"):
+              "gemma4_ffn_block_q", "moe_forward_noalloc", "moe_expert_ffn_mx"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -213,6 +214,17 @@ def moe_expert_ffn_q(d, fmt, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_dow
                                  _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots),
                                  _ptr(y_slots), _ptr(ws), ws.numel() if ws is not None else 0,
                                  _stream(stream)))
+
+
+def moe_expert_ffn_mx(d, fmt, T, x, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
+                      topk_w, offsets, sorted_slots, y_slots, ws, stream=None):
+    """E4M3 / MXFP4 experts on the 8-bit / 4-bit matrix instructions, MXFP8
+    activations."""
+    _check(_lib.moe_expert_ffn_mx(ctypes.byref(d), fmt, T, _ptr(x), _ptr(w_gate_up_q),
+                                  _ptr(w_gate_up_scale), _ptr(w_down_q), _ptr(w_down_scale),
+                                  _ptr(topk_w), _ptr(offsets), _ptr(sorted_slots),
+                                  _ptr(y_slots), _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream)))
 
 
 def moe_expert_gate_up(d, T, x, w_gate_up, offsets, sorted_slots, h, stream=None):

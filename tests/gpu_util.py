@@ -93,3 +93,93 @@ def bf16_path_bound(x, gate_up, down, idx, w, bf16_slots=False, out_rounded=True
     if bf16_slots:
         bound += 2.0 ** -8 * hterm * 1.001
     return bound, exact
+
+
+# Accumulation error of gfx950's scaled 8-bit / 4-bit matrix instruction,
+# relative to the sum of the magnitudes of the products it adds: an
+# in-bounds check of the instruction on random E4M3 / E2M1 operands with
+# random block scales, against an exact host evaluation, found at most
+# 1.5e-4 (median 2e-5) with an 8-bit operand; 2^-12 = 2.4e-4 covers it.
+MX_ACC_REL = 2.0 ** -12
+
+
+def _mx8_on_scale(v, shared):
+    """E4M3 value (torch float8_e4m3fn rounding, +-448 saturation) of v on
+    the grid 2^shared (shared broadcast per element), times 2^shared."""
+    s = np.clip(v / 2.0 ** shared, -448, 448)
+    r = torch.tensor(s, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return r * 2.0 ** shared
+
+
+def mx_path_bound(x, gate_up, down, idx, w, acc_rel=MX_ACC_REL):
+    """Per-element bound of the 8-bit / 4-bit expert path against the
+    oracle's expert loop with MXFP8 activations (oracle.experts_mx8), on the
+    weights' values gate_up / down.
+
+    The input's MXFP8 codes are the same on both sides (bit-exact quantizer),
+    so the path differs from the oracle only by (i) the matrix instruction's
+    accumulation, at most acc_rel of the summed product magnitudes, in the
+    gate / up sums, in the down sums and (ii) through (i), the MXFP8 codes of
+    h: an element within its error interval of an E4M3 decision point may
+    take the neighbouring code, and a block whose maximum lies within its
+    interval of a power of two may take the neighbouring scale.  Each
+    element of h may so move by d = the largest distance, over both ends of
+    its interval and the candidate scales, between its MXFP8 value and the
+    oracle's; y then moves by at most |w| (|W_d| @ d).  Plus the output's
+    bf16 rounding (2^-8 |out|) and fp32 rounding.  Returns (bound, exact)."""
+    import oracle
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    E, I2, _ = gate_up.shape
+    I = I2 // 2
+    xq = oracle.dequantize_mx8(*oracle.quantize_mx8(x))
+    idx = np.asarray(idx)
+    w = np.asarray(w, np.float64)
+    exact = np.zeros((T, H))
+    err = np.zeros((T, H))
+    c0 = np.sqrt(2.0 / np.pi)
+    for e in range(E):
+        tt, kk = np.nonzero(idx == e)
+        if len(tt) == 0:
+            continue
+        wg = gate_up[e, :I].astype(np.float64)
+        wu = gate_up[e, I:].astype(np.float64)
+        wd = down[e].astype(np.float64)
+        a = xq[tt]
+        g, u = a @ wg.T, a @ wu.T
+        gerr = acc_rel * (np.abs(a) @ np.abs(wg).T) + 2.0 ** -23 * np.abs(g)
+        uerr = acc_rel * (np.abs(a) @ np.abs(wu).T) + 2.0 ** -23 * np.abs(u)
+        th = np.tanh(c0 * (g + 0.044715 * g ** 3))
+        gel = 0.5 * g * (1.0 + th)
+        h = gel * u
+        # |gelu'| <= 1.13 everywhere; fp32 evaluation of gelu and the product
+        herr = 1.13 * gerr * (np.abs(u) + uerr) + np.abs(gel) * uerr + 1e-6 * np.abs(h)
+        hq, he8 = oracle.quantize_mx8(h)
+        q = oracle.dequantize_mx8(hq, he8)
+        shared = np.repeat(he8.astype(np.int64) - 127, 32, axis=1)
+        d = np.zeros_like(h)
+        for s_shift in (0, -1, 1):
+            if s_shift != 0:
+                # blocks whose maximum's interval reaches across a power of two
+                bmax = np.abs(h).reshape(len(tt), -1, 32)
+                berr = herr.reshape(len(tt), -1, 32)
+                lo = np.max(np.maximum(bmax - berr, 0.0), -1)
+                hi = np.max(bmax + berr, -1)
+                sh = he8.astype(np.int64) - 127 - 8
+                if s_shift > 0:
+                    cand = hi >= 2.0 ** (sh + 9)
+                else:
+                    cand = lo < 2.0 ** (sh + 8)
+                mask = np.repeat(cand & (he8 > 0), 32, axis=1)
+                if not mask.any():
+                    continue
+            else:
+                mask = np.ones_like(h, dtype=bool)
+            for v in (h - herr, h + herr):
+                qv = _mx8_on_scale(v, shared + s_shift)
+                d = np.maximum(d, np.where(mask, np.abs(qv - q), 0.0))
+        wk = w[tt, kk][:, None]
+        exact[tt] += wk * (q @ wd.T)
+        err[tt] += np.abs(wk) * (d @ np.abs(wd).T + acc_rel * (np.abs(q) @ np.abs(wd).T))
+    bound = 2.0 ** -8 * np.abs(exact) * 1.001 + err * 1.001 + 1e-6 * np.abs(exact)
+    return bound, exact
