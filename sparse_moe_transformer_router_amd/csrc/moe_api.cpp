@@ -92,9 +92,10 @@ struct Layout {
   size_t h;                         // expert gate_up output
   size_t idx, w, counts, offsets, sorted, y;  // experts-only path / layer
   size_t xd, xm, hd, dn;            // layer only
-  size_t xq, xs, hq, hs;            // MXFP8 activations of the 8-bit / 4-bit experts
   size_t wt;                        // router weights transposed
   size_t counter;                   // small-batch top-K completion counter
+  size_t base_end;                  // end of the regions above (all but the MXFP8 ones)
+  size_t xq, xs, hq, hs;            // MXFP8 activations of the 8-bit / 4-bit experts
   size_t total;
 };
 
@@ -125,12 +126,13 @@ Layout layout(const moe_dims* d, long long T) {
   L.xm = take(act * T * d->hidden);
   L.hd = take(act * T * d->dense_inter);
   L.dn = take(slot * T * d->hidden);
+  L.wt = take(4 * (size_t)d->num_experts * d->hidden);
+  L.counter = take(4);
+  L.base_end = o;
   L.xq = take((size_t)T * d->hidden);
   L.xs = take((size_t)T * (d->hidden / 32));
   L.hq = take((size_t)S * d->expert_inter);
   L.hs = take((size_t)S * (d->expert_inter / 32));
-  L.wt = take(4 * (size_t)d->num_experts * d->hidden);
-  L.counter = take(4);
   L.total = o;
   return L;
 }
@@ -756,7 +758,7 @@ int moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x, const fl
   REQUIRE_PTR(x); REQUIRE_PTR(router_w); REQUIRE_PTR(router_scale);
   REQUIRE_PTR(per_expert_scale); REQUIRE_PTR(w_gate_up); REQUIRE_PTR(w_down); REQUIRE_PTR(out);
   OPTIONAL_PTR(topk_idx); OPTIONAL_PTR(topk_w);
-  const size_t need = layout(dims, T).total;
+  const size_t need = layout(dims, T).base_end;  // moe_forward uses no MXFP8 region
   if (need > kNoAllocScratchBytes)
     return fail(MOE_ERR_WORKSPACE,
                 "moe_forward_noalloc: T=%d needs %zu bytes of scratch, the library's array "
