@@ -370,11 +370,13 @@ QUANT_FORMATS = {
 }
 
 
-def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed, native=False):
+def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed, native=False,
+                         skew=False):
     """Decode with the experts' weights quantized on the GPU (from the same
     weight copies) into one of QUANT_FORMATS: route, experts, combine.  With
     native, the experts run on the 8-bit / 4-bit matrix instructions with
-    MXFP8 activations (moe_expert_ffn_mx) instead of widening the codes."""
+    MXFP8 activations (moe_expert_ffn_mx) instead of widening the codes.
+    With skew, the inputs and router weights of the skewed prefill leg."""
     fmt, per_byte, sbytes, desc = QUANT_FORMATS[name]
     experts = lib.moe_expert_ffn_mx if native else lib.moe_expert_ffn_q
 
@@ -388,12 +390,15 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed,
         lib.moe_quantize(fmt, wt, q, sc)
         return q, sc
 
+    if skew:
+        xs, copies = skewed_inputs(torch, wl, T, seed)
+    else:
+        xs, copies = wl.batches(T, xbatches, seed), wl.copies
     qcopies = []
-    for rw, rs, pes, gu, dn in wl.copies:
+    for rw, rs, pes, gu, dn in copies:
         qcopies.append((rw, rs, pes, *quant(gu), *quant(dn)))
     torch.cuda.synchronize()
     r = Runner(wl, T)
-    xs = wl.batches(T, xbatches, seed)
     d = wl.dims
 
     def step(i, ev=None):
@@ -440,7 +445,13 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed,
     per_expert = (2 * I * H + H * I) // per_byte + 2 * I * sbytes(H) + H * sbytes(I)
     expert_bytes = U * per_expert + T * H * 2
     step_bytes = U * per_expert + ROUTER_BYTES + 2 * T * H * 2
-    return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+    flops = T * K * 6 * H * I
+    peak = 5000.0  # dense 8-bit / 4-bit-by-8-bit matrix peak (TFLOP/s)
+    extra = {}
+    if native and T > 256:
+        extra = {"experts_tflops": flops / (seg["experts"] * 1e-3) / 1e12,
+                 "experts_frac_of_fp8_mfma_peak": flops / (seg["experts"] * 1e-3) / 1e12 / peak}
+    return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), **extra,
             "distinct_experts": U, "kernel_ms": seg, "weights": desc,
             "matrix_path": ("8-bit / 4-bit scaled matrix instructions, MXFP8 activations"
                             if native else "codes widened to bf16, bf16 matrix instructions"),
@@ -1067,7 +1078,11 @@ def main():
             native[name][str(b)] = quant_decode_measure(torch, lib, wl, name, b, args.steps,
                                                         args.warmup, args.xbatches, args.seed,
                                                         native=True)
-        done(f"{name} experts on the 8/4-bit matrix instructions, decode")
+        if args.prefill > 0:
+            native[name][f"{args.prefill}_skewed"] = quant_decode_measure(
+                torch, lib, wl, name, args.prefill, max(5, args.steps // 5),
+                max(2, args.warmup // 5), 2, args.seed, native=True, skew=True)
+        done(f"{name} experts on the 8/4-bit matrix instructions")
 
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
     done("tiny fp32")

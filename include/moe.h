@@ -328,9 +328,11 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
  * weights' row scales multiply the k-sums.  So y_slots[t,k,:] = topk_w[t,k]
  * * down[e] MX(gelu_tanh(gate[e] MX(x_t)) * (up[e] MX(x_t))), MX() being the
  * MXFP8 value.  fmt: MOE_W_FP8 or MOE_W_MXFP4, weights and scales as
- * moe_quantize lays them out.  act dtype bf16; up to 256 tokens with at most
- * 16 rows per expert on average (T * top_k <= 16 * num_experts), else
- * MOE_ERR_UNSUPPORTED; the workspace as for moe_expert_ffn. */
+ * moe_quantize lays them out.  act dtype bf16.  Up to 256 tokens with at
+ * most 16 rows per expert on average (T * top_k <= 16 * num_experts) the
+ * weights are streamed per row tile; larger batches take tiled grouped GEMMs,
+ * which need hidden and expert_inter to be multiples of 64 and at most 4096
+ * (else MOE_ERR_UNSUPPORTED).  The workspace as for moe_expert_ffn. */
 int moe_expert_ffn_mx(const moe_dims* dims, int32_t fmt, int32_t T, const void* x,
                       const void* w_gate_up_q, const void* w_gate_up_scale, const void* w_down_q,
                       const void* w_down_scale, const float* topk_w,

@@ -43,6 +43,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// s_waitcnt vmcnt(N) with the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Row tiles of a grouped GEMM.  Expert e owns rows [offsets[e], offsets[e+1])
 // of the expert-sorted slot order; it is cut into ceil(count / bm) tiles of
 // bm rows.  Tiles are numbered expert by expert in ascending order.  One wave

@@ -78,14 +78,6 @@ constexpr int gemm_lds_bytes() {
 
 __device__ __forceinline__ int gswz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// s_waitcnt vmcnt(N) with the other counters unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// s_waitcnt lgkmcnt(0).
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // GU: h[row] = GELU(A[row] . W0[n]) * (A[row] . W1[n]) for the block's 128
 // columns n, A row = token of the slot (or the row itself when ident).

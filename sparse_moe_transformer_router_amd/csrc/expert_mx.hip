@@ -457,6 +457,433 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill sizes: grouped GEMM tiles of 256 rows x 256 output columns
+// (gate_up: 128 gate + the matching 128 up columns), 64-long k-tiles, on
+// v_mfma_scale_f32_32x32x64_f8f6f4.  8 waves (2 x 4), each a 128 x 64
+// sub-tile.  Every k-tile of A (MXFP8 rows: 64 bytes) and B (weight rows: 64
+// bytes in E4M3, 32 in MXFP4) goes global -> LDS directly (global_load_lds,
+// 16 bytes per lane) into a ring of NSTAGE stages; a stage is refilled as
+// soon as the barrier of the next k-tile has passed.  LDS lines are 64 bytes
+// (an MXFP4 line holds two weight rows); chunk c of line L sits at position
+// c ^ ((L >> 2) & 3).  The tile's E8M0 scales (A rows, and MXFP4 weight
+// rows) are staged in LDS past the ring once per tile.  A wave reads the
+// next k-tile's B fragments first, then, after the instructions that last use
+// each A fragment, that fragment's successor, so only B is double-buffered.
+// gate_up's epilogue stages h = GELU(gate) * up in fp32 in LDS and a thread
+// per (row, 32-column block) writes its MXFP8 codes and scale; down's stages
+// the rows and writes each slot's output times its routing weight.
+// ---------------------------------------------------------------------------
+constexpr int MXBM = 256, MXGN = 256, MXGK = 64;
+constexpr int kMxDnStageRows = 128, kMxDnStride = MXGN + 4;  // floats
+constexpr int kMxGuStride = MXGN / 2 + 4;                     // floats
+
+template <int OPB>
+struct MxTile {
+  static constexpr int RB = OPB == kOpFp4 ? 32 : 64;  // bytes of a B row per k-tile
+  static constexpr int ALINES = MXBM, BLINES = MXGN * RB / 64, LINES = ALINES + BLINES;
+  static constexpr int SB = LINES * 64;               // stage bytes
+};
+
+__device__ __forceinline__ int mswz(int line, int c) { return c ^ ((line >> 2) & 3); }
+
+template <bool GU, int OPB, int NSTAGE>
+struct MxLds {
+  typedef MxTile<OPB> T;
+  static constexpr int ring = NSTAGE * T::SB;
+  // scale bytes: A rows then (MXFP4) B rows, nsb per row; placed past the ring
+  static constexpr int scales(int nsb) { return (OPB == kOpFp4 ? 2 : 1) * 256 * nsb; }
+  static constexpr int stage_out = GU ? MXBM * kMxGuStride * 4 : kMxDnStageRows * kMxDnStride * 4;
+  static constexpr int slots(int nsb) {
+    return ring + scales(nsb) > stage_out ? ring + scales(nsb) : stage_out;
+  }
+  static constexpr int total(int nsb) { return slots(nsb) + (GU ? 0 : MXBM * 8); }
+};
+
+template <bool GU, int OPB, int NSTAGE, typename YT>
+__global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
+    int Kd, int Nout, int E, int K, int rows, int NT, const uint8_t* __restrict__ A,
+    const uint8_t* __restrict__ As, const uint8_t* __restrict__ W0,
+    const uint8_t* __restrict__ W1, long long w_stride, const void* __restrict__ S0,
+    const void* __restrict__ S1, long long s_stride, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slots, const float* __restrict__ topk_w,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, YT* __restrict__ yout) {
+  typedef MxTile<OPB> TL;
+  typedef MxLds<GU, OPB, NSTAGE> LD;
+  typedef MxWeights<OPB> W;
+  constexpr int WM = 2, WN = 4, NW = WM * WN;
+  constexpr int WR = MXBM / WM, WC = MXGN / WN, TM = WR / 32, TN = WC / 32;
+  constexpr int LPW = TL::LINES / 16 / NW;
+  static_assert(LPW * NW * 16 == TL::LINES, "copies cover a stage");
+  static_assert(!GU || TN == 2, "a gate_up wave takes one gate and one up sub-tile");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nsb = Kd / 32;
+
+  int e = 0, row0, row1, nt;
+  {
+    RowTileScan sc;
+    row_tile_scan(offsets, E, MXBM, sc);
+    const int item = xcd_item(blockIdx.x, sc.total * NT);
+    if (item < 0) return;  // uniform over the block
+    nt = item % NT;
+    row_tile_lookup(sc, offsets, MXBM, item / NT, e, row0, row1);
+  }
+  const int lane = lane_id(), wave = threadIdx.x / kWave, tid = threadIdx.x;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nbase = GU ? nt * (MXGN / 2) : nt * MXGN;
+  uint8_t* sA = smem + LD::ring;
+  uint8_t* sBs = sA + 256 * nsb;
+  int* row_slot = reinterpret_cast<int*>(smem + LD::slots(nsb));
+  float* row_w = reinterpret_cast<float*>(row_slot + MXBM);
+  // A row r of the tile (rows past the tile re-read row0: outputs dropped)
+  auto arow = [&](int r) -> long long {
+    int gr = row0 + r;
+    if (gr >= row1) gr = row0;
+    return GU ? sorted_slots[gr] / K : gr;
+  };
+  // B row n of the tile: pointer to its codes and (MXFP4) its scales
+  auto brow = [&](int n, const uint8_t*& codes, const uint8_t*& sc) {
+    const uint8_t* base = W0;
+    const void* sbase = S0;
+    int col = nbase + n;
+    if (GU && n >= MXGN / 2) {
+      base = W1;
+      sbase = S1;
+      col = nbase + n - MXGN / 2;
+    }
+    if (col >= Nout) col = 0;  // past the last column: a valid row, output dropped
+    codes = base + (e * w_stride + (long long)col * Kd) / W::kPerByte;
+    sc = nullptr;
+    if constexpr (!W::kChannelScale)
+      sc = static_cast<const uint8_t*>(sbase) + e * s_stride + (long long)col * nsb;
+  };
+
+  // the tile's scale rows into LDS (two bytes at a time; nsb is even)
+  for (int i = tid; i < 256 * nsb / 2; i += 512) {
+    const int r = i / (nsb / 2), c = i % (nsb / 2);
+    reinterpret_cast<uint16_t*>(sA)[i] =
+        reinterpret_cast<const uint16_t*>(As + arow(r) * nsb)[c];
+    if constexpr (!W::kChannelScale) {
+      const uint8_t* codes;
+      const uint8_t* sc;
+      brow(r, codes, sc);
+      reinterpret_cast<uint16_t*>(sBs)[i] = reinterpret_cast<const uint16_t*>(sc)[c];
+    }
+  }
+  if constexpr (!GU) {
+    if (tid < MXBM) {
+      const int row = row0 + tid;
+      int slot = 0;
+      float w = 0.0f;
+      if (row < row1) {
+        slot = sorted_slots[row];
+        w = topk_w[slot];
+      }
+      row_slot[tid] = slot;
+      row_w[tid] = w;
+    }
+  }
+
+  // copy j of this lane: LDS line 16 q + lane / 4 of a stage, position lane % 4
+  // Copy j of wave w fills lines 16 q .. 16 q + 15 with q = j * NW + w, so
+  // that copy j is of A lines for every wave or of B lines for every wave
+  // (the A lines are a multiple of 16 * NW).
+  static_assert(TL::ALINES % (16 * NW) == 0, "copy j is of one kind in every wave");
+  constexpr int JA = TL::ALINES / (16 * NW);  // copies j < JA are of A lines
+  const uint8_t* src[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int q = j * NW + wave;
+    const int line = 16 * q + lane / 4;
+    const int lc = mswz(line, lane % 4);  // logical chunk this lane fetches
+    if (j < JA) {
+      src[j] = A + arow(line) * Kd + lc * 16;
+    } else {
+      const int bl = line - TL::ALINES;
+      const uint8_t* codes;
+      const uint8_t* sc;
+      if constexpr (OPB == kOpFp4) {
+        brow(2 * bl + (lc >> 1), codes, sc);
+        src[j] = codes + (lc & 1) * 16;
+      } else {
+        brow(bl, codes, sc);
+        src[j] = codes + lc * 16;
+      }
+    }
+  }
+  const int nk = Kd / MXGK;
+  auto copy = [&](int kt, int j) {
+    const int ktc = kt < nk ? kt : nk - 1;  // past the end: the last tile again
+    const int q = j * NW + wave;
+    const int kstep = j < JA || OPB != kOpFp4 ? MXGK : MXGK / 2;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src[j] + (long long)ktc * kstep,
+                                     (void*)(smem + (kt % NSTAGE) * TL::SB + q * 1024), 16, 0,
+                                     0);
+#endif
+  };
+
+  // fragment addresses within a stage
+  const int fr = lane % 32, g = lane / 32;
+  // An 8-bit operand's two chunks g and 2 + g sit 32 bytes apart after the
+  // swizzle (the swizzle flips only the low two chunk bits): offset ^ 32.
+  // Rows of the wave's sub-tiles: A (wm * WR + 32 i + fr), B as below; the
+  // swizzle term (r >> 2) & 3 is the same for rows 32 apart.
+  const int ar0 = wm * WR + fr;
+  const int aoff = ar0 * 64 + mswz(ar0, g) * 16;  // + i * 32 * 64 for sub-tile i
+  int boff[TN], browl[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int n;
+    if (GU) n = (j == 0 ? 0 : MXGN / 2) + wn * (WC / 2) + fr;
+    else n = wn * WC + j * 32 + fr;
+    browl[j] = n;
+    if constexpr (OPB == kOpFp4) {
+      const int line = TL::ALINES + n / 2;
+      boff[j] = line * 64 + mswz(line, (n % 2) * 2 + g) * 16;
+    } else {
+      const int line = TL::ALINES + n;
+      boff[j] = line * 64 + mswz(line, g) * 16;
+    }
+  }
+  int nv;  // 32-row sub-tiles of this wave holding rows of the tile (uniform)
+  {
+    const int left = row1 - row0 - wm * WR;
+    nv = left <= 0 ? 0 : min(TM, (left + 31) / 32);
+    nv = __builtin_amdgcn_readfirstlane(nv);
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  i32x8 fa[TM], fb[2][TN];
+  uint32_t sa[TM], sb[2][TN];
+  auto ld16 = [&](const unsigned char* st, int off) {
+    return *reinterpret_cast<const uint4*>(st + off);
+  };
+  auto rd_a = [&](const unsigned char* st, int kt, int i) {
+    const int o = aoff + i * 32 * 64;
+    const uint4 x = ld16(st, o), y = ld16(st, o ^ 32);
+    fa[i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    sa[i] = sA[(ar0 + 32 * i) * nsb + 2 * kt + g];
+  };
+  auto rd_b = [&](const unsigned char* st, int kt, int j, int buf) {
+    const uint4 x = ld16(st, boff[j]);
+    uint4 y = make_uint4(0, 0, 0, 0);
+    if constexpr (OPB == kOpFp8) y = ld16(st, boff[j] ^ 32);
+    fb[buf][j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                       (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    sb[buf][j] = W::kChannelScale ? kUnitScale : (uint32_t)sBs[browl[j] * nsb + 2 * kt + g];
+  };
+  auto mma = [&](int i, int j, int buf) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        fa[i], fb[buf][j], acc[i][j], kOpFp8, OPB, 0, (int)sa[i], 0, (int)sb[buf][j]);
+  };
+
+  auto mainloop = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st)
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) copy(st, j);
+    wait_vmem<(NSTAGE - 1) * LPW>();
+    __syncthreads();  // tile 0 landed everywhere; the scale rows are in LDS
+#pragma unroll
+    for (int i = 0; i < TM; ++i) rd_a(smem, 0, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) rd_b(smem, 0, j, 0);
+    wait_lds();
+    // iteration kt: B of tile kt in buffer `cur`
+    auto iter = [&](int kt, auto cur_tag) {
+      constexpr int cur = decltype(cur_tag)::value, nxt = 1 - cur;
+      const bool more = kt + 1 < nk;
+      wait_vmem<(NSTAGE - 2) * LPW>();   // tile kt+1 landed (this wave's copies)
+      __builtin_amdgcn_s_barrier();      // ... everyone's; tile kt's slot is free
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned char* sn = smem + ((kt + 1) % NSTAGE) * TL::SB;
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) rd_b(sn, kt + 1, j, nxt);
+      }
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) copy(kt + NSTAGE, j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (FULL || i < nv) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mma(i, j, cur);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) rd_a(sn, kt + 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lds();
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      iter(kt, std::integral_constant<int, 0>{});
+      iter(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < nk) iter(kt, std::integral_constant<int, 0>{});
+    wait_vmem<0>();
+  };
+  if (nv == TM) mainloop(std::true_type{});
+  else mainloop(std::false_type{});
+
+  __syncthreads();  // every wave is done with the ring and the scale rows
+  if constexpr (GU) {
+    // h = GELU(gate * s_g) * (up * s_u) in fp32, staged row-major in LDS
+    float* stg = reinterpret_cast<float*>(smem);
+    const int n = nbase + wn * (WC / 2) + fr;
+    float cg = 1.0f, cu = 1.0f;
+    if constexpr (W::kChannelScale) {
+      const int nn = min(n, Nout - 1);
+      cg = static_cast<const float*>(S0)[e * s_stride + nn];
+      cu = static_cast<const float*>(S1)[e * s_stride + nn];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= nv) break;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = wm * WR + i * 32 + 8 * (q / 4) + 4 * g + (q % 4);
+        stg[r * kMxGuStride + wn * (WC / 2) + fr] =
+            gelu_tanh(acc[i][0][q] * cg) * (acc[i][1][q] * cu);
+      }
+    }
+    __syncthreads();
+    // one thread per (row, 32-column block): 256 rows x 4 blocks
+    const int nsh = Nout / 32;
+#pragma unroll
+    for (int it = 0; it < MXBM * 4 / 512; ++it) {
+      const int k = tid + it * 512;
+      const int r = k / 4, b = k % 4;
+      const int col = nbase + 32 * b;
+      if (row0 + r >= row1 || col >= Nout) continue;
+      const float* v = stg + r * kMxGuStride + 32 * b;
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+      uint32_t code8 = 0, out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (m > 0.0f) {
+        int ex;
+        (void)frexpf(m, &ex);
+        const int shared = min(max(ex - 1 - 8, -127), 127);
+        code8 = (uint32_t)(shared + 127);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) out[i / 4] |= e4m3_encode(ldexpf(v[i], -shared)) << (8 * (i % 4));
+      }
+      uint4* dst = reinterpret_cast<uint4*>(hq + (size_t)(row0 + r) * Nout + col);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      hs[(size_t)(row0 + r) * nsh + col / 32] = (uint8_t)code8;
+    }
+  } else {
+    float* stg = reinterpret_cast<float*>(smem);
+    constexpr int CH = MXGN / 4;  // chunks of 4 fp32 per row
+#pragma unroll
+    for (int pass = 0; pass < MXBM / kMxDnStageRows; ++pass) {
+      if (wm * WR / kMxDnStageRows == pass) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if (i >= nv) break;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm * WR - pass * kMxDnStageRows + i * 32 + 8 * (q / 4) + 4 * g + (q % 4);
+              stg[r * kMxDnStride + wn * WC + j * 32 + fr] = acc[i][j][q];
+            }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < kMxDnStageRows * CH / 512; ++it) {
+        const int k = tid + it * 512;
+        const int rl = k / CH, ch = k % CH;
+        const int r = pass * kMxDnStageRows + rl;
+        const int col = nbase + ch * 4;
+        if (row0 + r < row1 && col < Nout) {
+          float4 cs = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          if constexpr (W::kChannelScale)
+            cs = *reinterpret_cast<const float4*>(static_cast<const float*>(S0) +
+                                                  e * s_stride + col);
+          const float sc = row_w[r];
+          const float4 v = *reinterpret_cast<const float4*>(stg + rl * kMxDnStride + ch * 4);
+          YT* dst = yout + (size_t)row_slot[r] * Nout + col;
+          const float o[4] = {sc * (v.x * cs.x), sc * (v.y * cs.y), sc * (v.z * cs.z),
+                              sc * (v.w * cs.w)};
+          if constexpr (std::is_same<YT, float>::value) {
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = from_f32<YT>(o[u]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <bool GU, int OPB, int NSTAGE, typename YT>
+hipError_t launch_grouped_mx(int Kd, int Nout, const MxArgs& a, int NT, const uint8_t* A,
+                             const uint8_t* As, const uint8_t* W0, const uint8_t* W1,
+                             long long w_stride, const void* S0, const void* S1,
+                             long long s_stride, hipStream_t s) {
+  auto kf = grouped_mx_kernel<GU, OPB, NSTAGE, YT>;
+  const int lds = MxLds<GU, OPB, NSTAGE>::total(Kd / 32);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  static int attr_set = 0;  // the largest size set so far
+  if (lds > attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kf),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = lds;
+  }
+  const int RT = tile_count_bound(false, a.rows, a.T, a.E, MXBM);
+  hipLaunchKernelGGL(kf, dim3(RT * NT), dim3(512), lds, s, Kd, Nout, a.E, a.K, a.rows, NT, A, As,
+                     W0, W1, w_stride, S0, S1, s_stride, a.offsets, a.sorted_slots, a.topk_w,
+                     a.hq, a.hs, static_cast<YT*>(a.y));
+  return hipGetLastError();
+}
+
+template <int OP>
+hipError_t launch_mx_tiled(const MxArgs& a, hipStream_t s) {
+  const long long I = a.I, H = a.H;
+  const int pb = MxWeights<OP>::kPerByte;
+  const uint8_t* gq = static_cast<const uint8_t*>(a.gate_up_q);
+  const void* gs = a.gate_up_s;
+  const void* us;
+  long long gss, dss;
+  if constexpr (OP == kOpFp8) {
+    us = static_cast<const float*>(gs) + I;
+    gss = 2 * I;
+    dss = H;
+  } else {
+    us = static_cast<const uint8_t*>(gs) + I * (H / 32);
+    gss = 2 * I * (H / 32);
+    dss = H * (I / 32);
+  }
+  constexpr int NSG = OP == kOpFp4 ? 4 : 4;
+  hipError_t e = launch_grouped_mx<true, OP, NSG, float>(
+      a.H, a.I, a, (a.I + MXGN / 2 - 1) / (MXGN / 2), a.xq, a.xs, gq, gq + I * H / pb, 2 * I * H,
+      gs, us, gss, s);
+  if (e != hipSuccess) return e;
+  const uint8_t* dq = static_cast<const uint8_t*>(a.down_q);
+  const int NTd = (a.H + MXGN - 1) / MXGN;
+  if (a.y_bf16)
+    return launch_grouped_mx<false, OP, 4, bf16>(a.I, a.H, a, NTd, a.hq, a.hs, dq, dq, H * I,
+                                                 a.down_s, a.down_s, dss, s);
+  return launch_grouped_mx<false, OP, 4, float>(a.I, a.H, a, NTd, a.hq, a.hs, dq, dq, H * I,
+                                                a.down_s, a.down_s, dss, s);
+}
+
 template <int OP, int WK, int MB, int NS, int NC>
 void launch_gu_mx(const MxArgs& a, hipStream_t s) {
   const long long cgs = (a.I + 16 * NC - 1) / (16 * NC);
@@ -523,12 +950,22 @@ hipError_t launch_mx8_dequantize(long long rows, int cols, const uint8_t* q, con
 bool mx_uses_stream_kernels(int T, int rows, int E) { return T <= 256 && rows <= 16 * E; }
 
 hipError_t launch_expert_ffn_mx(const MxArgs& a, hipStream_t s) {
-  if (!mx_uses_stream_kernels(a.T, a.rows, a.E)) return hipErrorInvalidValue;
   hipError_t e = launch_mx8_quantize(a.T, a.H, a.x, a.xq, a.xs, s);
   if (e != hipSuccess) return e;
-  if (a.fmt == WFormat::kFP8) launch_mx_stream<kOpFp8>(a, s);
-  else launch_mx_stream<kOpFp4>(a, s);
-  return hipGetLastError();
+  if (mx_uses_stream_kernels(a.T, a.rows, a.E)) {
+    if (a.fmt == WFormat::kFP8) launch_mx_stream<kOpFp8>(a, s);
+    else launch_mx_stream<kOpFp4>(a, s);
+    return hipGetLastError();
+  }
+  return a.fmt == WFormat::kFP8 ? launch_mx_tiled<kOpFp8>(a, s) : launch_mx_tiled<kOpFp4>(a, s);
+}
+
+bool mx_tiled_supported(int H, int I) {
+  return H % MXGK == 0 && I % MXGK == 0 &&
+         MxLds<true, kOpFp4, 4>::total(H / 32) <= 160 * 1024 &&
+         MxLds<true, kOpFp8, 4>::total(H / 32) <= 160 * 1024 &&
+         MxLds<false, kOpFp4, 4>::total(I / 32) <= 160 * 1024 &&
+         MxLds<false, kOpFp8, 4>::total(I / 32) <= 160 * 1024;
 }
 
 }  // namespace moe

@@ -163,6 +163,9 @@ struct MxArgs {
 };
 hipError_t launch_expert_ffn_mx(const MxArgs& a, hipStream_t s);
 bool mx_uses_stream_kernels(int T, int rows, int E);
+// The tiled (prefill) form needs H and I multiples of 64 and the tile's scale
+// rows in LDS beside the copy ring.
+bool mx_tiled_supported(int H, int I);
 // MXFP8 codes and E8M0 block scales of rows x cols bf16 (cols % 32 == 0).
 hipError_t launch_mx8_quantize(long long rows, int cols, const void* in, uint8_t* q,
                                uint8_t* e8, hipStream_t s);

@@ -642,9 +642,10 @@ int moe_expert_ffn_mx(const moe_dims* dims, int32_t fmt, int32_t T, const void* 
     return fail(MOE_ERR_ARG, "moe_expert_ffn_mx takes E4M3 or MXFP4 expert weights");
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "8-bit / 4-bit experts take bf16 activations");
-  if (!moe::mx_uses_stream_kernels(T, T * dims->top_k, dims->num_experts))
-    return fail(MOE_ERR_UNSUPPORTED, "8-bit / 4-bit experts: at most 256 tokens and 16 rows "
-                                     "per expert on average");
+  if (!moe::mx_uses_stream_kernels(T, T * dims->top_k, dims->num_experts) &&
+      !moe::mx_tiled_supported(dims->hidden, dims->expert_inter))
+    return fail(MOE_ERR_UNSUPPORTED, "8-bit / 4-bit experts past 256 tokens: hidden and "
+                                     "expert_inter must be multiples of 64, at most 4096");
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
   REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);

@@ -147,3 +147,43 @@ def test_experts_mx_small_ragged(name):
     np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
     note(f"  max err / RMS = {rel_max_err(out, ref):.4f}")
     assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) / bound))
+
+
+def _check_mx(c, name, T, x, idx, w, q, full_rms=True):
+    y, out = _mx_path(c, FMTS[name], T, x, idx, w, q)
+    ref = _oracle_mx(name, x.f32, q, idx, w)
+    deq = oracle.dequantize_fp8 if name == "fp8" else oracle.dequantize_mxfp4
+    bound, exact = mx_path_bound(x.f32, deq(q[0], q[1]), deq(q[2], q[3]), idx, w)
+    np.testing.assert_allclose(exact, ref, rtol=1e-9, atol=1e-12)
+    rms_err = float(np.sqrt(np.mean((out - ref) ** 2) / np.mean(ref ** 2)))
+    note(f"  max err / RMS = {rel_max_err(out, ref):.4f}, RMS err / RMS = {rms_err:.4f}, "
+         f"max err / bound = {float(np.max(np.abs(out - ref) / bound)):.3f}")
+    assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) / bound))
+    assert rms_err <= 5e-3
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+def test_experts_mx_tiled_small(name):
+    """The tiled (prefill) kernels on a small layer: 300 tokens at top-2 of 8
+    experts (75 rows per expert on average, ragged 256-row tiles), hidden 256,
+    expert width 192 (one full and one partial 128-column gate_up tile)."""
+    c = synth.moe_case(300, seed=21, H=256, E=8, K=2, I=192, weight_std=0.1)
+    quant = oracle.quantize_fp8 if name == "fp8" else oracle.quantize_mxfp4
+    q = (*quant(c.gate_up.f32), *quant(c.down.f32))
+    idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note(f"experts {name} on 8/4-bit matrix cores, tiled, small")
+    _check_mx(c, name, c.T, c.x, idx, w, q)
+
+
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+def test_experts_mx_26b_prefill_skewed(case26b, oracle_q, name):
+    """4096 skewed tokens (hottest expert ~3100 rows, a dozen experts empty)
+    through the tiled kernels, every row against the oracle."""
+    c = case26b
+    T = 4096
+    x = synth.moe_x(T, seed=0, skew=True)
+    rw, rs, pes = synth.moe_router_weights(0, skew=True)
+    idx, w = oracle.router(x.f32, rw, rs, pes, c.K)
+    q = oracle_q[name]
+    note(f"experts {name} on 8/4-bit matrix cores, 26B prefill {T} skewed")
+    _check_mx(c, name, T, x, idx, w, q)
