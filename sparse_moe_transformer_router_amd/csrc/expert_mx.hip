@@ -497,7 +497,9 @@ struct MxLds {
   static constexpr int slots(int nsb) {
     return ring + scales(nsb) > stage_out ? ring + scales(nsb) : stage_out;
   }
-  static constexpr int total(int nsb) { return slots(nsb) + (GU ? 0 : MXBM * 8); }
+  // the tile's A row indices (gathered token or sorted row) past everything
+  static constexpr int tok(int nsb) { return slots(nsb) + (GU ? 0 : MXBM * 8); }
+  static constexpr int total(int nsb) { return tok(nsb) + MXBM * 4; }
 };
 
 template <bool GU, int OPB, int NSTAGE, typename YT>
@@ -535,39 +537,62 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
   uint8_t* sBs = sA + 256 * nsb;
   int* row_slot = reinterpret_cast<int*>(smem + LD::slots(nsb));
   float* row_w = reinterpret_cast<float*>(row_slot + MXBM);
+  int* rtok = reinterpret_cast<int*>(smem + LD::tok(nsb));
   // A row r of the tile (rows past the tile re-read row0: outputs dropped)
-  auto arow = [&](int r) -> long long {
-    int gr = row0 + r;
+  if (tid < MXBM) {
+    int gr = row0 + tid;
     if (gr >= row1) gr = row0;
-    return GU ? sorted_slots[gr] / K : gr;
+    rtok[tid] = GU ? sorted_slots[gr] / K : gr;
+  }
+  // B row n of the tile: its column in the weight matrix (its row there), the
+  // gate or up half for gate_up; byte offsets within the expert's weights
+  const uint8_t* wbase = W0 + e * w_stride / W::kPerByte;
+  const uint8_t* sbase0 = nullptr;
+  if constexpr (!W::kChannelScale) sbase0 = static_cast<const uint8_t*>(S0) + e * s_stride;
+  const long long up_off = GU ? (long long)(W1 - W0) : 0;  // bytes from gate to up rows
+  const long long sup_off =
+      GU && !W::kChannelScale ? static_cast<const uint8_t*>(S1) - static_cast<const uint8_t*>(S0)
+                              : 0;
+  auto bcol = [&](int n, bool& up) {
+    up = GU && n >= MXGN / 2;
+    int col = nbase + n - (up ? MXGN / 2 : 0);
+    return col < Nout ? col : 0;  // past the last column: a valid row, output dropped
   };
-  // B row n of the tile: pointer to its codes and (MXFP4) its scales
-  auto brow = [&](int n, const uint8_t*& codes, const uint8_t*& sc) {
-    const uint8_t* base = W0;
-    const void* sbase = S0;
-    int col = nbase + n;
-    if (GU && n >= MXGN / 2) {
-      base = W1;
-      sbase = S1;
-      col = nbase + n - MXGN / 2;
-    }
-    if (col >= Nout) col = 0;  // past the last column: a valid row, output dropped
-    codes = base + (e * w_stride + (long long)col * Kd) / W::kPerByte;
-    sc = nullptr;
-    if constexpr (!W::kChannelScale)
-      sc = static_cast<const uint8_t*>(sbase) + e * s_stride + (long long)col * nsb;
+  auto boffs = [&](int n) -> unsigned {
+    bool up;
+    const int col = bcol(n, up);
+    return (unsigned)((up ? up_off : 0) + (long long)col * Kd / W::kPerByte);
   };
+  __syncthreads();
 
-  // the tile's scale rows into LDS (two bytes at a time; nsb is even)
-  for (int i = tid; i < 256 * nsb / 2; i += 512) {
-    const int r = i / (nsb / 2), c = i % (nsb / 2);
-    reinterpret_cast<uint16_t*>(sA)[i] =
-        reinterpret_cast<const uint16_t*>(As + arow(r) * nsb)[c];
-    if constexpr (!W::kChannelScale) {
-      const uint8_t* codes;
-      const uint8_t* sc;
-      brow(r, codes, sc);
-      reinterpret_cast<uint16_t*>(sBs)[i] = reinterpret_cast<const uint16_t*>(sc)[c];
+  // the tile's scale rows into LDS, two bytes at a time (nsb is even), in
+  // batches of 8 loads per thread
+  {
+    const int h2 = nsb / 2, tot = MXBM * h2;
+    constexpr int BT = 8;
+    for (int i0 = tid; i0 < tot; i0 += 512 * BT) {
+      uint16_t va[BT], vb[BT];
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const int i = i0 + 512 * b;
+        const int r = i < tot ? i / h2 : 0, c = i < tot ? i % h2 : 0;
+        va[b] = reinterpret_cast<const uint16_t*>(As + (long long)rtok[r] * nsb)[c];
+        vb[b] = 0;
+        if constexpr (!W::kChannelScale) {
+          bool up;
+          const int col = bcol(r, up);
+          vb[b] = reinterpret_cast<const uint16_t*>(sbase0 + (up ? sup_off : 0) +
+                                                     (long long)col * nsb)[c];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const int i = i0 + 512 * b;
+        if (i < tot) {
+          reinterpret_cast<uint16_t*>(sA)[i] = va[b];
+          if constexpr (!W::kChannelScale) reinterpret_cast<uint16_t*>(sBs)[i] = vb[b];
+        }
+      }
     }
   }
   if constexpr (!GU) {
@@ -590,25 +615,20 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
   // (the A lines are a multiple of 16 * NW).
   static_assert(TL::ALINES % (16 * NW) == 0, "copy j is of one kind in every wave");
   constexpr int JA = TL::ALINES / (16 * NW);  // copies j < JA are of A lines
-  const uint8_t* src[LPW];
+  // byte offsets of this lane's copy sources: from A (32 bits: A has at most
+  // 2^32 bytes) or from the expert's weights (wbase)
+  unsigned src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int q = j * NW + wave;
     const int line = 16 * q + lane / 4;
     const int lc = mswz(line, lane % 4);  // logical chunk this lane fetches
     if (j < JA) {
-      src[j] = A + arow(line) * Kd + lc * 16;
+      src[j] = (unsigned)rtok[line] * (unsigned)Kd + lc * 16;
     } else {
       const int bl = line - TL::ALINES;
-      const uint8_t* codes;
-      const uint8_t* sc;
-      if constexpr (OPB == kOpFp4) {
-        brow(2 * bl + (lc >> 1), codes, sc);
-        src[j] = codes + (lc & 1) * 16;
-      } else {
-        brow(bl, codes, sc);
-        src[j] = codes + lc * 16;
-      }
+      if constexpr (OPB == kOpFp4) src[j] = boffs(2 * bl + (lc >> 1)) + (lc & 1) * 16;
+      else src[j] = boffs(bl) + lc * 16;
     }
   }
   const int nk = Kd / MXGK;
@@ -616,8 +636,9 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
     const int ktc = kt < nk ? kt : nk - 1;  // past the end: the last tile again
     const int q = j * NW + wave;
     const int kstep = j < JA || OPB != kOpFp4 ? MXGK : MXGK / 2;
+    const uint8_t* base = j < JA ? A : wbase;
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src[j] + (long long)ktc * kstep,
+    __builtin_amdgcn_global_load_lds(base + src[j] + (unsigned)(ktc * kstep),
                                      (void*)(smem + (kt % NSTAGE) * TL::SB + q * 1024), 16, 0,
                                      0);
 #endif
@@ -684,8 +705,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
         fa[i], fb[buf][j], acc[i][j], kOpFp8, OPB, 0, (int)sa[i], 0, (int)sb[buf][j]);
   };
 
-  auto mainloop = [&](auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  {
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st)
 #pragma unroll
@@ -700,7 +720,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
     // iteration kt: B of tile kt in buffer `cur`
     auto iter = [&](int kt, auto cur_tag) {
       constexpr int cur = decltype(cur_tag)::value, nxt = 1 - cur;
-      const bool more = kt + 1 < nk;
+      const bool more = __builtin_amdgcn_readfirstlane(kt + 1 < nk ? 1 : 0) != 0;
       wait_vmem<(NSTAGE - 2) * LPW>();   // tile kt+1 landed (this wave's copies)
       __builtin_amdgcn_s_barrier();      // ... everyone's; tile kt's slot is free
       __builtin_amdgcn_sched_barrier(0);
@@ -714,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if (FULL || i < nv) {
+        if (i < nv) {  // uniform: sub-tiles past the group's rows skip their products
 #pragma unroll
           for (int j = 0; j < TN; ++j) mma(i, j, cur);
         }
@@ -731,9 +751,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
     }
     if (kt < nk) iter(kt, std::integral_constant<int, 0>{});
     wait_vmem<0>();
-  };
-  if (nv == TM) mainloop(std::true_type{});
-  else mainloop(std::false_type{});
+  }
 
   __syncthreads();  // every wave is done with the ring and the scale rows
   if constexpr (GU) {
