@@ -936,10 +936,13 @@ def _oracle_experts_rate(x, args, gu32, dn32, seconds):
             return n / el, n // x.shape[0], el
 
 
-def cpu_oracle_configs(torch, wl, xs, T, layer, prefill_T, seed, seconds):
+def cpu_oracle_configs(torch, wl, xs, T, layers, prefill_T, seed, seconds, stack_steps,
+                       stack_prefill):
     """Oracle rates on the other configurations (bounded samples): the decode
     batch on one thread, 64 tokens of the skewed prefill batch, the tiny fp32
-    experts-only case and the whole block on 16 tokens."""
+    experts-only case, the whole block on 16 tokens, and the 30-layer stack
+    extrapolated from layers 0, 14 and 29 timed on 16 tokens each."""
+    layer = layers[0] if layers else None
     import oracle
     from sparse_moe_transformer_router_amd import synth
 
@@ -994,6 +997,28 @@ def cpu_oracle_configs(torch, wl, xs, T, layer, prefill_T, seed, seconds):
         res["block"] = {"tokens_per_s": n / el,
                         "sample": f"whole block on 16 tokens, {n // 16} calls over {el:.1f} s"}
         del args
+    if layers is not None and len(layers) >= LAYERS:
+        # the stack: layers 0, 14 and 29 on 16 tokens each (the oracle's cost
+        # is linear in the tokens and equal for every layer of these shapes);
+        # the stack's rates are extrapolated from their mean per-token time
+        per = []
+        for li in (0, 14, LAYERS - 1):
+            ly = layers[li]
+            args = [f(t) for t in (*ly.gains, *ly.dense, ly.rw, ly.rs, ly.pes, ly.gu, ly.dn)]
+            t0 = time.perf_counter()
+            oracle.block(x, *args, 0.06, K)
+            per.append((time.perf_counter() - t0) / x.shape[0])
+            del args
+        layer_s = sum(per) / len(per)
+        res["stack_extrapolated"] = {
+            "sample": "layers 0, 14 and 29 of the stack, one call on 16 tokens each; the "
+                      f"stack's figures are extrapolated to {LAYERS} layers (labelled "
+                      "extrapolation, not measured end to end)",
+            "seconds_per_token_per_layer": per,
+            "decode_tokens_per_s": 1.0 / (LAYERS * layer_s),
+            "decode_seconds_for_the_gpu_run": stack_steps * T * LAYERS * layer_s,
+            "prefill_tokens_per_s": 1.0 / (LAYERS * layer_s),
+            "prefill_seconds_for_the_gpu_run": stack_prefill * LAYERS * layer_s}
     return res
 
 
@@ -1136,9 +1161,9 @@ def main():
         if prefill is not None:
             prefill["routing_vs_oracle"] = prefill_routing_check(torch, wl, args.prefill,
                                                                  args.seed)
-        cpu_configs = cpu_oracle_configs(torch, wl, xs, args.batch,
-                                         layers[0] if layers else None, args.prefill, args.seed,
-                                         args.cpu_seconds)
+        cpu_configs = cpu_oracle_configs(torch, wl, xs, args.batch, layers or None,
+                                         args.prefill, args.seed, args.cpu_seconds,
+                                         args.stack_steps, args.stack_prefill)
         done("cpu baselines")
 
     achieved = head["gate_up_gbs"]
