@@ -52,6 +52,29 @@ __device__ __forceinline__ void wait_vmem() {
 // s_waitcnt lgkmcnt(0).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes at gsrc land at lds + 16 l (lds is the same for every
+// lane).  Issued from inline asm, so the compiler does not see it: when it
+// tracks such copies itself it cannot tell the slots of a copy ring apart,
+// and makes LDS reads that follow a copy wait for every copy in flight,
+// which drains the ring on each k-tile.  Callers order the ring with
+// wait_vmem and a barrier.  The low 32 bits of a generic LDS address are the
+// LDS offset; M0 takes it, and one wait state separates that write from the
+// copy.
+__device__ __forceinline__ void lds_copy16(const void* gsrc, const void* lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+// s_barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Row tiles of a grouped GEMM.  Expert e owns rows [offsets[e], offsets[e+1])
 // of the expert-sorted slot order; it is cut into ceil(count / bm) tiles of
 // bm rows.  Tiles are numbered expert by expert in ascending order.  One wave

@@ -638,9 +638,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
     const int kstep = j < JA || OPB != kOpFp4 ? MXGK : MXGK / 2;
     const uint8_t* base = j < JA ? A : wbase;
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(base + src[j] + (unsigned)(ktc * kstep),
-                                     (void*)(smem + (kt % NSTAGE) * TL::SB + q * 1024), 16, 0,
-                                     0);
+    lds_copy16(base + src[j] + (unsigned)(ktc * kstep), smem + (kt % NSTAGE) * TL::SB + q * 1024);
 #endif
   };
 
@@ -722,7 +720,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
       constexpr int cur = decltype(cur_tag)::value, nxt = 1 - cur;
       const bool more = __builtin_amdgcn_readfirstlane(kt + 1 < nk ? 1 : 0) != 0;
       wait_vmem<(NSTAGE - 2) * LPW>();   // tile kt+1 landed (this wave's copies)
-      __builtin_amdgcn_s_barrier();      // ... everyone's; tile kt's slot is free
+      block_barrier();                   // ... everyone's; tile kt's slot is free
       __builtin_amdgcn_sched_barrier(0);
       const unsigned char* sn = smem + ((kt + 1) % NSTAGE) * TL::SB;
       if (more) {
