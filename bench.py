@@ -446,11 +446,15 @@ def quant_decode_measure(torch, lib, wl, name, T, steps, warmup, xbatches, seed,
     expert_bytes = U * per_expert + T * H * 2
     step_bytes = U * per_expert + ROUTER_BYTES + 2 * T * H * 2
     flops = T * K * 6 * H * I
-    peak = 5000.0  # dense 8-bit / 4-bit-by-8-bit matrix peak (TFLOP/s)
+    # dense matrix peak (TFLOP/s): 8-bit / 4-bit-by-8-bit, or bf16 for the
+    # widened codes
+    peak = 5000.0 if native else 2500.0
     extra = {}
-    if native and T > 256:
-        extra = {"experts_tflops": flops / (seg["experts"] * 1e-3) / 1e12,
-                 "experts_frac_of_fp8_mfma_peak": flops / (seg["experts"] * 1e-3) / 1e12 / peak}
+    if T > 256:
+        tf = flops / (seg["experts"] * 1e-3) / 1e12
+        extra = {"experts_tflops": tf,
+                 ("experts_frac_of_fp8_mfma_peak" if native
+                  else "experts_frac_of_bf16_mfma_peak"): tf / peak}
     return {"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), **extra,
             "distinct_experts": U, "kernel_ms": seg, "weights": desc,
             "matrix_path": ("8-bit / 4-bit scaled matrix instructions, MXFP8 activations"
@@ -1108,6 +1112,12 @@ def main():
                 torch, lib, wl, name, args.prefill, max(5, args.steps // 5),
                 max(2, args.warmup // 5), 2, args.seed, native=True, skew=True)
         done(f"{name} experts on the 8/4-bit matrix instructions")
+    quant_prefill = {}
+    for name in (QUANT_FORMATS if args.quant and args.prefill > 0 else ()):
+        quant_prefill[name] = quant_decode_measure(
+            torch, lib, wl, name, args.prefill, max(5, args.steps // 5), max(2, args.warmup // 5),
+            2, args.seed, skew=True)
+        done(f"{name} experts at {args.prefill} skewed tokens (tiled, widened codes)")
 
     tiny = tiny_measure(torch, lib, args.steps, args.warmup)
     done("tiny fp32")
@@ -1199,6 +1209,7 @@ def main():
         "dense_masked_ablation": dense_mask or None,
         "quantized_experts_decode": quant,
         "quantized_experts_native_decode": native or None,
+        "quantized_experts_prefill": quant_prefill or None,
         "tiny_f32": tiny,
         "block": block,
         "block_decode_quantized": block_q,

@@ -251,8 +251,9 @@ int moe_expert_gate_up_timed(const moe_dims* dims, int32_t T, const void* x,
  * moe_expert_ffn_int8: moe_expert_ffn with the experts' weights as int8 codes
  * and per-row scales (gate_up: codes [E,2I,H], scales [E,2I]; down: codes
  * [E,H,I], scales [E,H]).  The code rows enter bf16 MFMAs exactly and each
- * output channel is multiplied by its scale after the k-sum.  Batches of
- * T <= 256 tokens only, act dtype bf16, else MOE_ERR_UNSUPPORTED. */
+ * output channel is multiplied by its scale after the k-sum.  Act dtype bf16,
+ * else MOE_ERR_UNSUPPORTED; any T that moe_expert_ffn takes (as
+ * moe_expert_ffn_q with MOE_W_INT8). */
 int moe_quantize_int8(int64_t rows, int32_t cols, const void* w, int8_t* q, float* scale,
                       void* stream);
 int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
@@ -291,9 +292,10 @@ int moe_expert_ffn_int8(const moe_dims* dims, int32_t T, const void* x,
  * as moe_quantize lays them out).  Codes widen to bf16 exactly in registers
  * (MXFP4 with its block scale; block scales must exceed 2^-125 to stay in
  * bf16's normal range), enter bf16 MFMAs, and int8 / E4M3 output channels
- * are multiplied by their scale after the k-sum.  The weights are streamed
- * (no tiled kernels for these formats), so batches of T <= 256 tokens only,
- * act dtype bf16, else MOE_ERR_UNSUPPORTED.
+ * are multiplied by their scale after the k-sum.  Up to 256 tokens the
+ * weights are streamed from HBM (decode kernels); past that the tiled grouped
+ * GEMMs stage the codes in LDS as stored and widen them after the LDS reads.
+ * Act dtype bf16, else MOE_ERR_UNSUPPORTED; T as for moe_expert_ffn.
  *
  *   MOE_W_MXFP8  q uint8 [rows, cols], scale uint8 [rows, cols / 32]: per
  *                32-value block, shared = floor(log2 max |w|) - 8 clamped to
@@ -402,12 +404,13 @@ int gemma4_ffn_block(const moe_dims* dims, int32_t T, const void* residual,
  * [E, 2I, H] and down [E, H, I].  Norm gains, router weights and
  * layer_scalar stay fp32; activations are bf16 (act_dtype MOE_BF16).  The
  * codes widen to bf16 exactly in registers, as in moe_expert_ffn_q, so the
- * result is the bf16 layer on the dequantized weights.  All matrices go
- * through the weight-streaming kernels (there are no tiled kernels for these
- * formats): T <= 256.  Otherwise as gemma4_ffn_block, including the side
- * stream of the dense branch.  MOE_ERR_UNSUPPORTED for act_dtype MOE_F32,
- * dense_inter == 0, T > 256, or MXFP4 with dense_inter > 8192 (its kernels
- * stage the block scales of a contraction of at most 8192 weights);
+ * result is the bf16 layer on the dequantized weights.  Every matrix goes
+ * through the weight-streaming kernels up to 256 tokens and through the tiled
+ * grouped GEMMs past that, as in moe_expert_ffn_q.  Otherwise as
+ * gemma4_ffn_block, including the side stream of the dense branch.
+ * MOE_ERR_UNSUPPORTED for act_dtype MOE_F32, dense_inter == 0, or MXFP4 with
+ * dense_inter > 8192 (its kernels stage the block scales of a contraction of
+ * at most 8192 weights);
  * MOE_ERR_ARG for an unknown format or a missing pointer. */
 typedef struct gemma4_ffn_weights_q {
   int32_t fmt;                   /* moe_wformat of every quantized matrix */

@@ -52,8 +52,8 @@ hipError_t launch_dense_mask(int T, int E, int K, const int32_t* topk_idx, const
                              int32_t* offsets, int32_t* sorted_slots, float* w_dense,
                              hipStream_t s);
 
-// Storage format of the expert weights (decode sizes only below bf16): see
-// wformat.h.  The values equal the moe_wformat codes of include/moe.h.
+// Storage format of the expert weights: see wformat.h.  The values equal the
+// moe_wformat codes of include/moe.h.
 enum class WFormat : int { kBF16 = 0, kInt8 = 1, kFP8 = 2, kMXFP4 = 3, kMXFP8 = 4 };
 
 // Grouped gated-MLP over row groups.  Group e owns rows [offsets[e],
@@ -72,10 +72,10 @@ struct GateUpArgs {
   const int32_t* offsets;      // [E+1] (unused when ident)
   const int32_t* sorted_slots; // [rows] (unused when ident)
   void* h;                     // [rows, N] act dtype, sorted order
-  // Weights below bf16 (decode sizes only): w_gate / w_up hold codes; int8
-  // and E4M3 rows n of group e are scaled by the fp32 s_gate / s_up[e *
-  // s_stride + n]; MXFP4 rows carry E8M0 block scales at s_gate / s_up + e *
-  // s_stride + n * (H / 32).  w_stride counts weights (not stored units).
+  // Weights below bf16: w_gate / w_up hold codes; int8 and E4M3 rows n of
+  // group e are scaled by the fp32 s_gate / s_up[e * s_stride + n]; MXFP4
+  // rows carry E8M0 block scales at s_gate / s_up + e * s_stride + n * (H /
+  // 32).  w_stride counts weights (not stored units).
   WFormat w_fmt;
   const void* s_gate;
   const void* s_up;
@@ -121,7 +121,13 @@ struct DownArgs {
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
 // Decode-sized variants (few rows per group): weight-streaming kernels.
+// launch_gate_up / launch_down pick them for bf16 weights where
+// use_stream_kernels holds, and for weights below bf16 (which need bf16
+// activations) up to kMaxQuantStreamTokens tokens; past that, the tiled
+// kernels widen those weights after their LDS reads.
+constexpr int kMaxQuantStreamTokens = 256;
 bool use_stream_kernels(int T, int rows, int E, bool ident);
+bool quant_uses_stream_kernels(int T);
 hipError_t launch_gate_up_stream(const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down_stream(const DownArgs& a, hipStream_t s);
 

@@ -16,7 +16,6 @@ namespace {
 
 // Quantized experts run on the weight-streaming kernels only, which pay up to
 // about 16 rows per expert (256 tokens at top-8 of 128 experts).
-constexpr int kMaxQuantTokens = 256;
 
 thread_local std::string g_err;
 
@@ -296,7 +295,8 @@ int run_expert_ffn(const moe_dims* d, int32_t T, const void* x, const void* w_ga
 // Experts on weights stored below bf16 (fmt: int8, E4M3 or MXFP4).  Codes
 // of gate_up are [E, 2I, H] and of down [E, H, I] (MXFP4: two per byte);
 // scales are fp32 [E, 2I] / [E, H] (int8, E4M3) or E8M0 [E, 2I, H/32] /
-// [E, H, I/32] (MXFP4).
+// [E, H, I/32] (MXFP4).  Weight-streaming kernels up to 256 tokens, the
+// tiled grouped GEMMs past that.
 int run_expert_ffn_q(const moe_dims* d, moe::WFormat fmt, int32_t T, const void* x,
                      const void* guq, const void* gus, const void* dnq, const void* dns,
                      const float* topk_w, const int32_t* offsets, const int32_t* sorted,
@@ -321,7 +321,7 @@ int run_expert_ffn_q(const moe_dims* d, moe::WFormat fmt, int32_t T, const void*
     g.s_up = static_cast<const float*>(gus) + I;
     g.s_stride = 2 * I;
   }
-  hipError_t e = moe::launch_gate_up_stream(g, s);
+  hipError_t e = moe::launch_gate_up(g, s);
   if (e != hipSuccess) return hip_fail(e, "expert gate_up (quantized weights)");
   moe::DownArgs dn{};
   dn.T = T; dn.H = d->hidden; dn.N = d->expert_inter; dn.E = d->num_experts; dn.K = d->top_k;
@@ -330,7 +330,7 @@ int run_expert_ffn_q(const moe_dims* d, moe::WFormat fmt, int32_t T, const void*
   dn.h = h; dn.w_down = dnq; dn.w_stride = H * I;
   dn.offsets = offsets; dn.sorted_slots = sorted; dn.topk_w = topk_w; dn.y = y;
   dn.w_fmt = fmt; dn.s_down = dns; dn.s_stride = mx ? H * (I / 32) : H;
-  e = moe::launch_down_stream(dn, s);
+  e = moe::launch_down(dn, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert down (quantized weights)");
 }
 
@@ -418,9 +418,9 @@ int run_layer(const moe_dims* dims, int32_t T, const void* residual, const Layer
     // one group: the per-expert strides are never applied
     g.w_fmt = lw.fmt; g.s_gate = lw.dgs; g.s_up = lw.dus; g.s_stride = 0;
     dd.w_fmt = lw.fmt; dd.s_down = lw.dds; dd.s_stride = 0;
-    if ((e = moe::launch_gate_up_stream(g, s2)) != hipSuccess)
+    if ((e = moe::launch_gate_up(g, s2)) != hipSuccess)
       return hip_fail(e, "ffn layer (dense gate_up, quantized weights)");
-    if ((e = moe::launch_down_stream(dd, s2)) != hipSuccess)
+    if ((e = moe::launch_down(dd, s2)) != hipSuccess)
       return hip_fail(e, "ffn layer (dense down, quantized weights)");
   } else {
     if ((e = moe::launch_gate_up(g, s2)) != hipSuccess)
@@ -616,8 +616,6 @@ int moe_expert_ffn_q(const moe_dims* dims, int32_t fmt, int32_t T, const void* x
     return fail(MOE_ERR_ARG, "MXFP8 is an activation format, not an expert weight format here");
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "quantized experts take bf16 activations");
-  if (T > kMaxQuantTokens)
-    return fail(MOE_ERR_UNSUPPORTED, "quantized experts: T <= %d only", kMaxQuantTokens);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x); REQUIRE_PTR(w_gate_up_q); REQUIRE_PTR(w_gate_up_scale); REQUIRE_PTR(w_down_q);
   REQUIRE_PTR(w_down_scale); REQUIRE_PTR(topk_w); REQUIRE_PTR(expert_offsets);
@@ -841,8 +839,6 @@ int gemma4_ffn_block_q(const moe_dims* dims, int32_t T, const void* residual,
     return fail(MOE_ERR_UNSUPPORTED, "gemma4_ffn_block_q needs dense_inter > 0");
   if (dims->act_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "quantized layer takes bf16 activations");
-  if (T > kMaxQuantTokens)
-    return fail(MOE_ERR_UNSUPPORTED, "quantized layer: T <= %d only", kMaxQuantTokens);
   g_err.clear();
   if (T == 0) return MOE_OK;
   if (!wt) return fail(MOE_ERR_ARG, "weights is NULL");

@@ -140,8 +140,10 @@ def test_quantized_block_validates():
     w.fmt = lib_mod.MOE_W_INT8
     wp = ctypes.byref(w)
     args = (FAKE, wp, FAKE, None, None, None, FAKE, 1 << 40, None)
-    assert Lq(dp, 257, *args) == lib_mod.MOE_ERR_UNSUPPORTED
-    assert "T <= 256" in lib_mod.last_error()
+    # past 256 tokens the tiled kernels take over: validation goes on to the
+    # workspace check
+    assert Lq(dp, 257, FAKE, wp, FAKE, None, None, None, FAKE, 0,
+              None) == lib_mod.MOE_ERR_WORKSPACE
     d32 = D(act=lib_mod.MOE_F32)
     assert Lq(ctypes.byref(d32), 4, *args) == lib_mod.MOE_ERR_UNSUPPORTED
     d0 = D(dense_inter=0)
@@ -192,8 +194,7 @@ def test_int8_entry_points_validate_on_the_host():
     d = D()
     args = [FAKE] * 10
     assert f(ctypes.byref(d), 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
-    assert f(ctypes.byref(d), 257, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
-    assert "T <= 256" in lib_mod.last_error()
+    assert f(ctypes.byref(d), 4097, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
     d32 = D(act=lib_mod.MOE_F32)
     assert f(ctypes.byref(d32), 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     bad = list(args)
@@ -268,7 +269,7 @@ def test_quantized_format_entry_points_validate_on_the_host():
     args = [FAKE] * 10
     assert ffn(ctypes.byref(d), F8, 0, *([None] * 10), 0, None) == lib_mod.MOE_OK
     assert ffn(ctypes.byref(d), 0, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_ARG
-    assert ffn(ctypes.byref(d), MX, 257, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
+    assert ffn(ctypes.byref(d), MX, 4097, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE
     d32 = D(act=lib_mod.MOE_F32)
     assert ffn(ctypes.byref(d32), F8, 4, *args, 1 << 40, None) == lib_mod.MOE_ERR_UNSUPPORTED
     assert ffn(ctypes.byref(d), MX, 4, *args, 0, None) == lib_mod.MOE_ERR_WORKSPACE

@@ -10,8 +10,9 @@ quantizer matches bit for bit, tests/test_gpu_int8.py and test_gpu_lowp.py);
 the GPU runs the layer on those codes, and the oracle runs its layer on the
 dequantized weights.  Routing is bit-exact (the router stays fp32); the
 layer output and its pre-residual part are within 2e-2 x RMS, every row, at
-one token, at a decode batch (64 tokens) and at the largest batch the
-quantized layer takes (256 tokens)."""
+one token, at a decode batch (64 tokens), at the largest batch of the
+weight-streaming kernels (256 tokens) and past it (640 tokens: the tiled
+grouped GEMMs for the experts and the dense branch)."""
 import numpy as np
 import pytest
 import torch
@@ -38,7 +39,7 @@ MATRICES = ("dense_gate", "dense_up", "dense_down", "gate_up", "down")
 
 @pytest.fixture(scope="module")
 def case():
-    return synth.block_case(256, seed=8)
+    return synth.block_case(640, seed=8)
 
 
 def _weights(b, name):
@@ -73,7 +74,7 @@ def test_quantized_layer_26b(case, name):
     note(f"quantized layer {name}: oracle quantization")
     q = {n: quant(_weights(b, n).f32) for n in MATRICES}
     dq = {n: deq(*q[n]) for n in MATRICES}
-    for T in (1, 64, 256):
+    for T in (1, 64, 256, 640):
         note(f"quantized layer {name} T={T}")
         out, ffn, idx, w = _run(b, fmt, T, q)
         r = oracle.block(m.x.f32[:T], b.g_pre, b.g_pre2, b.g_post1, b.g_post2, b.g_post,
