@@ -363,7 +363,7 @@ int moe_forward(const moe_dims* dims, int32_t T, const void* x, const float* rou
  * the library loads on a device, held until the process ends) instead of a
  * caller buffer; the call makes no allocation of its own.  Sizes whose
  * workspace exceeds that array are refused with MOE_ERR_WORKSPACE (at
- * 26B-A4B shapes: up to 527 tokens; moe_forward needs less workspace than
+ * 26B-A4B shapes: up to 538 tokens; moe_forward needs less workspace than
  * moe_workspace_size, which also covers the MXFP8 buffers of
  * moe_expert_ffn_mx).  Every call on a
  * GPU shares that GPU's array: calls that may overlap on one GPU (two

@@ -23,7 +23,6 @@ struct RouterArgs {
   float* ws_r0;                  // [T]   inverse RMS of x (pre-norm), if pre_gain
   float* ws_r;                   // [T]   inverse RMS of the router input
   float* ws_logits;              // [T,E]
-  float* ws_wt;                  // [H,E] transposed weights (large batches) or nullptr
   unsigned* ws_counter;          // completion counter of the small-batch top-K kernel
   // Optional dispatch right after the top-K (all null = router only).
   int32_t* counts;               // [E]

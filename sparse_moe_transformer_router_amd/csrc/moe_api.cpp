@@ -91,7 +91,6 @@ struct Layout {
   size_t h;                         // expert gate_up output
   size_t idx, w, counts, offsets, sorted, y;  // experts-only path / layer
   size_t xd, xm, hd, dn;            // layer only
-  size_t wt;                        // router weights transposed
   size_t counter;                   // small-batch top-K completion counter
   size_t base_end;                  // end of the regions above (all but the MXFP8 ones)
   size_t xq, xs, hq, hs;            // MXFP8 activations of the 8-bit / 4-bit experts
@@ -125,7 +124,6 @@ Layout layout(const moe_dims* d, long long T) {
   L.xm = take(act * T * d->hidden);
   L.hd = take(act * T * d->dense_inter);
   L.dn = take(slot * T * d->hidden);
-  L.wt = take(4 * (size_t)d->num_experts * d->hidden);
   L.counter = take(4);
   L.base_end = o;
   L.xq = take((size_t)T * d->hidden);
@@ -231,7 +229,6 @@ int run_router(const moe_dims* d, int32_t T, const void* x, const float* router_
   a.per_expert_scale = pes; a.topk_idx = idx; a.topk_w = w;
   a.ws_r0 = at<float>(ws, L.r0); a.ws_r = at<float>(ws, L.r);
   a.ws_logits = at<float>(ws, L.logits);
-  a.ws_wt = at<float>(ws, L.wt);
   a.ws_counter = at<unsigned>(ws, L.counter);
   a.counts = counts; a.offsets = offsets; a.sorted_slots = sorted;
   a.ws_blk_counts = at<int32_t>(ws, L.blk_counts);

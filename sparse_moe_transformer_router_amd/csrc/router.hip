@@ -26,8 +26,9 @@
 // Large batches take three:
 //   router_prep   one wave per token: the inverse RMS of x (and, with a
 //                 pre-norm gain, of v = x * r0 * gain), in the fixed order;
-//   router_transpose  the weights [E, H] -> [H, E] (when E % 4 == 0);
-//   router_logits_split  a block takes 32 tokens x 64 experts, a thread 4
+//   router_logits_split  (E % 4 == 0) a block takes 32 tokens x 64 experts;
+//                 each chunk's weights are read from [E, H] and transposed
+//                 in registers on their way into LDS; a thread 4
 //                 tokens x 4 experts (16 chains, one 16-B weight and one 16-B
 //                 input LDS read per 16 fmas); the block's G wave groups take
 //                 the chunks in turn (chunk c to group c % G), and the
@@ -332,32 +333,12 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(
   }
 }
 
-// W [E, H] -> WT [H, E]; 32 x 32 tiles through LDS.
-__global__ __launch_bounds__(256) void router_transpose_kernel(int E, int H,
-                                                               const float* __restrict__ W,
-                                                               float* __restrict__ WT) {
-  __shared__ float tile[32][33];
-  const int h0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
-#pragma unroll
-  for (int i = ty; i < 32; i += 8) {
-    const int e = e0 + i, h = h0 + tx;
-    tile[i][tx] = (e < E && h < H) ? W[(size_t)e * H + h] : 0.0f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = ty; i < 32; i += 8) {
-    const int h = h0 + i, e = e0 + tx;
-    if (h < H && e < E) WT[(size_t)h * E + e] = tile[tx][i];
-  }
-}
-
 // Large batches, E % 4 == 0, chunks split over wave groups: block = 32 tokens
 // x 64 experts, G groups of 128 threads; group g takes chunks g, g + G, ...
 // Thread (tq, eq) of a group runs 16 chains: tokens 4 tq .. 4 tq + 3 x
 // experts 4 eq .. 4 eq + 3, with one 16-B weight read and one 16-B input
-// read per 16 fmas.  Per round every group stages its chunk (transposed
-// weights [64][64], router input [64][32 + 4]) in its own LDS region, runs
+// read per 16 fmas.  Per round every group stages its chunk (weights
+// transposed to [64 k][64 e], router input [64][32 + 4]) in its own LDS region, runs
 // its chains, and groups 1 .. G-1 leave their chunk results in LDS, which
 // group 0 adds to its totals in chunk order.
 constexpr int kSplitT = 32, kSplitE = 64, kSplitVP = kSplitT + 4;
@@ -365,7 +346,7 @@ template <typename XT, int G>
 __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
     const float* __restrict__ r0v, const float* __restrict__ rv,
-    const float* __restrict__ scale, const float* __restrict__ WT, float* __restrict__ logits) {
+    const float* __restrict__ scale, const float* __restrict__ W, float* __restrict__ logits) {
   __shared__ __align__(16) float wl[G][kChunk][kSplitE];
   __shared__ __align__(16) float vl[G][kChunk][kSplitVP];
   __shared__ float ex[G > 1 ? G - 1 : 1][16][128];
@@ -381,14 +362,23 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
   const float r0 = pre ? r0v[tcl] : 0.0f, r = rv[tcl];
   const XT* xr = x + (size_t)tcl * H + sk;
 
+  // The chunk's weights come straight from W [E, H]: pair q = j * 128 + tig
+  // (j < 2) of this thread is expert quad q % 16 and k quad q / 16; its 4 x 4
+  // block (4 rows of 16 B) is transposed in registers and stored as 4 float4
+  // along the experts, so the LDS tile is W^T [k][e] as the chains read it.
   float4 wreg[8];
   float xv[16], sv[16], gv[16];
   auto gload = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = j * 128 + tig, k = f / 16, e = e0 + 4 * (f % 16);
-      wreg[j] = e < E ? *reinterpret_cast<const float4*>(WT + (size_t)(c * kChunk + k) * E + e)
-                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = 0; j < 2; ++j) {
+      const int q = j * 128 + tig, eq = q % 16, kq = q / 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 4 * eq + i;
+        wreg[4 * j + i] =
+            e < E ? *reinterpret_cast<const float4*>(W + (size_t)e * H + c * kChunk + 4 * kq)
+                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
     }
     load8(xr + c * kChunk, xv);
     load8(xr + c * kChunk + 8, xv + 8);
@@ -404,9 +394,13 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
   };
   auto lstore = [&]() {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = j * 128 + tig;
-      *reinterpret_cast<float4*>(&wl[g][f / 16][4 * (f % 16)]) = wreg[j];
+    for (int j = 0; j < 2; ++j) {
+      const int q = j * 128 + tig, eq = q % 16, kq = q / 16;
+      const float4* b = wreg + 4 * j;  // b[i] = expert 4 eq + i, k 4 kq .. 4 kq + 3
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 0][4 * eq]) = make_float4(b[0].x, b[1].x, b[2].x, b[3].x);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 1][4 * eq]) = make_float4(b[0].y, b[1].y, b[2].y, b[3].y);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 2][4 * eq]) = make_float4(b[0].z, b[1].z, b[2].z, b[3].z);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 3][4 * eq]) = make_float4(b[0].w, b[1].w, b[2].w, b[3].w);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) vl[g][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
@@ -592,16 +586,16 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
                      a.eps, x, a.pre_gain, a.ws_r0, a.ws_r);
-  if (a.E % 4 == 0 && a.ws_wt != nullptr) {
-    hipLaunchKernelGGL(router_transpose_kernel, dim3((a.H + 31) / 32, (a.E + 31) / 32), dim3(256),
-                       0, s, a.E, a.H, a.router_w, a.ws_wt);
+  if (a.E % 4 == 0) {
     const dim3 sg((a.T + kSplitT - 1) / kSplitT, (a.E + kSplitE - 1) / kSplitE);
     if ((long long)sg.x * sg.y <= kSplitOneBlockPerCu)
       hipLaunchKernelGGL((router_logits_split_kernel<XT, 4>), sg, dim3(512), 0, s, a.T, a.H, a.E,
-                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.ws_wt, a.ws_logits);
+                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
+                         a.ws_logits);
     else
       hipLaunchKernelGGL((router_logits_split_kernel<XT, 2>), sg, dim3(256), 0, s, a.T, a.H, a.E,
-                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.ws_wt, a.ws_logits);
+                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
+                         a.ws_logits);
   } else {
     hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
                        dim3(256), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0, a.ws_r,

@@ -300,6 +300,6 @@ def test_noalloc_forward_validates_on_the_host():
              None) == lib_mod.MOE_ERR_ARG
     assert f(dp, 4, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
              None) == lib_mod.MOE_ERR_ARG
-    assert f(dp, 528, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+    assert f(dp, 539, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
              None) == lib_mod.MOE_ERR_WORKSPACE
     assert "scratch" in lib_mod.last_error()

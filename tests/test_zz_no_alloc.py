@@ -62,6 +62,6 @@ def test_noalloc_rejects_sizes_beyond_its_array():
     d = lib.dims(2816, 128, 8, 704, 0)
     L = lib.raw()
     fake = ctypes.c_void_p(0x10000)
-    rc = L.moe_forward_noalloc(ctypes.byref(d), 528, fake, fake, fake, fake, fake, fake, fake,
+    rc = L.moe_forward_noalloc(ctypes.byref(d), 539, fake, fake, fake, fake, fake, fake, fake,
                                None, None, None)
     assert rc == lib.MOE_ERR_WORKSPACE and "scratch" in lib.last_error()
