@@ -487,8 +487,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int K,
 // so the top-K of the batch is spread over many CUs.  With counts != null
 // the last block to finish (a completion counter, zeroed by the logits kernel
 // of the same call) groups all T*K <= 1024 slots by expert.  The counter only
-// orders the blocks; every result is computed in one fixed order.
+// orders the blocks; every result is computed in one fixed order.  Up to
+// kTopkOneBlockTokens tokens one block does it all: its 16 waves take a token
+// each, the slots' experts stay in LDS, and the dispatch follows a block
+// barrier; no completion counter, so none of the device-scope release /
+// acquire fences around it (an L2 write-back and invalidate).  The route at
+// 1 token went 22 -> 18 us; from 32 tokens, where a wave would take two or
+// more tokens in turn, the spread-out form is faster (64 tokens: 24 against
+// 35 us).
 constexpr int kTopkTok = 4;
+constexpr int kTopkOneBlockTokens = kChunkWaves;
 __global__ __launch_bounds__(kChunkSlots) void route_topk_dispatch_kernel(
     int T, int E, int K, const float* __restrict__ logits, const float* __restrict__ pes,
     int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ counts,
@@ -498,7 +506,19 @@ __global__ __launch_bounds__(kChunkSlots) void route_topk_dispatch_kernel(
   __shared__ int totals[kMaxE];
   __shared__ int offs[kMaxE + 1];
   __shared__ int last;
+  __shared__ int slot_e[kChunkSlots];
   const int wave = threadIdx.x / kWave;
+  if (gridDim.x == 1) {  // uniform: the one-block form
+    for (int t = wave; t < T; t += kChunkWaves)
+      wave_topk(logits + (size_t)t * E, E, K, pes, idx + (size_t)t * K, w + (size_t)t * K,
+                counts != nullptr ? slot_e + t * K : nullptr);
+    if (counts == nullptr) return;
+    __syncthreads();
+    const bool valid = (int)threadIdx.x < T * K;
+    const int e = valid ? slot_e[threadIdx.x] : 0;
+    dispatch_lone_chunk(e, valid, E, counts, offsets, sorted_slots, wave_base, totals, offs);
+    return;
+  }
   const int t = blockIdx.x * kTopkTok + wave;
   if (wave < kTopkTok && t < T)
     wave_topk(logits + (size_t)t * E, E, K, pes, idx + (size_t)t * K, w + (size_t)t * K, nullptr);
@@ -576,7 +596,8 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
     // 12 tokens 21 -> 14 us, at 32 tokens 21 -> 19 us; from 40 tokens 8 win
     else if (a.T <= 32) launch_small<XT, 4, 1>(a, fuse, s);
     else launch_small<XT, 4, 2>(a, fuse, s);
-    hipLaunchKernelGGL(route_topk_dispatch_kernel, dim3((a.T + kTopkTok - 1) / kTopkTok),
+    const int tb = a.T <= kTopkOneBlockTokens ? 1 : (a.T + kTopkTok - 1) / kTopkTok;
+    hipLaunchKernelGGL(route_topk_dispatch_kernel, dim3(tb),
                        dim3(kChunkSlots), 0, s, a.T, a.E, a.K, a.ws_logits, a.per_expert_scale,
                        a.topk_idx, a.topk_w, fuse ? a.counts : nullptr, a.offsets,
                        a.sorted_slots, a.ws_counter);
