@@ -96,3 +96,18 @@ def test_experts_q_26b_prefill_skewed(skew26b, name):
     note(f"experts {name} 26B prefill 4096 skewed")
     y, out = _q_path(c, fmt, c.T, c.x, idx, w, q)
     _check(name, c, c.x.f32, idx, w, q, y, out)
+
+
+@pytest.mark.parametrize("name", list(FORMATS))
+@pytest.mark.parametrize("H,I", [(8192, 256), (256, 8192)])
+def test_experts_q_tiled_longest_contraction(name, H, I):
+    """The longest contraction the ABI takes (8192) on either GEMM, past 256
+    tokens: 256 k-tiles, and for MXFP4 a full 256-byte block-scale row per
+    weight row staged in LDS."""
+    fmt, quant, _, _ = FORMATS[name]
+    c = synth.tiny_case(seed=14, T=264, H=H, E=4, K=2, I=I, bf16=True)
+    q = (*quant(c.gate_up.f32), *quant(c.down.f32))
+    idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note(f"experts {name} tiled, H={H} I={I}")
+    y, out = _q_path(c, fmt, c.T, c.x, idx, w, q)
+    _check(name, c, c.x.f32, idx, w, q, y, out)
