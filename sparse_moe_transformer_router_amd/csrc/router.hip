@@ -342,6 +342,9 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(
 // its chains, and groups 1 .. G-1 leave their chunk results in LDS, which
 // group 0 adds to its totals in chunk order.
 constexpr int kSplitT = 32, kSplitE = 64, kSplitVP = kSplitT + 4;
+// Column swizzle of the staged weight tile: k quad kq's expert quads are
+// permuted by an XOR with 2 (kq mod 8), a bijection on 0 .. 15.
+__device__ __forceinline__ int wswz(int kq) { return 2 * (kq & 7); }
 template <typename XT, int G>
 __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
@@ -362,26 +365,41 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
   const float r0 = pre ? r0v[tcl] : 0.0f, r = rv[tcl];
   const XT* xr = x + (size_t)tcl * H + sk;
 
-  // The chunk's weights come straight from W [E, H]: pair q = j * 128 + tig
-  // (j < 2) of this thread is expert quad q % 16 and k quad q / 16; its 4 x 4
-  // block (4 rows of 16 B) is transposed in registers and stored as 4 float4
-  // along the experts, so the LDS tile is W^T [k][e] as the chains read it.
+  // The chunk's weights come straight from W [E, H].  Pair j (< 2) of this
+  // thread is expert quad eq = tig / 8 and k quad kq = tig % 8 + 8 j, so the 8
+  // lanes of an expert row read 128 contiguous bytes and one load instruction
+  // covers 8 whole lines.  Its 4 x 4 block (4 rows of 16 B) is transposed in
+  // registers and stored as 4 float4 along the experts: the LDS tile is
+  // W^T [k][e] as the chains read it, with expert quad column eq ^ wswz(kq),
+  // so that the 16 lanes of a store phase fill 16 distinct bank quads.
+  // The input stays as loaded (bf16 bits or fp32) until lstore, so nothing
+  // waits on these loads before the round's chains run.
+  constexpr bool kBf16In = std::is_same<XT, bf16>::value;
   float4 wreg[8];
+  uint4 xu[2];
   float xv[16], sv[16], gv[16];
   auto gload = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int q = j * 128 + tig, eq = q % 16, kq = q / 16;
+      const int eqj = tig / 8, kq = tig % 8 + 8 * j;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = e0 + 4 * eq + i;
+        // Rows past E (a partial last expert tile) load row E - 1: only the
+        // chains of experts past E read them, and those results are dropped.
+        // No condition around the load, so the loads of a chunk all go out
+        // before the first wait.
+        const int e = min(e0 + 4 * eqj + i, E - 1);
         wreg[4 * j + i] =
-            e < E ? *reinterpret_cast<const float4*>(W + (size_t)e * H + c * kChunk + 4 * kq)
-                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            *reinterpret_cast<const float4*>(W + (size_t)e * H + c * kChunk + 4 * kq);
       }
     }
-    load8(xr + c * kChunk, xv);
-    load8(xr + c * kChunk + 8, xv + 8);
+    if constexpr (kBf16In) {
+      xu[0] = *reinterpret_cast<const uint4*>(xr + c * kChunk);
+      xu[1] = *reinterpret_cast<const uint4*>(xr + c * kChunk + 8);
+    } else {
+      load8(reinterpret_cast<const float*>(xr) + c * kChunk, xv);
+      load8(reinterpret_cast<const float*>(xr) + c * kChunk + 8, xv + 8);
+    }
     load8(scale + c * kChunk + sk, sv);
     load8(scale + c * kChunk + sk + 8, sv + 8);
     if (pre) {
@@ -393,14 +411,26 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     }
   };
   auto lstore = [&]() {
+    if constexpr (kBf16In) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned u[4] = {xu[h].x, xu[h].y, xu[h].z, xu[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[8 * h + 2 * i] = __uint_as_float(u[i] << 16);
+          xv[8 * h + 2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int q = j * 128 + tig, eq = q % 16, kq = q / 16;
-      const float4* b = wreg + 4 * j;  // b[i] = expert 4 eq + i, k 4 kq .. 4 kq + 3
-      *reinterpret_cast<float4*>(&wl[g][4 * kq + 0][4 * eq]) = make_float4(b[0].x, b[1].x, b[2].x, b[3].x);
-      *reinterpret_cast<float4*>(&wl[g][4 * kq + 1][4 * eq]) = make_float4(b[0].y, b[1].y, b[2].y, b[3].y);
-      *reinterpret_cast<float4*>(&wl[g][4 * kq + 2][4 * eq]) = make_float4(b[0].z, b[1].z, b[2].z, b[3].z);
-      *reinterpret_cast<float4*>(&wl[g][4 * kq + 3][4 * eq]) = make_float4(b[0].w, b[1].w, b[2].w, b[3].w);
+      const int eqj = tig / 8, kq = tig % 8 + 8 * j;
+      const int col = 4 * (eqj ^ wswz(kq));
+      const float4* b = wreg + 4 * j;  // b[i] = expert 4 eqj + i, k 4 kq .. 4 kq + 3
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 0][col]) = make_float4(b[0].x, b[1].x, b[2].x, b[3].x);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 1][col]) = make_float4(b[0].y, b[1].y, b[2].y, b[3].y);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 2][col]) = make_float4(b[0].z, b[1].z, b[2].z, b[3].z);
+      *reinterpret_cast<float4*>(&wl[g][4 * kq + 3][col]) = make_float4(b[0].w, b[1].w, b[2].w, b[3].w);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) vl[g][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
@@ -426,7 +456,7 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     if (have) {
 #pragma unroll 8
       for (int k = 0; k < kChunk; ++k) {
-        const float4 w = *reinterpret_cast<const float4*>(&wl[g][k][4 * eq]);
+        const float4 w = *reinterpret_cast<const float4*>(&wl[g][k][4 * (eq ^ wswz(k / 4))]);
         const float4 v = *reinterpret_cast<const float4*>(&vl[g][k][4 * tq]);
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
