@@ -19,6 +19,7 @@
 // data layout.  For the 32x32x64 form: row l % 32, group g = l / 32, an
 // 8-bit operand's bytes k = 16g .. 16g + 15 then 32 + 16g .. 32 + 16g + 15,
 // a 4-bit operand's k = 32g .. 32g + 31.
+#include <initializer_list>
 #include <type_traits>
 
 #include "common.h"
@@ -107,18 +108,24 @@ __global__ __launch_bounds__(256) void mx8_dequantize_kernel(long long nblocks, 
   for (int i = 0; i < 32; ++i) dst[i] = e4m3_value(src[i]) * sc;
 }
 
-// One lane's operand of a 128-k block.  o0 / o1: byte offsets (within the
-// row) of its two 16-byte halves (8-bit formats) or of its one half (4-bit),
-// already clamped into the row; v0 / v1: whether each half lies inside the
-// contraction (else it contributes zero codes).
+// One lane's operand of a 128-k block as loaded.  o0 / o1: byte offsets
+// (within the row) of its two 16-byte halves (8-bit formats) or of its one
+// half (4-bit), already clamped into the row.
 template <int OP>
-__device__ __forceinline__ i32x8 ld_op(const uint8_t* row, int o0, int o1, bool v0, bool v1) {
+__device__ __forceinline__ i32x8 ld_op(const uint8_t* row, int o0, int o1) {
   const uint4 a = *reinterpret_cast<const uint4*>(row + o0);
   uint4 b = make_uint4(0, 0, 0, 0);
   if constexpr (OP == kOpFp8) b = *reinterpret_cast<const uint4*>(row + o1);
-  const uint4 za = keep4(a, v0), zb = keep4(b, v1);
-  return i32x8{(int)za.x, (int)za.y, (int)za.z, (int)za.w,
-               (int)zb.x, (int)zb.y, (int)zb.z, (int)zb.w};
+  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// Zeroes the halves of an operand that lie past the contraction (v0 / v1:
+// whether each half lies inside it).  Applied where the operand is used, in
+// the k-blocks that reach past the end only, so that no load is waited for
+// before its k-block's matrix instructions.
+__device__ __forceinline__ i32x8 keep_op(i32x8 v, bool v0, bool v1) {
+  return i32x8{v0 ? v[0] : 0, v0 ? v[1] : 0, v0 ? v[2] : 0, v0 ? v[3] : 0,
+               v1 ? v[4] : 0, v1 ? v[5] : 0, v1 ? v[6] : 0, v1 ? v[7] : 0};
 }
 
 // Byte offsets and validity of lane group g's share of 128-k block kb of a
@@ -161,16 +168,29 @@ template <int OP> struct MxWeights {
   static constexpr bool kChannelScale = OP == kOpFp8;
 };
 
+// Scale staging of the decode kernels (MXFP4 weights, SU > 0): the E8M0
+// scale rows of a block's weight rows go to LDS once, in SU-byte pieces (SU
+// divides the row length and every row's offset), up to kStgPieces pieces
+// per thread, all loaded before the ring's first operand loads.  The k-loop
+// then loads the weight codes alone; their scale bytes come from LDS.
+// Loaded in the k-loop, one byte per lane, the weight scales were as many
+// loads as the weight codes.
+constexpr int kStgPieces = 8;
+template <int SU>
+using StgPiece = typename std::conditional<SU == 8, uint2, unsigned short>::type;
+
 // ---------------------------------------------------------------------------
 // Decode sizes: the weights streamed once per 16 * MB-row tile of an expert.
 // gate_up: one block = one row tile x NC groups of 16 gate + 16 up columns;
 // WK waves split the contraction H in 128-k blocks.  Each lane loads its
 // weight spans straight into registers, NS - 1 k-blocks ahead of the
-// matrix instructions; loads are unconditional (addresses clamped into
-// their rows, out-of-range spans zeroed at load), so the waits count only
-// what a step needs.
+// matrix instructions.  Loads are unconditional (addresses clamped into
+// their rows) and issued in ring order, and the spans past the contraction
+// are zeroed where they are used, in the tail k-blocks only, so that each
+// step waits for its own slot alone (a condition around a load, or a value
+// masked right after it, made the compiler drain the whole ring there).
 // ---------------------------------------------------------------------------
-template <int OP, int WK, int MB, int NS, int NC>
+template <int OP, int WK, int MB, int NS, int NC, int SU>
 __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
     int H, int N, int E, int K, int rows, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xs, const uint8_t* __restrict__ wg,
@@ -181,7 +201,11 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
   typedef MxWeights<OP> W;
   static_assert(NS >= 2, "the load ring needs two slots or more");
   static_assert(NC % 2 == 0, "a 32-column MXFP8 block of h spans two column groups");
+  static_assert(SU == 0 || (OP == kOpFp4 && (SU == 2 || SU == 8)), "scale staging: MXFP4 only");
   __shared__ f32x4 red[WK][MB][NC][2][kWave];
+  // staged weight scale rows: gate rows 16 c + r, up rows 16 NC + 16 c + r,
+  // nsb bytes each
+  extern __shared__ __align__(16) uint8_t sst[];
   int e, row0, row1, cg;
   const int CG = (N + 16 * NC - 1) / (16 * NC);
   if (!stream_item(false, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
@@ -218,6 +242,24 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
   const int KB = (H + 127) / 128;
   const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
 
+  constexpr int NRW = 32 * NC;  // staged rows: 16 NC gate rows, then 16 NC up rows
+  StgPiece<SU == 0 ? 2 : SU> stv[SU > 0 ? kStgPieces : 1];
+  const int ppr = SU > 0 ? nsb / (SU > 0 ? SU : 1) : 1, npc = NRW * ppr;
+  if constexpr (SU > 0) {
+    // every piece is loaded and later stored unconditionally (the index
+    // clamped; surplus threads repeat the last piece), so that no wait lands
+    // before the ring's loads
+#pragma unroll
+    for (int i = 0; i < kStgPieces; ++i) {
+      const int j = min((int)threadIdx.x + i * 64 * WK, npc - 1), r = j / ppr;
+      const bool up = r >= 16 * NC;
+      const long long n = min(cg * 16 * NC + (up ? r - 16 * NC : r), N - 1);
+      const uint8_t* src = static_cast<const uint8_t*>(up ? su : sg) + e * s_stride + n * nsb;
+      stv[i] = *reinterpret_cast<const StgPiece<SU>*>(src + (j - r * ppr) * SU);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   f32x4 accg[MB][NC], accu[MB][NC];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -225,30 +267,60 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
     for (int c = 0; c < NC; ++c) accg[mb][c] = accu[mb][c] = f32x4{0, 0, 0, 0};
   i32x8 ra[NS][MB], rg[NS][NC], ru[NS][NC];
   uint32_t sa[NS][MB], sgw[NS][NC], suw[NS][NC];
-  auto load = [&](int kb, int slot) {
+  int kbs[NS];  // the k-block each ring slot holds
+  auto load_w = [&](int kb, int slot) {
     int o0, o1;
     bool v0, v1;
+    kbs[slot] = kb;
     op_span<kOpFp8>(kb, g, H, o0, o1, v0, v1);
     const int sb = min(kb * 4 + g, nsb - 1);  // natural 32-block of this lane
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1, v0, v1);
+      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1);
       sa[slot][mb] = asc[mb][sb];
     }
     op_span<OP>(kb, g, H, o0, o1, v0, v1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      rg[slot][c] = ld_op<OP>(grow[c], o0, o1, v0, v1);
-      ru[slot][c] = ld_op<OP>(urow[c], o0, o1, v0, v1);
+      rg[slot][c] = ld_op<OP>(grow[c], o0, o1);
+      ru[slot][c] = ld_op<OP>(urow[c], o0, o1);
+    }
+  };
+  // the weight scales (from LDS when staged)
+  auto load_s = [&](int kb, int slot) {
+    const int sb = min(kb * 4 + g, nsb - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
       if constexpr (W::kChannelScale) {
         sgw[slot][c] = suw[slot][c] = kUnitScale;
+      } else if constexpr (SU > 0) {
+        sgw[slot][c] = sst[(16 * c + fr) * nsb + sb];
+        suw[slot][c] = sst[(16 * NC + 16 * c + fr) * nsb + sb];
       } else {
         sgw[slot][c] = gsc[c][sb];
         suw[slot][c] = usc[c][sb];
       }
     }
   };
-  auto step = [&](int slot) {
+  auto load = [&](int kb, int slot) {
+    load_w(kb, slot);
+    load_s(kb, slot);
+  };
+  // CHECKED: the slot's k-block may reach past H (only in the tail loop).
+  auto step = [&](int slot, auto checked) {
+    if (decltype(checked)::value && (kbs[slot] + 1) * 128 > H) {  // uniform
+      int o0, o1;
+      bool v0, v1;
+      op_span<kOpFp8>(kbs[slot], g, H, o0, o1, v0, v1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ra[slot][mb] = keep_op(ra[slot][mb], v0, v1);
+      op_span<OP>(kbs[slot], g, H, o0, o1, v0, v1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        rg[slot][c] = keep_op(rg[slot][c], v0, v1);
+        ru[slot][c] = keep_op(ru[slot][c], v0, v1);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -260,16 +332,38 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
                                 accu[mb][c], std::integral_constant<int, OP>{});
         }
   };
+  // The ring's first NS - 1 slots, loaded unconditionally: a wave with
+  // fewer k-blocks loads a valid one again and never uses it.  (Loads under
+  // a condition make the waits after them count as if none had been issued.)
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (kb0 + s < kb1) load(kb0 + s, s);
+  for (int s = 0; s < NS - 1; ++s) {
+    const int kbp = max(min(kb0 + s, kb1 - 1), 0);
+    if constexpr (SU > 0) load_w(kbp, s);
+    else load(kbp, s);
+    __builtin_amdgcn_sched_barrier(0);  // slots issued in order
+  }
+  if constexpr (SU > 0) {
+#pragma unroll
+    for (int i = 0; i < kStgPieces; ++i) {
+      const int j = min((int)threadIdx.x + i * 64 * WK, npc - 1), r = j / ppr;
+      *reinterpret_cast<StgPiece<SU>*>(sst + r * nsb + (j - r * ppr) * SU) = stv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) load_s(max(min(kb0 + s, kb1 - 1), 0), s);
+  }
   int kb = kb0;
-  // steady state: every load of the unrolled NS steps lies inside the range
-  for (; kb + 2 * NS - 2 < kb1; kb += NS) {
+  // steady state: every load of the unrolled NS steps lies inside the range,
+  // and every k-block it loads lies wholly inside H, so no operand is masked
+  // and each step waits only for its own slot
+  const int kbf = min(kb1, H / 128);
+  for (; kb + 2 * NS - 2 < kbf; kb += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       load(kb + s + NS - 1, (s + NS - 1) % NS);
-      step(s);
+      __builtin_amdgcn_sched_barrier(0);
+      step(s, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   for (; kb < kb1; kb += NS) {
@@ -277,7 +371,7 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
     for (int s = 0; s < NS; ++s) {
       if (kb + s >= kb1) break;
       if (kb + s + NS - 1 < kb1) load(kb + s + NS - 1, (s + NS - 1) % NS);
-      step(s);
+      step(s, std::true_type{});
     }
   }
 #pragma unroll
@@ -347,7 +441,7 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
 // down: one block = one row tile x WN waves of NC groups of 16 output
 // columns (the contraction, the expert width, is short and is not split).
 // A = the tile's rows of h in MXFP8 (expert-sorted order).
-template <int OP, int WN, int MB, int NS, int NC, typename YT>
+template <int OP, int WN, int MB, int NS, int NC, int SU, typename YT>
 __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
     int H, int N, int E, int rows, const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
     const uint8_t* __restrict__ wd, long long w_stride, const void* __restrict__ sd,
@@ -356,6 +450,10 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
     YT* __restrict__ y) {
   typedef MxWeights<OP> W;
   static_assert(NS >= 2, "the load ring needs two slots or more");
+  static_assert(SU == 0 || (OP == kOpFp4 && (SU == 2 || SU == 8)), "scale staging: MXFP4 only");
+  // staged weight scale rows: row 16 NC w + 16 c + r is wave w's column
+  // group c, lane row r; nsb bytes each
+  extern __shared__ __align__(16) uint8_t sst[];
   int e, row0, row1, cg;
   const int CG = (H + 16 * WN * NC - 1) / (16 * WN * NC);
   if (!stream_item(false, rows, offsets, E, 16 * MB, CG, e, row0, row1, cg)) return;
@@ -383,6 +481,20 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
     asc[mb] = hs + (long long)rr * nsb;
   }
   const int KB = (N + 127) / 128;
+  constexpr int NRW = 16 * WN * NC;  // staged rows
+  StgPiece<SU == 0 ? 2 : SU> stv[SU > 0 ? kStgPieces : 1];
+  const int ppr = SU > 0 ? nsb / (SU > 0 ? SU : 1) : 1, npc = NRW * ppr;
+  if constexpr (SU > 0) {
+    // unconditional loads and stores, as in gate_up
+#pragma unroll
+    for (int i = 0; i < kStgPieces; ++i) {
+      const int j = min((int)threadIdx.x + i * 64 * WN, npc - 1), r = j / ppr;
+      const long long n = min(cg * 16 * WN * NC + r, H - 1);
+      const uint8_t* src = static_cast<const uint8_t*>(sd) + e * s_stride + n * nsb;
+      stv[i] = *reinterpret_cast<const StgPiece<SU>*>(src + (j - r * ppr) * SU);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   f32x4 acc[MB][NC];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -390,24 +502,48 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
     for (int c = 0; c < NC; ++c) acc[mb][c] = f32x4{0, 0, 0, 0};
   i32x8 ra[NS][MB], rb[NS][NC];
   uint32_t sa[NS][MB], sb[NS][NC];
-  auto load = [&](int kb, int slot) {
+  int kbs[NS];  // the k-block each ring slot holds
+  auto load_w = [&](int kb, int slot) {
     int o0, o1;
     bool v0, v1;
+    kbs[slot] = kb;
     op_span<kOpFp8>(kb, g, N, o0, o1, v0, v1);
     const int s8 = min(kb * 4 + g, nsb - 1);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1, v0, v1);
+      ra[slot][mb] = ld_op<kOpFp8>(arow[mb], o0, o1);
       sa[slot][mb] = asc[mb][s8];
     }
     op_span<OP>(kb, g, N, o0, o1, v0, v1);
 #pragma unroll
+    for (int c = 0; c < NC; ++c) rb[slot][c] = ld_op<OP>(brow[c], o0, o1);
+  };
+  // the weight scales (from LDS when staged)
+  auto load_s = [&](int kb, int slot) {
+    const int s8 = min(kb * 4 + g, nsb - 1);
+#pragma unroll
     for (int c = 0; c < NC; ++c) {
-      rb[slot][c] = ld_op<OP>(brow[c], o0, o1, v0, v1);
-      sb[slot][c] = W::kChannelScale ? kUnitScale : (uint32_t)bsc[c][s8];
+      if constexpr (W::kChannelScale) sb[slot][c] = kUnitScale;
+      else if constexpr (SU > 0) sb[slot][c] = sst[(16 * NC * wave + 16 * c + fr) * nsb + s8];
+      else sb[slot][c] = bsc[c][s8];
     }
   };
-  auto step = [&](int slot) {
+  auto load = [&](int kb, int slot) {
+    load_w(kb, slot);
+    load_s(kb, slot);
+  };
+  // CHECKED: the slot's k-block may reach past N (only in the tail loop).
+  auto step = [&](int slot, auto checked) {
+    if (decltype(checked)::value && (kbs[slot] + 1) * 128 > N) {  // uniform
+      int o0, o1;
+      bool v0, v1;
+      op_span<kOpFp8>(kbs[slot], g, N, o0, o1, v0, v1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ra[slot][mb] = keep_op(ra[slot][mb], v0, v1);
+      op_span<OP>(kbs[slot], g, N, o0, o1, v0, v1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) rb[slot][c] = keep_op(rb[slot][c], v0, v1);
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -416,15 +552,33 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
           acc[mb][c] = mfma_mx(ra[slot][mb], sa[slot][mb], rb[slot][c], sb[slot][c], acc[mb][c],
                                std::integral_constant<int, OP>{});
   };
+  // the ring's first slots, unconditionally (as in gate_up)
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < KB) load(s, s);
+  for (int s = 0; s < NS - 1; ++s) {
+    if constexpr (SU > 0) load_w(min(s, KB - 1), s);
+    else load(min(s, KB - 1), s);
+    __builtin_amdgcn_sched_barrier(0);  // slots issued in order
+  }
+  if constexpr (SU > 0) {
+#pragma unroll
+    for (int i = 0; i < kStgPieces; ++i) {
+      const int j = min((int)threadIdx.x + i * 64 * WN, npc - 1), r = j / ppr;
+      *reinterpret_cast<StgPiece<SU>*>(sst + r * nsb + (j - r * ppr) * SU) = stv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) load_s(min(s, KB - 1), s);
+  }
   int kb = 0;
-  for (; kb + 2 * NS - 2 < KB; kb += NS) {
+  // steady state as in gate_up: k-blocks wholly inside N, nothing masked
+  const int kbf = N / 128;
+  for (; kb + 2 * NS - 2 < kbf; kb += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       load(kb + s + NS - 1, (s + NS - 1) % NS);
-      step(s);
+      __builtin_amdgcn_sched_barrier(0);
+      step(s, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   for (; kb < KB; kb += NS) {
@@ -432,7 +586,7 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
     for (int s = 0; s < NS; ++s) {
       if (kb + s >= KB) break;
       if (kb + s + NS - 1 < KB) load(kb + s + NS - 1, (s + NS - 1) % NS);
-      step(s);
+      step(s, std::true_type{});
     }
   }
 #pragma unroll
@@ -900,6 +1054,18 @@ hipError_t launch_mx_tiled(const MxArgs& a, hipStream_t s) {
                                                 a.down_s, a.down_s, dss, s);
 }
 
+// Piece size of the scale staging (8 or 2 bytes; 0: none): it must divide
+// the row length nsb and every base address and stride in `align`, and the
+// nrows rows must fit kStgPieces pieces per thread of the block.
+int stage_unit(long long nsb, int nrows, int nthreads, std::initializer_list<uintptr_t> align) {
+  for (int u : {8, 2}) {
+    bool ok = nsb % u == 0 && nrows * (nsb / u) <= (long long)kStgPieces * nthreads;
+    for (uintptr_t v : align) ok = ok && v % u == 0;
+    if (ok) return u;
+  }
+  return 0;
+}
+
 template <int OP, int WK, int MB, int NS, int NC>
 void launch_gu_mx(const MxArgs& a, hipStream_t s) {
   const long long cgs = (a.I + 16 * NC - 1) / (16 * NC);
@@ -918,9 +1084,20 @@ void launch_gu_mx(const MxArgs& a, hipStream_t s) {
     us = static_cast<const uint8_t*>(gs) + I * (H / 32);
     ss = 2 * I * (H / 32);
   }
-  hipLaunchKernelGGL((gate_up_mx_kernel<OP, WK, MB, NS, NC>), grid, dim3(64 * WK), 0, s, a.H,
-                     a.I, a.E, a.K, a.rows, a.xq, a.xs, gq, uq, 2 * I * H, gs, us, ss, a.offsets,
-                     a.sorted_slots, a.hq, a.hs);
+  auto go = [&](auto su_tag) {
+    constexpr int SU = decltype(su_tag)::value;
+    const size_t lds = SU > 0 ? (size_t)(32 * NC) * (H / 32) : 0;
+    hipLaunchKernelGGL((gate_up_mx_kernel<OP, WK, MB, NS, NC, SU>), grid, dim3(64 * WK), lds, s,
+                       a.H, a.I, a.E, a.K, a.rows, a.xq, a.xs, gq, uq, 2 * I * H, gs, us, ss,
+                       a.offsets, a.sorted_slots, a.hq, a.hs);
+  };
+  if constexpr (OP == kOpFp4) {
+    const int su = stage_unit(H / 32, 32 * NC, 64 * WK,
+                              {(uintptr_t)gs, (uintptr_t)us, (uintptr_t)ss});
+    if (su == 8) return go(std::integral_constant<int, 8>{});
+    if (su == 2) return go(std::integral_constant<int, 2>{});
+  }
+  go(std::integral_constant<int, 0>{});
 }
 
 template <int OP, int WN, int MB, int NS, int NC, typename YT>
@@ -929,18 +1106,46 @@ void launch_dn_mx(const MxArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(tile_count_bound(false, a.rows, a.T, a.E, 16 * MB) * cgs));
   const long long I = a.I, H = a.H;
   const long long ss = OP == kOpFp8 ? H : H * (I / 32);
-  hipLaunchKernelGGL((down_mx_kernel<OP, WN, MB, NS, NC, YT>), grid, dim3(64 * WN), 0, s, a.H,
-                     a.I, a.E, a.rows, a.hq, a.hs, static_cast<const uint8_t*>(a.down_q), H * I,
-                     a.down_s, ss, a.offsets, a.sorted_slots, a.topk_w, static_cast<YT*>(a.y));
+  auto go = [&](auto su_tag) {
+    constexpr int SU = decltype(su_tag)::value;
+    const size_t lds = SU > 0 ? (size_t)(16 * WN * NC) * (I / 32) : 0;
+    hipLaunchKernelGGL((down_mx_kernel<OP, WN, MB, NS, NC, SU, YT>), grid, dim3(64 * WN), lds, s,
+                       a.H, a.I, a.E, a.rows, a.hq, a.hs, static_cast<const uint8_t*>(a.down_q),
+                       H * I, a.down_s, ss, a.offsets, a.sorted_slots, a.topk_w,
+                       static_cast<YT*>(a.y));
+  };
+  if constexpr (OP == kOpFp4) {
+    const int su = stage_unit(I / 32, 16 * WN * NC, 64 * WN, {(uintptr_t)a.down_s, (uintptr_t)ss});
+    if (su == 8) return go(std::integral_constant<int, 8>{});
+    if (su == 2) return go(std::integral_constant<int, 2>{});
+  }
+  go(std::integral_constant<int, 0>{});
 }
 
+// Configurations from a sweep at 1 / 8 / 64 / 256 tokens (26B shapes):
+// MXFP4 gate_up 2 waves x 2 column groups x ring depth 3 (16-row tiles up to
+// 128 tokens, 32-row past), down 4 waves x 2 column groups x depth 2; E4M3
+// gate_up 4 waves x 2 groups x depth 2, down 2 waves x 1 group x depth 2 up
+// to 128 tokens and 4 waves x 2 groups with 32-row tiles past.
 template <int OP>
 void launch_mx_stream(const MxArgs& a, hipStream_t s) {
-  constexpr int NCG = OP == kOpFp4 ? 4 : 2;
-  if (a.T <= 128) launch_gu_mx<OP, 2, 1, 3, NCG>(a, s);
-  else launch_gu_mx<OP, 2, 2, 3, NCG>(a, s);
-  if (a.y_bf16) launch_dn_mx<OP, 4, 1, 2, 1, bf16>(a, s);
-  else launch_dn_mx<OP, 4, 1, 2, 1, float>(a, s);
+  const bool small = a.T <= 128;
+  if constexpr (OP == kOpFp4) {
+    if (small) launch_gu_mx<OP, 2, 1, 3, 2>(a, s);
+    else launch_gu_mx<OP, 2, 2, 3, 2>(a, s);
+    if (a.y_bf16) launch_dn_mx<OP, 4, 1, 2, 2, bf16>(a, s);
+    else launch_dn_mx<OP, 4, 1, 2, 2, float>(a, s);
+  } else {
+    if (small) launch_gu_mx<OP, 4, 1, 2, 2>(a, s);
+    else launch_gu_mx<OP, 4, 2, 2, 2>(a, s);
+    if (small) {
+      if (a.y_bf16) launch_dn_mx<OP, 2, 1, 2, 1, bf16>(a, s);
+      else launch_dn_mx<OP, 2, 1, 2, 1, float>(a, s);
+    } else {
+      if (a.y_bf16) launch_dn_mx<OP, 4, 2, 2, 2, bf16>(a, s);
+      else launch_dn_mx<OP, 4, 2, 2, 2, float>(a, s);
+    }
+  }
 }
 
 }  // namespace
