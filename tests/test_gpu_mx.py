@@ -149,6 +149,21 @@ def test_experts_mx_small_ragged(name):
     assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) / bound))
 
 
+@pytest.mark.parametrize("name", ["fp8", "mxfp4"])
+def test_experts_mx_decode_scale_staging_shapes(name):
+    """Decode kernels at H = 8192, I = 256: MXFP4 gate_up's scale rows (256
+    bytes each) exceed what a block stages in LDS, so it loads them per
+    k-block instead, and down stages its 8-byte rows in 8-byte pieces; the
+    26B shapes (2- and 8-byte pieces) and the small ragged layer (2-byte
+    pieces, and odd 3-byte rows loaded per k-block) cover the other forms."""
+    c = synth.moe_case(40, seed=12, H=8192, E=8, K=2, I=256, weight_std=0.05)
+    quant = oracle.quantize_fp8 if name == "fp8" else oracle.quantize_mxfp4
+    q = (*quant(c.gate_up.f32), *quant(c.down.f32))
+    idx, w = oracle.router(c.x.f32, c.router_w, c.router_scale, c.per_expert_scale, c.K, c.eps)
+    note(f"experts {name} on 8/4-bit matrix cores, decode H=8192 I=256")
+    _check_mx(c, name, c.T, c.x, idx, w, q)
+
+
 def _check_mx(c, name, T, x, idx, w, q, full_rms=True):
     y, out = _mx_path(c, FMTS[name], T, x, idx, w, q)
     ref = _oracle_mx(name, x.f32, q, idx, w)
