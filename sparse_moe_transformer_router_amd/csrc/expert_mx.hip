@@ -240,7 +240,12 @@ __global__ __launch_bounds__(64 * WK) void gate_up_mx_kernel(
   }
   (void)rowb;
   const int KB = (H + 127) / 128;
-  const int kb0 = wave * KB / WK, kb1 = (wave + 1) * KB / WK;
+  // The waves split the contraction in whole 128-byte lines of the weight
+  // rows: an MXFP4 line holds two 128-weight blocks, and a line split between
+  // two waves was read from HBM twice (gate_up read 1.11x its bytes).
+  constexpr int KL = OP == kOpFp4 ? 2 : 1;  // k-blocks per line
+  const int KBL = (KB + KL - 1) / KL;
+  const int kb0 = min(KL * (wave * KBL / WK), KB), kb1 = min(KL * ((wave + 1) * KBL / WK), KB);
 
   constexpr int NRW = 32 * NC;  // staged rows: 16 NC gate rows, then 16 NC up rows
   StgPiece<SU == 0 ? 2 : SU> stv[SU > 0 ? kStgPieces : 1];
