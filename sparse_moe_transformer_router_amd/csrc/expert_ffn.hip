@@ -703,10 +703,18 @@ hipError_t launch_grouped(int Kd, int Nout, int E, int K, int rows, bool ident, 
   return hipSuccess;
 }
 
+// Ring depth of the tiled gate_up: bf16 takes 5 stages of 32 KB, the whole
+// 160 KB of LDS (2048 tokens 302 -> 280 us, 4096 skewed 428 -> 420 against
+// 4 stages); int8 and E4M3 (24 KB stages) take 6 (int8 at 2048 tokens 353 ->
+// 306 us); MXFP4 keeps 4, its scale rows sitting past the ring.  down stays
+// at 4 stages in every format (6 were 2-5% slower for int8 and E4M3).
+template <int WF>
+constexpr int gate_up_stages() { return WF == kWfBF16 ? 5 : WF == kWfMXFP4 ? 4 : 6; }
+
 template <int WF>
 hipError_t launch_gate_up_tiled(const GateUpArgs& a, hipStream_t s) {
   const int NT = (a.N + GN / 2 - 1) / (GN / 2);
-  return launch_grouped<true, 256, 4, 4, 4, float, WF>(
+  return launch_grouped<true, 256, 4, 4, gate_up_stages<WF>(), float, WF>(
       a.H, a.N, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
       static_cast<const bf16*>(a.x), a.w_gate, a.w_up, a.w_stride, a.s_gate, a.s_up, a.s_stride,
       a.offsets, a.sorted_slots, nullptr, static_cast<bf16*>(a.h), static_cast<float*>(nullptr),
