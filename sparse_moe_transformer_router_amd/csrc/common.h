@@ -135,8 +135,29 @@ __device__ __forceinline__ void row_tile_lookup(const RowTileScan& s,
   row1 = min(row0 + bm, offsets[e_out + 1]);
 }
 
-// Work items are (row tile, column tile) pairs, column tiles fastest.  Block
-// b of a 1-D grid runs on XCD b % 8 (workgroups go round-robin to the eight
+// Work item `item` of a grouped GEMM with NT column tiles -> expert, row
+// range and column tile, numbered expert by expert and, within an expert,
+// column tile by column tile with the expert's row tiles fastest: the row
+// tiles that stream the same weight slab are neighbours, so they run on one
+// XCD at about the same time and share the slab through its L2.  (Item i lies
+// in expert e's range exactly when tile i / NT is one of e's tiles.)
+__device__ __forceinline__ void weight_major_item(const RowTileScan& s,
+                                                  const int32_t* __restrict__ offsets, int bm,
+                                                  int item, int NT, int& e, int& row0,
+                                                  int& row1, int& nt) {
+  const int tile = item / NT;
+  row_tile_lookup(s, offsets, bm, tile, e, row0, row1);
+  const int first = tile - (row0 - offsets[e]) / bm;  // the expert's first tile
+  const int re = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  const int local = item - first * NT;
+  nt = local / re;
+  row0 = offsets[e] + (local % re) * bm;
+  row1 = min(row0 + bm, offsets[e + 1]);
+}
+
+// Work items are numbered in the order of the caller (stream_item: the
+// column groups of a row tile fastest; the tiled GEMMs: weight_major_item).
+// Block b of a 1-D grid runs on XCD b % 8 (workgroups go round-robin to the eight
 // XCDs); each XCD takes a contiguous range of the real items, so that items
 // sharing gathered rows or a weight slab run on one XCD at about the same time
 // and share its L2.  Blocks past an XCD's range get -1.  Needs gridDim.x >=

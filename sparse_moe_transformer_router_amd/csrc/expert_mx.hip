@@ -758,8 +758,7 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
     row_tile_scan(offsets, E, MXBM, sc);
     const int item = xcd_item(blockIdx.x, sc.total * NT);
     if (item < 0) return;  // uniform over the block
-    nt = item % NT;
-    row_tile_lookup(sc, offsets, MXBM, item / NT, e, row0, row1);
+    weight_major_item(sc, offsets, MXBM, item, NT, e, row0, row1, nt);
   }
   const int lane = lane_id(), wave = threadIdx.x / kWave, tid = threadIdx.x;
   const int wm = wave / WN, wn = wave % WN;
