@@ -8,14 +8,16 @@
 // Rows are the expert-sorted token-slots from the dispatch: expert e owns
 // rows [offsets[e], offsets[e+1]).  A block takes one row tile of one expert
 // (found from the offsets by one wave, no tile list needed) and one column
-// tile.  The dense MLP of the layer runs through the same kernels as a single
-// group whose rows are the tokens themselves.
+// tile; the row tiles of an expert that read the same weight slab are
+// consecutive work items.  The dense MLP of the layer runs through the same
+// kernels as a single group whose rows are the tokens themselves.
 //
 // bf16 path at prefill sizes (decode sizes use the weight-streaming kernels):
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation on 256 x 256 block tiles
 // of 16 waves; A rows are gathered from the token matrix by the per-lane
-// source addresses of direct global -> LDS copies into a 4-stage ring shared
-// with the weight tiles.  gate_up's epilogue applies GELU(gate) * up and
+// source addresses of direct global -> LDS copies into a ring shared with the
+// weight tiles (gate_up: 5 stages in bf16, 6 for 8-bit codes, 4 for MXFP4;
+// down: 4).  gate_up's epilogue applies GELU(gate) * up and
 // rounds h to bf16; down's epilogue multiplies each row by its routing weight
 // and writes it to the slot-major output; both leave through LDS-staged rows.
 // Weights stored as int8, E4M3 or MXFP4 take the same kernels past the
