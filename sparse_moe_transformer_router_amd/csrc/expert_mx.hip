@@ -1065,7 +1065,9 @@ __global__ __launch_bounds__(512, 1) void grouped_mx_kernel(
           const float o[4] = {sc * (v.x * cs.x), sc * (v.y * cs.y), sc * (v.z * cs.z),
                               sc * (v.w * cs.w)};
           if constexpr (std::is_same<YT, float>::value) {
-            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            // streaming stores, as in the bf16 tiled down: read once, by the combine
+            const f32x4 ov = {o[0], o[1], o[2], o[3]};
+            __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(dst));
           } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u) dst[u] = from_f32<YT>(o[u]);
