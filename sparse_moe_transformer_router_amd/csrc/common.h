@@ -204,12 +204,18 @@ __device__ __forceinline__ bool stream_item(bool ident, int rows, const int32_t*
   return true;
 }
 
-// Upper bound on the number of bm-row tiles over all groups (host side).
+// Upper bound on the number of bm-row tiles over all groups (host side): a
+// tile holds at least one row, each group has at most bm - 1 rows of
+// padding, and a group (an expert) holds at most T rows.  The grids of the
+// grouped kernels are this bound times their column tiles; blocks past the
+// real items exit at once (at 1 token: 8 row tiles, not the 60 of the first
+// two terms).
 inline int tile_count_bound(bool ident, int rows, int T, int E, int bm) {
   if (ident) return (rows + bm - 1) / bm;
-  const long long a = ((long long)rows + (long long)E * (bm - 1)) / bm;
-  const long long b = (long long)E * ((T + bm - 1) / bm);
-  return (int)(a < b ? a : b);
+  long long n = ((long long)rows + (long long)E * (bm - 1)) / bm;
+  n = n < (long long)E * ((T + bm - 1) / bm) ? n : (long long)E * ((T + bm - 1) / bm);
+  n = n < rows ? n : rows;
+  return (int)n;
 }
 
 // Returns false if `tile` is past the last tile.

@@ -679,12 +679,6 @@ __global__ __launch_bounds__(256) void down_f32_kernel(
 }
 
 // Upper bound on the number of row tiles over all groups.
-int row_tile_bound(bool ident, int rows, int T, int E, int bm) {
-  if (ident) return (rows + bm - 1) / bm;
-  long long a = ((long long)rows + (long long)E * (bm - 1)) / bm;
-  long long b = (long long)E * ((T + bm - 1) / bm);
-  return (int)(a < b ? a : b);
-}
 
 }  // namespace
 
@@ -721,7 +715,7 @@ template <int WF>
 hipError_t launch_gate_up_tiled(const GateUpArgs& a, hipStream_t s) {
   const int NT = (a.N + GN / 2 - 1) / (GN / 2);
   return launch_grouped<true, 256, 4, 4, gate_up_stages<WF>(), float, WF>(
-      a.H, a.N, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
+      a.H, a.N, a.E, a.K, a.rows, a.ident, tile_count_bound(a.ident, a.rows, a.T, a.E, 256), NT,
       static_cast<const bf16*>(a.x), a.w_gate, a.w_up, a.w_stride, a.s_gate, a.s_up, a.s_stride,
       a.offsets, a.sorted_slots, nullptr, static_cast<bf16*>(a.h), static_cast<float*>(nullptr),
       s, a.ev_start, a.ev_stop);
@@ -731,7 +725,7 @@ template <typename YT, int WF>
 hipError_t launch_down_tiled(const DownArgs& a, hipStream_t s) {
   const int NT = (a.H + GN - 1) / GN;
   return launch_grouped<false, 256, 4, 4, 4, YT, WF>(
-      a.N, a.H, a.E, a.K, a.rows, a.ident, row_tile_bound(a.ident, a.rows, a.T, a.E, 256), NT,
+      a.N, a.H, a.E, a.K, a.rows, a.ident, tile_count_bound(a.ident, a.rows, a.T, a.E, 256), NT,
       static_cast<const bf16*>(a.h), a.w_down, a.w_down, a.w_stride, a.s_down, a.s_down,
       a.s_stride, a.offsets, a.sorted_slots, a.topk_w, nullptr, static_cast<YT*>(a.y), s);
 }
@@ -768,7 +762,7 @@ hipError_t launch_gate_up(const GateUpArgs& a, hipStream_t s) {
     const hipError_t e = launch_gate_up_tiled<kWfBF16>(a, s);
     if (e != hipSuccess) return e;
   } else {
-    dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.N + kFT - 1) / kFT);
+    dim3 grid(tile_count_bound(a.ident, a.rows, a.T, a.E, kFT), (a.N + kFT - 1) / kFT);
     launch_maybe_timed(gate_up_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, a.H, a.N,
                        a.E, a.K, a.rows, (int)a.ident, static_cast<const float*>(a.x),
                        static_cast<const float*>(a.w_gate), static_cast<const float*>(a.w_up),
@@ -790,7 +784,7 @@ hipError_t launch_down(const DownArgs& a, hipStream_t s) {
         a.y_bf16 ? launch_down_tiled_fmt<bf16>(a, s) : launch_down_tiled_fmt<float>(a, s);
     if (e != hipSuccess) return e;
   } else {
-    dim3 grid(row_tile_bound(a.ident, a.rows, a.T, a.E, kFT), (a.H + 2 * kFT - 1) / (2 * kFT));
+    dim3 grid(tile_count_bound(a.ident, a.rows, a.T, a.E, kFT), (a.H + 2 * kFT - 1) / (2 * kFT));
     hipLaunchKernelGGL(down_f32_kernel, grid, dim3(256), 0, s, a.H, a.N, a.E, a.rows,
                        (int)a.ident, static_cast<const float*>(a.h),
                        static_cast<const float*>(a.w_down), a.w_stride, a.offsets,

@@ -425,17 +425,10 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   }
 }
 
-int tile_bound(bool ident, int rows, int T, int E, int bm) {
-  if (ident) return (rows + bm - 1) / bm;
-  long long a = ((long long)rows + (long long)E * (bm - 1)) / bm;
-  long long b = (long long)E * ((T + bm - 1) / bm);
-  return (int)(a < b ? a : b);
-}
-
 template <typename WQ, int WK, int MB, int NS, int NC>
 void launch_gu(const GateUpArgs& a, hipStream_t s) {
   const long long cgs = (a.N + 16 * NC - 1) / (16 * NC);
-  dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
+  dim3 grid((unsigned)(tile_count_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
   launch_maybe_timed(gate_up_stream_kernel<WQ, WK, MB, NS, NC>, grid, dim3(64 * WK), 0, s,
                      a.ev_start, a.ev_stop, a.H, a.N, a.E, a.K, a.rows, (int)a.ident,
                      static_cast<const bf16*>(a.x), static_cast<const WQ*>(a.w_gate),
@@ -455,7 +448,7 @@ constexpr int kDnActLdsMinTokens = 9;
 template <typename WQ, int WN, int WK, int MB, int NS, int NC, typename YT>
 void launch_dn(const DownArgs& a, hipStream_t s) {
   const long long cgs = (a.H + 16 * WN * NC - 1) / (16 * WN * NC);
-  dim3 grid((unsigned)(tile_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
+  dim3 grid((unsigned)(tile_count_bound(a.ident, a.rows, a.T, a.E, 16 * MB) * cgs));
   const int al = 16 * MB * (a.N + 8) * 2;
   const int scales = WFmt<WQ>::kBlockScale ? 16 * WN * NC * kMaxScaleRow : 0;
   if (al + scales <= kDnActLdsMax && a.T >= kDnActLdsMinTokens)

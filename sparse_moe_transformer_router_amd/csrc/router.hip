@@ -65,6 +65,42 @@ __device__ __forceinline__ void load8(const bf16* p, float v[8]) {
   v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
 }
 
+// One 64-element chunk of an input row, loaded raw (16-B loads) and widened
+// to fp32 only when used.
+template <typename XT>
+struct RawChunk;
+template <>
+struct RawChunk<bf16> {
+  uint4 u[kChunk / 8];
+  __device__ __forceinline__ void load(const bf16* p) {
+#pragma unroll
+    for (int i = 0; i < kChunk / 8; ++i) u[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ void get(float* v) const {
+#pragma unroll
+    for (int i = 0; i < kChunk / 8; ++i) {
+      v[8 * i + 0] = __uint_as_float(u[i].x << 16); v[8 * i + 1] = __uint_as_float(u[i].x & 0xffff0000u);
+      v[8 * i + 2] = __uint_as_float(u[i].y << 16); v[8 * i + 3] = __uint_as_float(u[i].y & 0xffff0000u);
+      v[8 * i + 4] = __uint_as_float(u[i].z << 16); v[8 * i + 5] = __uint_as_float(u[i].z & 0xffff0000u);
+      v[8 * i + 6] = __uint_as_float(u[i].w << 16); v[8 * i + 7] = __uint_as_float(u[i].w & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct RawChunk<float> {
+  float4 u[kChunk / 4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < kChunk / 4; ++i) u[i] = reinterpret_cast<const float4*>(p)[i];
+  }
+  __device__ __forceinline__ void get(float* v) const {
+#pragma unroll
+    for (int i = 0; i < kChunk / 4; ++i) {
+      v[4 * i + 0] = u[i].x; v[4 * i + 1] = u[i].y; v[4 * i + 2] = u[i].z; v[4 * i + 3] = u[i].w;
+    }
+  }
+};
+
 // Sum of squares of one 64-element chunk, as one fma chain from +0.
 template <typename XT>
 __device__ __forceinline__ float chunk_sumsq(const XT* p) {
@@ -145,9 +181,14 @@ __device__ __forceinline__ float router_vhat(float x, bool pre, float r0, float 
   return (v * r) * s;
 }
 
+constexpr int kSmallMaxChunks = 48;  // H <= 3072
+
 // Small batches: block = TB (<= 4) tokens x 4 * EW experts; lane c owns
 // chunk c (H / 64 <= 64).  Dynamic LDS: vhat [TB][nc][65] + parts
-// [4][TB * EW][65] + norm partials [4][64].
+// [4][TB * EW][65] + norm partials [4][64] + (four tokens a block) the
+// router scale and the pre-norm gain [2][nc][65], staged at the start so that
+// their loads overlap the weights' and the input's instead of following the
+// norms.
 template <typename XT, int TB, int EW>
 __global__ __launch_bounds__(256) void router_logits_small_kernel(
     int T, int H, int E, float eps, const XT* __restrict__ x, const float* __restrict__ pre_gain,
@@ -155,6 +196,11 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
     unsigned* __restrict__ done_counter) {
   extern __shared__ float lds[];
   constexpr int P = TB * EW;
+  // Four tokens a block: the router scale and the pre-norm gain are staged in
+  // LDS with the first loads (128 tokens 24 -> 18 us, 256 tokens 45 -> 30);
+  // with one or two tokens a block the staging costs more than it saves
+  // (1 token 8 -> 11 us), and wave 0 loads them after the norms.
+  constexpr bool kStage = TB >= 4;
   // the completion counter of the top-K kernel that follows on the stream
   if (done_counter != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     *done_counter = 0u;
@@ -162,6 +208,8 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
   float* vh = lds;                              // [TB][nc][65]
   float* parts = vh + TB * nc * (kChunk + 1);   // [4][P][65]
   float* normp = parts + 4 * P * (kChunk + 1);  // [4][64]
+  float* scl = normp + 4 * kWave;               // [nc][65]
+  float* gnl = scl + nc * (kChunk + 1);         // [nc][65]
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int t0 = blockIdx.x * TB;
   const int e0 = blockIdx.y * 4 * EW + wave * EW;
@@ -186,12 +234,40 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
   // 2. norms and the normalised input: wave w takes token t0 + w
   const int tw = t0 + wave;
   const bool tok = wave < TB && tw < T;
+  // The input chunk (kept raw), the router scale and the pre-norm gain: every
+  // load goes out before any result is used, so that all of them (and the
+  // weights above) come back in one round trip.
+  RawChunk<XT> xraw;
+  if (tok && lc) xraw.load(x + (size_t)tw * H + lane * kChunk);
+  if constexpr (kStage) {
+    constexpr int kPer = kSmallMaxChunks * kChunk / 256;
+    float sv[kPer], gv[kPer];
+    auto put = [&](float* dst, const float (&v)[kPer]) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < H) dst[(i / kChunk) * (kChunk + 1) + i % kChunk] = v[k];
+      }
+    };
+    if (pre) {  // uniform
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = min((int)threadIdx.x + 256 * k, H - 1);
+        sv[k] = scale[i];
+        gv[k] = pre_gain[i];
+      }
+      put(scl, sv);
+      put(gnl, gv);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) sv[k] = scale[min((int)threadIdx.x + 256 * k, H - 1)];
+      put(scl, sv);
+    }
+  }
   float xv[kChunk];
   float part = 0.0f;
   if (tok && lc) {
-    const XT* xr = x + (size_t)tw * H + lane * kChunk;
-#pragma unroll
-    for (int i = 0; i < kChunk; i += 8) load8(xr + i, &xv[i]);
+    xraw.get(xv);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) part = __builtin_fmaf(xv[i], xv[i], part);
   }
@@ -201,15 +277,22 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
   if (tok && lane == 0) r = inv_rms_from_parts(normp + wave * kWave, nc, H, eps);
   r = __shfl(r, 0, kWave);
   if (pre) {
-    float g[kChunk];
     part = 0.0f;
     if (tok && lc) {
+      auto apply = [&](const float* g) {
 #pragma unroll
-      for (int i = 0; i < kChunk; i += 8) load8(pre_gain + lane * kChunk + i, &g[i]);
+        for (int i = 0; i < kChunk; ++i) {
+          xv[i] = (xv[i] * r) * g[i];
+          part = __builtin_fmaf(xv[i], xv[i], part);
+        }
+      };
+      if constexpr (kStage) {
+        apply(gnl + lane * (kChunk + 1));
+      } else {
+        float g[kChunk];
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        xv[i] = (xv[i] * r) * g[i];
-        part = __builtin_fmaf(xv[i], xv[i], part);
+        for (int i = 0; i < kChunk; i += 8) load8(pre_gain + lane * kChunk + i, &g[i]);
+        apply(g);
       }
     }
     __syncthreads();
@@ -219,12 +302,19 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(
     r = __shfl(r, 0, kWave);
   }
   if (wave < TB && lc) {
-    float s[kChunk];
-#pragma unroll
-    for (int i = 0; i < kChunk; i += 8) load8(scale + lane * kChunk + i, &s[i]);
     float* dst = vh + (wave * nc + lane) * (kChunk + 1);
+    auto put = [&](const float* sc) {
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) dst[i] = tok ? (xv[i] * r) * s[i] : 0.0f;
+      for (int i = 0; i < kChunk; ++i) dst[i] = tok ? (xv[i] * r) * sc[i] : 0.0f;
+    };
+    if constexpr (kStage) {
+      put(scl + lane * (kChunk + 1));
+    } else {
+      float sc[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; i += 8) load8(scale + lane * kChunk + i, &sc[i]);
+      put(sc);
+    }
   }
   __syncthreads();
 
@@ -569,8 +659,18 @@ __global__ __launch_bounds__(kChunkSlots) void route_topk_dispatch_kernel(
 template <typename XT, int TB, int EW>
 void launch_small(const RouterArgs& a, bool count, hipStream_t s) {
   const int nc = a.H / kChunk;
+  constexpr int kStaged = TB >= 4 ? 2 : 0;  // scale and gain rows staged in LDS
   const size_t lds = sizeof(float) * ((size_t)TB * nc * (kChunk + 1) +
-                                      4 * TB * EW * (kChunk + 1) + 4 * kWave);
+                                      4 * TB * EW * (kChunk + 1) + 4 * kWave +
+                                      kStaged * nc * (kChunk + 1));
+  // past 64 KB at 4 tokens per block (26B-A4B: 78 KB, two blocks per CU)
+  constexpr size_t kMaxLds = sizeof(float) * ((size_t)TB * kSmallMaxChunks * (kChunk + 1) +
+                                              4 * TB * EW * (kChunk + 1) + 4 * kWave +
+                                              kStaged * kSmallMaxChunks * (kChunk + 1));
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(router_logits_small_kernel<XT, TB, EW>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  (void)attr;  // a failure shows in the launch's error
   dim3 grid((a.T + TB - 1) / TB, (a.E + 4 * EW - 1) / (4 * EW));
   hipLaunchKernelGGL((router_logits_small_kernel<XT, TB, EW>), grid, dim3(256), lds, s, a.T, a.H,
                      a.E, a.eps, static_cast<const XT*>(a.x), a.pre_gain, a.router_scale,
@@ -579,7 +679,7 @@ void launch_small(const RouterArgs& a, bool count, hipStream_t s) {
 
 }  // namespace
 
-// Small-batch logits: up to 448 tokens, H <= 3072 (LDS within 64 KB).  The
+// Small-batch logits: up to 448 tokens, H <= 3072 (LDS within 96 KB).  The
 // chunk-parallel kernel spreads a token's 44 chunk chains (26B-A4B) over a
 // wave; the large-batch kernels run them one after another in a thread and
 // pay a fixed ~80 us for the chunk rounds (the whole route at 128 tokens:
@@ -589,7 +689,7 @@ void launch_small(const RouterArgs& a, bool count, hipStream_t s) {
 // most 1024 slots.
 constexpr int kSmallLogitsMaxT = 448;
 static bool router_small_logits(int T, int H) {
-  return H / kChunk <= 48 && T <= kSmallLogitsMaxT;
+  return H / kChunk <= kSmallMaxChunks && T <= kSmallLogitsMaxT;
 }
 // Four wave groups (one 8-wave block per CU, 124 KB of LDS) while the grid
 // fits the 256 CUs at one block each; past that two groups (58 KB, two
