@@ -102,9 +102,13 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
   const int n0 = cg * 16 * NC + fr;  // column of group c: n0 + 16 c
   // Every load below is unconditional and in bounds.  A column past N (a
   // ragged last group) reads row N - 1 and a row past row1 reads row row0:
-  // their MFMA outputs are never stored.  A span past the end of the
-  // contraction reads k = 0, and its weights are zeroed where they are used
-  // (only in a ragged last k-block).
+  // their MFMA outputs are never stored.  A weight span past the end of the
+  // contraction (only in a ragged last k-block) re-reads the row's last span
+  // that starts inside, part of the lines this k-block reads anyway, and is
+  // zeroed where it is used.  (Re-reading k = 0 instead fetched the row's
+  // first line a second time, long after the first: the int8 / E4M3 down
+  // projection, 704 long, read 1.15x its bytes.)
+  const int klast = (H - 1) / LK * LK;  // start of the row's last span
   long long wel[NC];  // first element of the weight row of column n0 + 16 c
   const uint8_t* gsr[NC];
   const uint8_t* usr[NC];
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(64 * WK) void gate_up_stream_kernel(
   auto load = [&](int kb, int slot) {
     const int ks = kb * KBK + LK * fg;  // first weight of this lane's span
     const bool kv = ks < H;
-    const int kc = kv ? ks : 0;              // in-bounds start
+    const int kc = kv ? ks : klast;          // in-bounds start
     const bool kfull = kc + LK <= H;       // else only its first half lies inside
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -278,8 +282,9 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   const int fr = lane % 16, fg = lane / 16;
   const int n0 = (cg * WN + wn) * 16 * NC + fr;  // column of group c: n0 + 16 c
   // Unconditional in-bounds loads, as in gate_up: a column past H reads row
-  // H - 1, a row past row1 reads row row0, a span past N reads k = 0 with its
-  // weights zeroed where they are used.
+  // H - 1, a row past row1 reads row row0, a weight span past N re-reads the
+  // row's last span that starts inside, zeroed where it is used.
+  const int klast = (N - 1) / LK * LK;
   long long wel[NC];
   const uint8_t* bsr[NC];
 #pragma unroll
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
   auto load_w = [&](int kb, int slot) {
     const int ks = kb * KBK + LK * fg;  // first weight of this lane's span
     const bool kv = ks < N;
-    const int kc = kv ? ks : 0;              // in-bounds start
+    const int kc = kv ? ks : klast;          // in-bounds start
     const bool kfull = kc + LK <= N;       // else only its first half lies inside
 #pragma unroll
     for (int c = 0; c < NC; ++c) bb[slot][c].load(wrow(wd, wel[c]), kc, bsr[c], kfull);
