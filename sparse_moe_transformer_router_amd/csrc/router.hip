@@ -423,34 +423,41 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(
   }
 }
 
-// Large batches, E % 4 == 0, chunks split over wave groups: block = 32 tokens
-// x 64 experts, G groups of 128 threads; group g takes chunks g, g + G, ...
-// Thread (tq, eq) of a group runs 16 chains: tokens 4 tq .. 4 tq + 3 x
-// experts 4 eq .. 4 eq + 3, with one 16-B weight read and one 16-B input
-// read per 16 fmas.  Per round every group stages its chunk (weights
-// transposed to [64 k][64 e], router input [64][32 + 4]) in its own LDS region, runs
-// its chains, and groups 1 .. G-1 leave their chunk results in LDS, which
-// group 0 adds to its totals in chunk order.
-constexpr int kSplitT = 32, kSplitE = 64, kSplitVP = kSplitT + 4;
+// Large batches, E % 4 == 0, chunks split over wave groups: block = 8 TQ
+// tokens x 64 experts (TQ = 4 or 2), G groups of 128 threads; group g takes
+// chunks g, g + G, ...  Thread (tq, eq) of a group runs 4 TQ chains: tokens
+// TQ tq .. TQ tq + TQ - 1 x experts 4 eq .. 4 eq + 3, with one 16-B weight
+// read and one 4 TQ-B input read per 4 TQ fmas.  Per round every group
+// stages its chunk (weights transposed to [64 k][64 e], router input [64][8
+// TQ + 4]) in its own LDS region, runs its chains, and groups 1 .. G-1 leave
+// their chunk results in LDS, which group 0 adds to its totals in chunk
+// order.  TQ = 2 halves a block's work where 32-token blocks would leave
+// CUs idle (up to 2048 tokens at 26B-A4B shapes): a block then also waits
+// less for a CU that another kernel holds (the layer's dense branch runs
+// beside the router).
+constexpr int kSplitE = 64;
 // Column swizzle of the staged weight tile: k quad kq's expert quads are
 // permuted by an XOR with 2 (kq mod 8), a bijection on 0 .. 15.
 __device__ __forceinline__ int wswz(int kq) { return 2 * (kq & 7); }
-template <typename XT, int G>
+template <typename XT, int G, int TQ>
 __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     int T, int H, int E, const XT* __restrict__ x, const float* __restrict__ pre_gain,
     const float* __restrict__ r0v, const float* __restrict__ rv,
     const float* __restrict__ scale, const float* __restrict__ W, float* __restrict__ logits) {
+  static_assert(TQ == 4 || TQ == 2, "tokens per thread");
+  constexpr int kSplitT = 8 * TQ, kSplitVP = kSplitT + 4;
+  constexpr int SK = kChunk * kSplitT / 128;  // input values a thread stages per chunk
   __shared__ __align__(16) float wl[G][kChunk][kSplitE];
   __shared__ __align__(16) float vl[G][kChunk][kSplitVP];
-  __shared__ float ex[G > 1 ? G - 1 : 1][16][128];
+  __shared__ float ex[G > 1 ? G - 1 : 1][4 * TQ][128];
   const int g = threadIdx.x / 128, tig = threadIdx.x % 128;
   const int tq = tig / 16, eq = tig % 16;
   const int t0 = blockIdx.x * kSplitT, e0 = blockIdx.y * kSplitE;
   const bool pre = pre_gain != nullptr;
   const int nc = H / kChunk;
   const int R = (nc + G - 1) / G;
-  // staging of the input: token st, k values sk .. sk + 15 of the chunk
-  const int st = tig % kSplitT, sk = (tig / kSplitT) * 16;
+  // staging of the input: token st, k values sk .. sk + SK - 1 of the chunk
+  const int st = tig % kSplitT, sk = (tig / kSplitT) * SK;
   const int tcl = min(t0 + st, T - 1);
   const float r0 = pre ? r0v[tcl] : 0.0f, r = rv[tcl];
   const XT* xr = x + (size_t)tcl * H + sk;
@@ -466,8 +473,8 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
   // waits on these loads before the round's chains run.
   constexpr bool kBf16In = std::is_same<XT, bf16>::value;
   float4 wreg[8];
-  uint4 xu[2];
-  float xv[16], sv[16], gv[16];
+  uint4 xu[SK / 8];
+  float xv[SK], sv[SK], gv[SK];
   auto gload = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -483,27 +490,27 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
             *reinterpret_cast<const float4*>(W + (size_t)e * H + c * kChunk + 4 * kq);
       }
     }
-    if constexpr (kBf16In) {
-      xu[0] = *reinterpret_cast<const uint4*>(xr + c * kChunk);
-      xu[1] = *reinterpret_cast<const uint4*>(xr + c * kChunk + 8);
-    } else {
-      load8(reinterpret_cast<const float*>(xr) + c * kChunk, xv);
-      load8(reinterpret_cast<const float*>(xr) + c * kChunk + 8, xv + 8);
+#pragma unroll
+    for (int h = 0; h < SK / 8; ++h) {
+      if constexpr (kBf16In)
+        xu[h] = *reinterpret_cast<const uint4*>(xr + c * kChunk + 8 * h);
+      else
+        load8(reinterpret_cast<const float*>(xr) + c * kChunk + 8 * h, xv + 8 * h);
     }
-    load8(scale + c * kChunk + sk, sv);
-    load8(scale + c * kChunk + sk + 8, sv + 8);
+#pragma unroll
+    for (int h = 0; h < SK / 8; ++h) load8(scale + c * kChunk + sk + 8 * h, sv + 8 * h);
     if (pre) {
-      load8(pre_gain + c * kChunk + sk, gv);
-      load8(pre_gain + c * kChunk + sk + 8, gv + 8);
+#pragma unroll
+      for (int h = 0; h < SK / 8; ++h) load8(pre_gain + c * kChunk + sk + 8 * h, gv + 8 * h);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) gv[i] = 0.0f;
+      for (int i = 0; i < SK; ++i) gv[i] = 0.0f;
     }
   };
   auto lstore = [&]() {
     if constexpr (kBf16In) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < SK / 8; ++h) {
         const unsigned u[4] = {xu[h].x, xu[h].y, xu[h].z, xu[h].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -523,12 +530,12 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
       *reinterpret_cast<float4*>(&wl[g][4 * kq + 3][col]) = make_float4(b[0].w, b[1].w, b[2].w, b[3].w);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vl[g][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
+    for (int i = 0; i < SK; ++i) vl[g][sk + i][st] = router_vhat(xv[i], pre, r0, gv[i], r, sv[i]);
   };
 
-  float total[4][4];
+  float total[TQ][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TQ; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) total[i][j] = 0.0f;
   if (g < nc) gload(g);
@@ -538,19 +545,25 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     if (have) lstore();
     __syncthreads();
     if (c + G < nc) gload(c + G);
-    float p[4][4];
+    float p[TQ][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TQ; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) p[i][j] = 0.0f;
     if (have) {
 #pragma unroll 8
       for (int k = 0; k < kChunk; ++k) {
         const float4 w = *reinterpret_cast<const float4*>(&wl[g][k][4 * (eq ^ wswz(k / 4))]);
-        const float4 v = *reinterpret_cast<const float4*>(&vl[g][k][4 * tq]);
-        const float vv[4] = {v.x, v.y, v.z, v.w};
+        float vv[TQ];
+        if constexpr (TQ == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(&vl[g][k][4 * tq]);
+          vv[0] = v.x; vv[1] = v.y; vv[2] = v.z; vv[3] = v.w;
+        } else {
+          const float2 v = *reinterpret_cast<const float2*>(&vl[g][k][2 * tq]);
+          vv[0] = v.x; vv[1] = v.y;
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TQ; ++i) {
           p[i][0] = __builtin_fmaf(vv[i], w.x, p[i][0]);
           p[i][1] = __builtin_fmaf(vv[i], w.y, p[i][1]);
           p[i][2] = __builtin_fmaf(vv[i], w.z, p[i][2]);
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
       }
       if (g > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TQ; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) ex[g - 1][4 * i + j][tig] = p[i][j];
       }
@@ -567,14 +580,14 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
     __syncthreads();
     if (g == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TQ; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + p[i][j];
 #pragma unroll
       for (int h = 1; h < G; ++h) {
         if (rr * G + h >= nc) break;  // uniform
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TQ; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) total[i][j] = total[i][j] + ex[h - 1][4 * i + j][tig];
       }
@@ -584,8 +597,8 @@ __global__ __launch_bounds__(128 * G) void router_logits_split_kernel(
   const int e = e0 + 4 * eq;
   if (e >= E) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * tq + i;
+  for (int i = 0; i < TQ; ++i) {
+    const int t = t0 + TQ * tq + i;
     if (t < T)
       *reinterpret_cast<float4*>(logits + (size_t)t * E + e) =
           make_float4(total[i][0], total[i][1], total[i][2], total[i][3]);
@@ -692,12 +705,19 @@ static bool router_small_logits(int T, int H) {
   return H / kChunk <= kSmallMaxChunks && T <= kSmallLogitsMaxT;
 }
 // Four wave groups (one 8-wave block per CU, 124 KB of LDS) while the grid
-// fits the 256 CUs at one block each; past that two groups (58 KB, two
-// 4-wave blocks per CU).  The whole route at 4096 tokens: 146 us with the
-// earlier kernel (one token per thread, 5 B of LDS per fma), 91 us with
-// four groups; at 8192 tokens with the pre-norm 191 -> 157 us with two
-// groups (four: 179 us).
+// of 32-token blocks fits the 256 CUs at one block each; past that two
+// groups (58 KB, two 4-wave blocks per CU).  The whole route at 4096 tokens:
+// 146 us with the earlier kernel (one token per thread, 5 B of LDS per fma),
+// 91 us with four groups; at 8192 tokens with the pre-norm 191 -> 157 us
+// with two groups (four: 179 us).  Below 256 such blocks the blocks take 16
+// tokens while twice as many still fit one round (at 26B-A4B shapes up to
+// 2048 tokens; the route at 512 / 1024 / 2048 tokens with the pre-norm 85 /
+// 87 / 95 -> 69 / 71 / 79 us with four groups, routing bit-identical; at 3000
+// tokens, two rounds of them, 100 -> 124 us); their smaller input tile
+// leaves room for six wave groups (146 KB), so a block runs 8 chunk rounds
+// instead of 11.
 constexpr long long kSplitOneBlockPerCu = 256;
+constexpr int kSplitG16 = 6;
 
 bool router_fuses_dispatch(int T, int H, int E, int K) {
   return router_small_logits(T, H) && T * K <= kChunkSlots;
@@ -738,14 +758,19 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(router_prep_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.H,
                      a.eps, x, a.pre_gain, a.ws_r0, a.ws_r);
   if (a.E % 4 == 0) {
-    const dim3 sg((a.T + kSplitT - 1) / kSplitT, (a.E + kSplitE - 1) / kSplitE);
-    if ((long long)sg.x * sg.y <= kSplitOneBlockPerCu)
-      hipLaunchKernelGGL((router_logits_split_kernel<XT, 4>), sg, dim3(512), 0, s, a.T, a.H, a.E,
-                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
+    const int ne = (a.E + kSplitE - 1) / kSplitE;
+    const dim3 sg((a.T + 31) / 32, ne), sg16((a.T + 15) / 16, ne);
+    if ((long long)sg16.x * sg16.y <= kSplitOneBlockPerCu)
+      hipLaunchKernelGGL((router_logits_split_kernel<XT, kSplitG16, 2>), sg16,
+                         dim3(128 * kSplitG16), 0, s, a.T, a.H, a.E, x, a.pre_gain, a.ws_r0,
+                         a.ws_r, a.router_scale, a.router_w, a.ws_logits);
+    else if ((long long)sg.x * sg.y <= kSplitOneBlockPerCu)
+      hipLaunchKernelGGL((router_logits_split_kernel<XT, 4, 4>), sg, dim3(512), 0, s, a.T, a.H,
+                         a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
                          a.ws_logits);
     else
-      hipLaunchKernelGGL((router_logits_split_kernel<XT, 2>), sg, dim3(256), 0, s, a.T, a.H, a.E,
-                         x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
+      hipLaunchKernelGGL((router_logits_split_kernel<XT, 2, 4>), sg, dim3(256), 0, s, a.T, a.H,
+                         a.E, x, a.pre_gain, a.ws_r0, a.ws_r, a.router_scale, a.router_w,
                          a.ws_logits);
   } else {
     hipLaunchKernelGGL(router_logits_tiled_kernel<XT>, dim3((a.T + 63) / 64, (a.E + 31) / 32),
