@@ -295,6 +295,26 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       bsr[c] = ssc + min(16 * (wn * NC + c) + fr, H - 1 - cg * 16 * WN * NC) * (N / 32);
   }
   const int nmb = (row1 - row0 + 15) / 16;
+  // Output slot and routing weight of this lane's rows (rows past the tile
+  // clamp to its last row), fetched behind the weight stream: the slots
+  // before the ring's first loads, the weights after them.  In the epilogue
+  // they were two dependent loads per row after the stream had ended.  The
+  // loads carry no condition (the dense branch, which has neither array,
+  // reads the first element of h instead and ignores it), so the ring's
+  // waits stay exact.
+  int oslot[MB][4];
+  float ow[MB][4];
+  {
+    const int32_t* sp = ident ? reinterpret_cast<const int32_t*>(hbuf) : sorted_slots;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(row0 + 16 * mb + 4 * fg + r, row1 - 1);
+        const int v = sp[ident ? 0 : row];
+        oslot[mb][r] = ident ? row : v;
+      }
+  }
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   const int ALS = N + 8;  // staged row pitch (bf16)
   const bf16* ap[MB];
@@ -376,14 +396,39 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (AL) {
+    // Loads in batches of four chunks, then their stores: one copy a chunk
+    // at a time waited for each load before its store (a round trip per
+    // chunk, ~6 per block at 704 columns).  A chunk index past the tile
+    // stands for the last chunk, which it re-reads and stores again with the
+    // same value: no condition, so the loads are not sunk to their stores.
     const int nrows = row1 - row0, cpr = N / 8;  // 16-B chunks per row
+    const int n = nrows * cpr;
+    constexpr int NT = 64 * WN * WK, kBatch = 4;
     bf16* al = reinterpret_cast<bf16*>(dyn_lds);
-    for (int i = threadIdx.x; i < nrows * cpr; i += blockDim.x) {
-      const int r = i / cpr, ch = i % cpr;
-      *reinterpret_cast<uint4*>(al + r * ALS + ch * 8) =
-          *reinterpret_cast<const uint4*>(hbuf + (size_t)(row0 + r) * N + ch * 8);
+    for (int i0 = 0; i0 < n; i0 += kBatch * NT) {
+      uint4 c[kBatch];
+      int dst[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = min(i0 + (int)threadIdx.x + j * NT, n - 1);
+        const int r = i / cpr, ch = i - r * cpr;
+        c[j] = *reinterpret_cast<const uint4*>(hbuf + (size_t)(row0 + r) * N + ch * 8);
+        dst[j] = r * ALS + ch * 8;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) *reinterpret_cast<uint4*>(al + dst[j]) = c[j];
     }
     __syncthreads();
+  }
+  {
+    const float* wp = ident ? reinterpret_cast<const float*>(hbuf) : topk_w;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = wp[ident ? 0 : oslot[mb][r]];
+        ow[mb][r] = ident ? 1.0f : v;
+      }
   }
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) load_a(max(min(kb0 + s, kb1 - 1), 0), s);
@@ -422,9 +467,7 @@ __global__ __launch_bounds__(64 * WN * WK) void down_stream_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 16 * mb + 4 * fg + r;
         if (row >= row1 || !nvalid) continue;
-        const int slot = ident ? row : sorted_slots[row];
-        const float sc = ident ? 1.0f : topk_w[slot];
-        y[(size_t)slot * H + n] = from_f32<YT>(sc * v[r]);
+        y[(size_t)oslot[mb][r] * H + n] = from_f32<YT>(ow[mb][r] * v[r]);
       }
     }
   }
