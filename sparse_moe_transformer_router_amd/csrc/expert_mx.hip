@@ -484,6 +484,17 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
       bsc[c] = static_cast<const uint8_t*>(sd) + e * s_stride + n * nsb;
   }
   const int nmb = (row1 - row0 + 15) / 16;
+  // Output slot and routing weight of this lane's rows (rows past the tile
+  // clamp to its last row): the slots loaded first, the weights before the
+  // k-loop, so that neither waits at the end.  In the epilogue each store
+  // had waited for its slot and then its weight, re-loaded for every column
+  // group.
+  int oslot[MB][4];
+  float ow[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oslot[mb][r] = sorted_slots[min(row0 + 16 * mb + 4 * g + r, row1 - 1)];
   const uint8_t* arow[MB];
   const uint8_t* asc[MB];
 #pragma unroll
@@ -646,6 +657,10 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
       load_s(min(s, KB - 1), s);
     }
   }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ow[mb][r] = topk_w[oslot[mb][r]];
   int kb = 0;
   // steady state as in gate_up: k-blocks wholly inside N, nothing masked
   const int kbf = N / 128;
@@ -681,8 +696,7 @@ __global__ __launch_bounds__(64 * WN) void down_mx_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 16 * mb + 4 * g + r;
         if (row >= row1 || !nvalid) continue;
-        const int slot = sorted_slots[row];
-        y[(size_t)slot * H + n] = from_f32<YT>(topk_w[slot] * v[r]);
+        y[(size_t)oslot[mb][r] * H + n] = from_f32<YT>(ow[mb][r] * v[r]);
       }
     }
   }
