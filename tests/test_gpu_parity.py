@@ -71,9 +71,12 @@ def test_router_decode_sizes(T):
     _check_router(synth.moe_case(T, seed=T, I=32, router_scale_std=0.05))
 
 
-# 4096 tokens: the chunk-split kernel's four-group form (256 blocks), 4128:
-# its two-group form (258 blocks)
-@pytest.mark.parametrize("T,skew", [(257, False), (4096, True), (4128, False)])
+# the chunk-split kernel at 26B shapes: 257 and 2048 tokens its 16-token form
+# (six wave groups; 2048: 256 blocks, the largest grid of that form), 2049
+# and 4096 its 32-token four-group form (130 and 256 blocks), 4128 its
+# two-group form (258 blocks)
+@pytest.mark.parametrize("T,skew", [(257, False), (2048, True), (2049, False), (4096, True),
+                                    (4128, False)])
 def test_router_prefill_sizes(T, skew):
     _check_router(synth.moe_case(T, seed=11, I=32, skew=skew))
 
@@ -87,9 +90,12 @@ def test_router_with_pre_norm(T):
 
 @pytest.mark.parametrize("T,H,E,K,bf16", [
     (600, 128, 6, 2, False),    # E % 4 != 0: lane-per-token tiled kernel
-    # chunk-split kernel; 4 groups up to 256 blocks, else 2
-    (600, 192, 132, 4, True),   # 4 groups, 3 chunks (group 3 idle), ragged expert block
-    (1000, 320, 64, 4, False),  # 4 groups, 5 chunks: a last round with one group
+    # chunk-split kernel: 16-token blocks with 6 groups while their grid fits
+    # 256 blocks, else 32-token blocks with 4 groups while theirs does, else 2
+    (600, 192, 132, 4, True),   # 16-token, 3 chunks (groups 3-5 idle), ragged expert block
+    (1000, 320, 64, 4, False),  # 16-token, 5 chunks: group 5 idle
+    (1000, 832, 64, 4, True),   # 16-token, 13 chunks: a last round with one group
+    (1500, 576, 132, 4, False), # 32-token (282 16-token blocks), 4 groups, 9 chunks
     (4100, 64, 256, 8, False),  # 2 groups, 1 chunk, ragged token tail
     (9000, 192, 128, 8, True),  # 2 groups, 3 chunks: a last round with one group
 ])
